@@ -1,0 +1,167 @@
+/*
+ * pkv.h -- C ABI of libpkv, paged KV-cache decode attention for AMD MI355X (gfx950).
+ *
+ * The operations follow the pages' statement of the problem:
+ *
+ *  - The KV cache is split into fixed-size blocks (16 or 32 tokens) held in one
+ *    preallocated pool; each sequence has a block table mapping its logical
+ *    blocks to physical ones, which need not be contiguous ("Master Paged
+ *    Attention for LLM Inference", section "How Paged Attention Works: The
+ *    Mechanics", items 1-3; "PagedAttention Explained", section "Block Tables
+ *    and Non-Contiguous Storage").
+ *  - Decode attention walks each sequence's block table, loads its blocks and
+ *    attends over the concatenated keys and values, without first gathering
+ *    them into contiguous memory ("PagedAttention Explained", sections "Block
+ *    Tables and Non-Contiguous Storage" and the closing remark of
+ *    "Implementing a Simplified Paged KV Cache").
+ *  - A new token's key and value go to row `length % block_size` of the last
+ *    block of its sequence (same page, "Implementing a Simplified Paged KV
+ *    Cache", append_token); here the caller passes that position as a slot.
+ *  - Blocks shared between sequences are copied before a sequence writes into
+ *    them (copy-on-write; "Master Paged Attention for LLM Inference", item 4 of
+ *    "How Paged Attention Works"; "PagedAttention Explained", "Shared Prefix
+ *    Caching").
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers; the caller allocates and owns every
+ *    buffer (the library allocates nothing).  Pointers to pkv_pool_desc /
+ *    pkv_decode_opts are HOST pointers read during the call only.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *    work on it and never synchronize the host.  Calls on different streams may
+ *    run concurrently when they write disjoint buffers.
+ *  - Host-checkable argument errors return a status before anything is
+ *    launched; the message of the last error on the calling thread is
+ *    available from pkv_last_error().  Nothing aborts or throws across the ABI.
+ *  - Values stored in device memory (block ids, context lengths, slots, copy
+ *    pairs) are preconditions the host cannot check without a synchronization.
+ *    The kernels still never touch memory outside the pools for a bad value:
+ *    an out-of-range block id makes the affected sequence's output rows NaN,
+ *    an out-of-range slot or copy pair is skipped.
+ *
+ * Pool layout (element = bfloat16 or float32; x = 16 / element bytes, i.e. one
+ * 16-byte chunk; N blocks, Hkv kv heads, bs = block_size, D = head_dim):
+ *  - key pool   [N][Hkv][D/x][bs][x]: key (block p, head h, row t, dim d) at
+ *                element ((p*Hkv + h)*(D/x) + d/x)*(bs*x) + t*x + d%x
+ *  - value pool [N][Hkv][D][bs]:      value (p, h, t, d) at element
+ *                ((p*Hkv + h)*D + d)*bs + t
+ *  Each (block, kv head) tile of either pool is one contiguous bs*D-element
+ *  region.  Rows of a block at or past a sequence's length may hold any bits
+ *  (blocks are reused without clearing); they never reach the output.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,         /* bad pointer, size, shape or combination */
+  PKV_EUNSUPPORTED = 2,   /* valid but not built: block_size, head_dim, group size, dtype */
+  PKV_EWORKSPACE = 3,     /* workspace missing or smaller than required */
+  PKV_EHIP = 4            /* the HIP runtime reported an error at launch */
+} pkv_status;
+
+/* Shapes shared by both pools. Supported: block_size 16 or 32, head_dim 64 or
+ * 128, dtype PKV_F32 or PKV_BF16, num_blocks*block_size < 2^31. */
+typedef struct {
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t head_dim;
+  int32_t dtype; /* pkv_dtype */
+} pkv_pool_desc;
+
+/* Decode kernel family. */
+typedef enum {
+  PKV_KERNEL_AUTO = 0,   /* MFMA for bf16 with 4 or 8 query heads per kv head, vector otherwise */
+  PKV_KERNEL_VECTOR = 1, /* per-lane dot products with cross-lane reductions (any supported group) */
+  PKV_KERNEL_MFMA = 2    /* grouped query tile on matrix cores (bf16, head_dim 128, group 4 or 8) */
+} pkv_kernel;
+
+/* Optional decode settings (pass NULL for defaults). */
+typedef struct {
+  /* Tokens per split-K partition: 0 = chosen by the library from the shapes;
+   * a positive value is rounded up to a whole number of blocks; a value at or
+   * above max_context_len means one pass with no partials and no reduce. */
+  int32_t partition_tokens;
+  int32_t kernel; /* pkv_kernel */
+} pkv_decode_opts;
+
+/* Bytes of workspace pkv_paged_attn_decode needs for these shapes and options
+ * (0 when the call runs as a single pass).  Returns 0 for invalid shapes. */
+size_t pkv_paged_attn_workspace_bytes(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_heads,
+                                      int32_t max_context_len, const pkv_decode_opts* opts);
+
+/*
+ * Paged decode attention: for every sequence b < num_seqs and query head
+ * h < num_heads,
+ *     out[b][h][:] = sum_t softmax_t(scale * <q[b][h], k_t>) * v_t
+ * over the sequence's tokens t < context_lens[b], where token t's key/value
+ * are row t % block_size of physical block block_tables[b][t / block_size]
+ * for kv head h / (num_heads / num_kv_heads).  context_lens[b] == 0 gives an
+ * all-zero output row.  Arithmetic: products and sums in float32, softmax as a
+ * running (max, sum) in float32 ("flash" form, exact up to rounding), output
+ * rounded to nearest-even when out_dtype is PKV_BF16.
+ *
+ *  q             [num_seqs][num_heads][head_dim], pool->dtype
+ *  k_pool/v_pool pools in the layout above
+ *  block_tables  [num_seqs][max_blocks_per_seq] int32; entries past a
+ *                sequence's last block are never read
+ *  context_lens  [num_seqs] int32, each in [0, max_context_len]
+ *  max_context_len  host-side upper bound of context_lens (<= max_blocks_per_seq*block_size)
+ *  out_dtype     PKV_BF16 or PKV_F32 for bf16 inputs; PKV_F32 for f32 inputs
+ *  out           [num_seqs][num_heads][head_dim] out_dtype; must not alias inputs
+ *  workspace     device scratch of at least pkv_paged_attn_workspace_bytes(); may be
+ *                NULL when that is 0.  Not aliased by other in-flight calls.
+ */
+pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 const pkv_pool_desc* pool, float scale, int32_t out_dtype, void* out,
+                                 void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts,
+                                 void* stream);
+
+/*
+ * Cache write: for every token i < num_tokens with slot s = slot_mapping[i] >= 0,
+ * copy the bits of k[i][h][:] / v[i][h][:] (all kv heads h) to row s % block_size
+ * of block s / block_size of k_pool / v_pool.  Negative slots are skipped.
+ *
+ *  k, v          token i, head h starts at element i*token_stride + h*head_dim;
+ *                token_stride = 0 means num_kv_heads*head_dim (dense [T][Hkv][D])
+ *  slot_mapping  [num_tokens] int32; slots must be distinct (else the survivor is unspecified)
+ */
+pkv_status pkv_reshape_and_cache(const void* k, const void* v, int64_t k_token_stride, int64_t v_token_stride,
+                                 const int32_t* slot_mapping, int32_t num_tokens, void* k_pool, void* v_pool,
+                                 const pkv_pool_desc* pool, void* stream);
+
+/*
+ * Copy-on-write block copy: for every pair i < num_pairs, block
+ * src_dst_pairs[2i+1] of both pools (all kv heads) becomes a bit copy of block
+ * src_dst_pairs[2i].  Destinations must be distinct and no destination may be
+ * a source of another pair (each copy then reads what its source held before
+ * the call).  src_dst_pairs is a device array [num_pairs][2] int32.
+ */
+pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_dst_pairs, int32_t num_pairs,
+                           const pkv_pool_desc* pool, void* stream);
+
+/* Static text for a status code. */
+const char* pkv_status_string(pkv_status status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int32_t pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,227 @@
+// C ABI of libpkv (declared in include/pkv.h): argument checks, kernel choice,
+// split-K planning and launches.  Host code only; no host synchronization.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/pkv.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+pkv_status ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elt_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : 4; }
+
+pkv_status check_pool(const pkv_pool_desc* pool) {
+  if (!pool) return fail(PKV_EINVAL, "pool descriptor is NULL");
+  if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0 || pool->block_size <= 0 || pool->head_dim <= 0)
+    return fail(PKV_EINVAL, "pool sizes must be positive");
+  if (pool->dtype != PKV_F32 && pool->dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "dtype must be F32 or BF16");
+  if (pool->block_size != 16 && pool->block_size != 32)
+    return fail(PKV_EUNSUPPORTED, "block_size must be 16 or 32");
+  if (pool->head_dim != 64 && pool->head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if ((int64_t)pool->num_blocks * pool->block_size >= (int64_t(1) << 31))
+    return fail(PKV_EINVAL, "num_blocks * block_size must stay below 2^31");
+  return PKV_OK;
+}
+
+// Partition plan of one decode call.
+struct Plan {
+  bool mfma = false;
+  int group = 1;
+  int blocks_per_part = 1;
+  int num_parts = 1;
+};
+
+pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_heads, int32_t max_context_len,
+                     const pkv_decode_opts* opts, Plan* plan) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs must be >= 0");
+  if (num_heads <= 0 || num_heads % pool->num_kv_heads != 0)
+    return fail(PKV_EINVAL, "num_heads must be a positive multiple of num_kv_heads");
+  if (max_context_len < 0) return fail(PKV_EINVAL, "max_context_len must be >= 0");
+  const int g = num_heads / pool->num_kv_heads;
+  const int bf16 = pool->dtype == PKV_BF16;
+  const int kernel = opts ? opts->kernel : PKV_KERNEL_AUTO;
+  if (kernel != PKV_KERNEL_AUTO && kernel != PKV_KERNEL_VECTOR && kernel != PKV_KERNEL_MFMA)
+    return fail(PKV_EINVAL, "unknown kernel selector");
+  const bool mfma_ok = pkv::mfma_supported(bf16, pool->head_dim, pool->block_size, g);
+  if (kernel == PKV_KERNEL_MFMA && !mfma_ok)
+    return fail(PKV_EUNSUPPORTED, "MFMA kernel needs bf16, head_dim 128 and 4 or 8 query heads per kv head");
+  plan->mfma = (kernel == PKV_KERNEL_MFMA) || (kernel == PKV_KERNEL_AUTO && mfma_ok);
+  if (!plan->mfma && !pkv::vector_supported(bf16, pool->head_dim, pool->block_size, g))
+    return fail(PKV_EUNSUPPORTED, "query heads per kv head must be 1, 2, 4 or 8");
+  plan->group = g;
+
+  const int bs = pool->block_size;
+  const int max_blocks = (max_context_len + bs - 1) / bs;
+  int64_t part_tokens = opts ? opts->partition_tokens : 0;
+  if (part_tokens < 0) return fail(PKV_EINVAL, "partition_tokens must be >= 0");
+  if (part_tokens == 0) {
+    // Automatic: aim for about 2048 workgroups (8 per CU) but never fewer than
+    // 2 blocks per wave; contexts up to 512 tokens stay in one pass.
+    const int64_t units = (int64_t)num_seqs * pool->num_kv_heads;
+    int64_t want_parts = units > 0 ? (2048 + units - 1) / units : 1;
+    int64_t tokens = (max_context_len + want_parts - 1) / (want_parts > 0 ? want_parts : 1);
+    const int64_t floor_tokens = 512;
+    part_tokens = tokens < floor_tokens ? floor_tokens : tokens;
+  }
+  int64_t bpp = (part_tokens + bs - 1) / bs;
+  if (bpp < 1) bpp = 1;
+  if (bpp >= max_blocks) bpp = max_blocks > 0 ? max_blocks : 1;
+  plan->blocks_per_part = (int)bpp;
+  plan->num_parts = max_blocks > 0 ? (int)((max_blocks + bpp - 1) / bpp) : 1;
+  if (plan->num_parts > 65535) return fail(PKV_EUNSUPPORTED, "too many partitions; raise partition_tokens");
+  return PKV_OK;
+}
+
+size_t workspace_for(const Plan& plan, int32_t num_seqs, int32_t num_heads, int32_t head_dim) {
+  if (plan.num_parts <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * num_heads * plan.num_parts;
+  return rows * (2 + (size_t)head_dim) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_paged_attn_workspace_bytes(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_heads,
+                                      int32_t max_context_len, const pkv_decode_opts* opts) {
+  Plan plan;
+  if (make_plan(pool, num_seqs, num_heads, max_context_len, opts, &plan) != PKV_OK) return 0;
+  return workspace_for(plan, num_seqs, num_heads, pool->head_dim);
+}
+
+pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 const pkv_pool_desc* pool, float scale, int32_t out_dtype, void* out,
+                                 void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts,
+                                 void* stream) {
+  Plan plan;
+  pkv_status st = make_plan(pool, num_seqs, num_heads, max_context_len, opts, &plan);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return ok();
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
+    return fail(PKV_EINVAL, "a data pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return fail(PKV_EINVAL, "q, pools and out must be 16-byte aligned");
+  if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "max_blocks_per_seq must be positive");
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * pool->block_size)
+    return fail(PKV_EINVAL, "max_context_len exceeds max_blocks_per_seq * block_size");
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale must be finite");
+  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return fail(PKV_EINVAL, "out_dtype must be F32 or BF16");
+  if (pool->dtype == PKV_F32 && out_dtype != PKV_F32) return fail(PKV_EUNSUPPORTED, "f32 inputs need an f32 output");
+  const size_t need = workspace_for(plan, num_seqs, num_heads, pool->head_dim);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(PKV_EWORKSPACE, "workspace missing, misaligned or smaller than pkv_paged_attn_workspace_bytes()");
+
+  pkv::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = pool->num_blocks;
+  a.max_context = max_context_len;
+  a.blocks_per_part = plan.blocks_per_part;
+  a.num_parts = plan.num_parts;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.out_bf16 = out_dtype == PKV_BF16;
+  if (plan.num_parts > 1) {
+    const size_t rows = (size_t)num_seqs * num_heads * plan.num_parts;
+    float* ws = static_cast<float*>(workspace);
+    a.ws_m = ws;
+    a.ws_l = ws + rows;
+    a.ws_acc = ws + 2 * rows;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int bf16 = pool->dtype == PKV_BF16;
+  hipError_t e = plan.mfma ? pkv::launch_decode_mfma(a, pool->head_dim, pool->block_size, plan.group, s)
+                           : pkv::launch_decode_vector(a, bf16, pool->head_dim, pool->block_size, plan.group, s);
+  if (e != hipSuccess) return fail(PKV_EHIP, std::string("decode launch: ") + hipGetErrorString(e));
+  if (plan.num_parts > 1) {
+    e = pkv::launch_splitk_reduce(a, pool->head_dim, pool->block_size, s);
+    if (e != hipSuccess) return fail(PKV_EHIP, std::string("reduce launch: ") + hipGetErrorString(e));
+  }
+  return ok();
+}
+
+pkv_status pkv_reshape_and_cache(const void* k, const void* v, int64_t k_token_stride, int64_t v_token_stride,
+                                 const int32_t* slot_mapping, int32_t num_tokens, void* k_pool, void* v_pool,
+                                 const pkv_pool_desc* pool, void* stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens must be >= 0");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping || !k_pool || !v_pool) return fail(PKV_EINVAL, "a data pointer is NULL");
+  const int elt = elt_bytes(pool->dtype);
+  const int x = 16 / elt;
+  const int64_t dense = (int64_t)pool->num_kv_heads * pool->head_dim;
+  const int64_t ks = k_token_stride == 0 ? dense : k_token_stride;
+  const int64_t vs = v_token_stride == 0 ? dense : v_token_stride;
+  if (ks < dense || vs < dense || ks % x || vs % x)
+    return fail(PKV_EINVAL, "token strides must be >= num_kv_heads*head_dim and a multiple of 16 bytes");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PKV_EINVAL, "k, v and pools must be 16-byte aligned");
+  hipError_t e = pkv::launch_reshape_and_cache(k, v, ks, vs, slot_mapping, num_tokens, k_pool, v_pool,
+                                               pool->num_blocks, pool->num_kv_heads, pool->block_size,
+                                               pool->head_dim, elt, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_EHIP, std::string("reshape_and_cache launch: ") + hipGetErrorString(e));
+  return ok();
+}
+
+pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_dst_pairs, int32_t num_pairs,
+                           const pkv_pool_desc* pool, void* stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return fail(PKV_EINVAL, "num_pairs must be >= 0");
+  if (num_pairs == 0) return ok();
+  if (!k_pool || !v_pool || !src_dst_pairs) return fail(PKV_EINVAL, "a data pointer is NULL");
+  if (!aligned16(k_pool) || !aligned16(v_pool)) return fail(PKV_EINVAL, "pools must be 16-byte aligned");
+  const int64_t block_bytes =
+      (int64_t)pool->num_kv_heads * pool->block_size * pool->head_dim * elt_bytes(pool->dtype);
+  hipError_t e = pkv::launch_copy_blocks(k_pool, v_pool, src_dst_pairs, num_pairs, pool->num_blocks, block_bytes,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_EHIP, std::string("copy_blocks launch: ") + hipGetErrorString(e));
+  return ok();
+}
+
+const char* pkv_status_string(pkv_status status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_EUNSUPPORTED: return "unsupported shape or type";
+    case PKV_EWORKSPACE: return "workspace missing or too small";
+    case PKV_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+int32_t pkv_version(void) { return 100; }
+
+}  // extern "C"

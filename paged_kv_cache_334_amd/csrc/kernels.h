@@ -1,0 +1,51 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kWaves = 4;  // waves per workgroup in the decode kernels
+
+// Everything a decode kernel reads, passed by value as the kernel argument.
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks;       // row stride of block_tables
+  int32_t num_blocks;       // pool size, for the block id range check
+  int32_t max_context;      // host bound of context_lens; a longer context makes its rows NaN
+  int32_t blocks_per_part;  // split-K partition length in blocks
+  int32_t num_parts;        // partitions allotted per sequence (grid x)
+  float scale_log2;         // scale * log2(e): logits are kept in the base-2 domain
+  void* out;
+  int32_t out_bf16;
+  // Partials when num_parts > 1, each indexed by (b*num_heads + h)*num_parts + part:
+  // ws_m (running max, base 2), ws_l (sum of exp2(s - m)), ws_acc (HD floats each).
+  float* ws_m;
+  float* ws_l;
+  float* ws_acc;
+};
+
+bool vector_supported(int dtype_bf16, int head_dim, int block_size, int group);
+bool mfma_supported(int dtype_bf16, int head_dim, int block_size, int group);
+
+hipError_t launch_decode_vector(const DecodeArgs& a, int dtype_bf16, int head_dim, int block_size, int group,
+                                hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, int block_size, int group, hipStream_t stream);
+hipError_t launch_splitk_reduce(const DecodeArgs& a, int head_dim, int block_size, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* k, const void* v, int64_t k_stride, int64_t v_stride,
+                                    const int32_t* slots, int32_t num_tokens, void* k_pool, void* v_pool,
+                                    int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                                    int32_t elt_bytes, hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t num_pairs,
+                              int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
+
+}  // namespace pkv

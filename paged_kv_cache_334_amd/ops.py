@@ -1,0 +1,195 @@
+"""ctypes binding of libpkv (C ABI in include/pkv.h), same entry-point names.
+
+Argument marshalling only: tensors become device pointers, shapes become the
+pool descriptor, and the current HIP stream of torch is passed through.  Every
+step of the computation runs in the library's kernels.  Importing this module
+raises ImportError when libpkv.so has not been built (``python -m
+paged_kv_cache_334_amd.build``); there is no fallback.
+
+Pool tensors use the library layout: keys ``[N, Hkv, D/x, bs, x]`` and values
+``[N, Hkv, D, bs]`` with ``x = 16 / element bytes`` (see ``new_pools``).
+"""
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m paged_kv_cache_334_amd.build`")
+lib = ctypes.CDLL(_LIB_PATH)
+
+PKV_F32, PKV_BF16 = 0, 1
+KERNELS = {"auto": 0, "vector": 1, "mfma": 2}
+STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP"}
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_blocks", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+lib.pkv_paged_attn_workspace_bytes.restype = _sz
+lib.pkv_paged_attn_workspace_bytes.argtypes = [ctypes.POINTER(PoolDesc), _i32, _i32, _i32, ctypes.POINTER(DecodeOpts)]
+lib.pkv_paged_attn_decode.restype = _i32
+lib.pkv_paged_attn_decode.argtypes = [
+    _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, ctypes.POINTER(PoolDesc), ctypes.c_float, _i32, _vp, _vp, _sz,
+    ctypes.POINTER(DecodeOpts), _vp,
+]
+lib.pkv_reshape_and_cache.restype = _i32
+lib.pkv_reshape_and_cache.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp, ctypes.POINTER(PoolDesc), _vp]
+lib.pkv_copy_blocks.restype = _i32
+lib.pkv_copy_blocks.argtypes = [_vp, _vp, _vp, _i32, ctypes.POINTER(PoolDesc), _vp]
+lib.pkv_status_string.restype = ctypes.c_char_p
+lib.pkv_status_string.argtypes = [_i32]
+lib.pkv_last_error.restype = ctypes.c_char_p
+lib.pkv_last_error.argtypes = []
+lib.pkv_version.restype = _i32
+lib.pkv_version.argtypes = []
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        detail = lib.pkv_last_error().decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({detail})")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return lib.pkv_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise PkvError(status, where)
+
+
+def _elem(t: torch.Tensor) -> int:
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return PKV_BF16
+    if t.dtype in (torch.float32, torch.int32):
+        return PKV_F32
+    raise TypeError(f"unsupported element type {t.dtype}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def pool_desc(k_pool: torch.Tensor, v_pool: torch.Tensor) -> PoolDesc:
+    """Descriptor from pool tensors shaped ``[N, Hkv, D/x, bs, x]`` and ``[N, Hkv, D, bs]``."""
+    if k_pool.dim() != 5 or v_pool.dim() != 4:
+        raise ValueError("k_pool must be [N, Hkv, D/x, bs, x] and v_pool [N, Hkv, D, bs]")
+    n, hkv, dx, bs, x = k_pool.shape
+    if tuple(v_pool.shape) != (n, hkv, dx * x, bs) or k_pool.dtype != v_pool.dtype:
+        raise ValueError("key and value pools disagree")
+    if not (k_pool.is_contiguous() and v_pool.is_contiguous()):
+        raise ValueError("pools must be contiguous")
+    dt = _elem(k_pool)
+    if x * (2 if dt == PKV_BF16 else 4) != 16:
+        raise ValueError("last key-pool axis must hold 16 bytes")
+    return PoolDesc(n, hkv, bs, dx * x, dt)
+
+
+def new_pools(num_blocks, num_kv_heads, block_size, head_dim, dtype=torch.bfloat16, device="cuda", fill=None):
+    """Allocate key/value pools in the library layout (torch allocates; the
+    library never does).  ``fill`` is an optional raw bit pattern."""
+    x = 16 // torch.tensor([], dtype=dtype).element_size()
+    k = torch.empty((num_blocks, num_kv_heads, head_dim // x, block_size, x), dtype=dtype, device=device)
+    v = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype, device=device)
+    if fill is not None:
+        bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+        val = fill - (1 << 16) if (bits == torch.int16 and fill >= 1 << 15) else fill
+        k.view(bits).fill_(val)
+        v.view(bits).fill_(val)
+    return k, v
+
+
+def paged_attn_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, max_context_len, partition_tokens=0,
+                               kernel="auto") -> int:
+    desc = pool_desc(k_pool, v_pool)
+    opts = DecodeOpts(partition_tokens, KERNELS[kernel])
+    return int(lib.pkv_paged_attn_workspace_bytes(ctypes.byref(desc), num_seqs, num_heads, max_context_len,
+                                                  ctypes.byref(opts)))
+
+
+def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, max_context_len=None,
+                      workspace=None, partition_tokens=0, kernel="auto", out_dtype=None, stream=None):
+    """``out[b, h] = softmax(scale * q[b, h] . K^T) . V`` over sequence b's
+    paged keys/values.  ``q`` is ``[B, Hq, D]``; ``block_tables`` ``[B, max_blocks]``
+    int32; ``context_lens`` ``[B]`` int32.  ``max_context_len`` is a host-side
+    upper bound (default ``max_blocks * block_size``).  Allocates ``out`` and the
+    workspace with torch when they are not given."""
+    desc = pool_desc(k_pool, v_pool)
+    nseq, nh, hd = q.shape
+    if hd != desc.head_dim or _elem(q) != desc.dtype:
+        raise ValueError("q does not match the pools")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if not (q.is_contiguous() and block_tables.is_contiguous() and context_lens.is_contiguous()):
+        raise ValueError("q, block_tables and context_lens must be contiguous")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * desc.block_size
+    if out is None:
+        odt = q.dtype if out_dtype is None else out_dtype
+        out = torch.empty((nseq, nh, hd), dtype=odt, device=q.device)
+    odt_code = PKV_BF16 if out.dtype == torch.bfloat16 else PKV_F32
+    opts = DecodeOpts(int(partition_tokens), KERNELS[kernel])
+    need = int(lib.pkv_paged_attn_workspace_bytes(ctypes.byref(desc), nseq, nh, int(max_context_len),
+                                                  ctypes.byref(opts)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pkv_paged_attn_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens), nseq,
+                                   nh, max_blocks, int(max_context_len), ctypes.byref(desc), float(scale), odt_code,
+                                   _ptr(out), _ptr(workspace), ws_bytes, ctypes.byref(opts), _stream(stream))
+    _check(st, "pkv_paged_attn_decode")
+    return out
+
+
+def reshape_and_cache(k, v, slot_mapping, k_pool, v_pool, stream=None):
+    """Write ``k, v [T, Hkv, D]`` (token axis may be strided) into the pools at
+    ``slot_mapping [T]`` int32 (negative = skip)."""
+    desc = pool_desc(k_pool, v_pool)
+    if slot_mapping.dtype != torch.int32 or not slot_mapping.is_contiguous():
+        raise TypeError("slot_mapping must be contiguous int32")
+    t = k.shape[0]
+    for x in (k, v):
+        if x.dim() != 3 or x.shape[1:] != (desc.num_kv_heads, desc.head_dim) or _elem(x) != desc.dtype:
+            raise ValueError("k/v must be [T, Hkv, D] of the pool's element type")
+        if x.stride(2) != 1 or x.stride(1) != desc.head_dim:
+            raise ValueError("k/v rows must be dense within a token")
+    if v.shape[0] != t or slot_mapping.shape[0] != t:
+        raise ValueError("k, v and slot_mapping lengths differ")
+    st = lib.pkv_reshape_and_cache(_ptr(k), _ptr(v), k.stride(0), v.stride(0), _ptr(slot_mapping), t, _ptr(k_pool),
+                                   _ptr(v_pool), ctypes.byref(desc), _stream(stream))
+    _check(st, "pkv_reshape_and_cache")
+
+
+def copy_blocks(k_pool, v_pool, src_dst_pairs, stream=None):
+    """Copy whole blocks of both pools: ``src_dst_pairs [P, 2]`` int32 on the device."""
+    desc = pool_desc(k_pool, v_pool)
+    if src_dst_pairs.dtype != torch.int32 or not src_dst_pairs.is_contiguous():
+        raise TypeError("src_dst_pairs must be contiguous int32")
+    p = src_dst_pairs.shape[0] if src_dst_pairs.numel() else 0
+    st = lib.pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(src_dst_pairs) if p else None, p, ctypes.byref(desc),
+                             _stream(stream))
+    _check(st, "pkv_copy_blocks")

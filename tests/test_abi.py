@@ -1,0 +1,117 @@
+"""The C ABI library, without a GPU: it loads, exports every entry point the
+header declares, and rejects bad host-side arguments before launching
+anything (these paths return before the first HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+LIB = os.path.join(ROOT, "paged_kv_cache_334_amd", "libpkv.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libpkv.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("pkv_paged_attn_decode", "pkv_reshape_and_cache", "pkv_copy_blocks"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from paged_kv_cache_334_amd import ops
+
+    return ops
+
+
+def test_status_strings(ops):
+    assert ops.status_string(0) == "ok"
+    assert ops.status_string(3) == "workspace missing or too small"
+    assert ops.lib.pkv_version() >= 100
+
+
+def _desc(ops, **kw):
+    base = dict(num_blocks=64, num_kv_heads=8, block_size=16, head_dim=128, dtype=ops.PKV_BF16)
+    base.update(kw)
+    return ops.PoolDesc(**base)
+
+
+def _decode(ops, desc, num_heads=32, max_ctx=256, ptr=16, opts=None, out_dtype=None, ws=0, ws_bytes=0,
+            max_blocks=16, scale=0.1):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    od = desc.dtype if out_dtype is None else out_dtype
+    return ops.lib.pkv_paged_attn_decode(p, p, p, p, p, 4, num_heads, max_blocks, max_ctx, ctypes.byref(desc), scale,
+                                         od, p, ctypes.c_void_p(ws) if ws else None, ws_bytes,
+                                         ctypes.byref(opts) if opts else None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_size=8), 2),
+    (dict(block_size=64), 2),
+    (dict(head_dim=96), 2),
+    (dict(dtype=7), 2),
+    (dict(num_blocks=0), 1),
+    (dict(num_blocks=(1 << 31) // 16), 1),
+])
+def test_bad_pool_is_rejected(ops, kw, status):
+    assert _decode(ops, _desc(ops, **kw)) == status
+    assert ops.lib.pkv_last_error().decode()
+
+
+def test_bad_decode_arguments(ops):
+    d = _desc(ops)
+    assert _decode(ops, d, num_heads=12) == 1            # not a multiple of kv heads
+    assert _decode(ops, d, num_heads=8 * 3) == 2         # group of 3 is not built
+    assert _decode(ops, d, ptr=0) == 1                   # NULL pointers
+    assert _decode(ops, d, ptr=8) == 1                   # misaligned
+    assert _decode(ops, d, max_ctx=16 * 16 + 1) == 1     # beyond max_blocks * block_size
+    assert _decode(ops, d, scale=float("inf")) == 1
+    assert _decode(ops, _desc(ops, dtype=ops.PKV_F32), out_dtype=ops.PKV_BF16) == 2
+    assert _decode(ops, d, opts=ops.DecodeOpts(0, 9)) == 1
+    assert _decode(ops, _desc(ops, num_kv_heads=32), opts=ops.DecodeOpts(0, 2)) == 2  # MFMA needs a group of 4/8
+
+
+def test_workspace_is_required_for_split(ops):
+    d = _desc(ops)
+    opts = ops.DecodeOpts(64, 0)
+    need = ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(opts))
+    assert need == 4 * 32 * 4 * (128 + 2) * 4  # 4 partitions of 64 tokens
+    assert _decode(ops, d, opts=opts) == 3
+    assert _decode(ops, d, opts=opts, ws=16, ws_bytes=need - 4) == 3
+    single = ops.DecodeOpts(1 << 30, 0)
+    assert ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(single)) == 0
+
+
+def test_zero_sequences_is_a_no_op(ops):
+    d = _desc(ops)
+    st = ops.lib.pkv_paged_attn_decode(None, None, None, None, None, 0, 32, 16, 256, ctypes.byref(d), 0.1, 1, None,
+                                       None, 0, None, None)
+    assert st == 0
+
+
+def test_cache_op_arguments(ops):
+    d = _desc(ops)
+    p = ctypes.c_void_p(16)
+    assert ops.lib.pkv_reshape_and_cache(p, p, 0, 0, p, -1, p, p, ctypes.byref(d), None) == 1
+    assert ops.lib.pkv_reshape_and_cache(p, p, 100, 0, p, 4, p, p, ctypes.byref(d), None) == 1  # stride too small
+    assert ops.lib.pkv_reshape_and_cache(None, p, 0, 0, p, 4, p, p, ctypes.byref(d), None) == 1
+    assert ops.lib.pkv_reshape_and_cache(p, p, 0, 0, p, 0, p, p, ctypes.byref(d), None) == 0  # nothing to do
+    assert ops.lib.pkv_copy_blocks(p, p, None, 3, ctypes.byref(d), None) == 1
+    assert ops.lib.pkv_copy_blocks(p, p, p, -2, ctypes.byref(d), None) == 1
+    assert ops.lib.pkv_copy_blocks(p, p, None, 0, ctypes.byref(d), None) == 0

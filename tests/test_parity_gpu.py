@@ -1,0 +1,214 @@
+"""HIP path against the CPU oracle, through the C ABI (needs an MI355X).
+
+* Cache ops: after the whole step (cached tokens, copy-on-write copies, new
+  tokens), both pools must equal the oracle's pools bit for bit, every element
+  (NaN-poisoned tails and unused blocks included).
+* Attention: every output of small cases that still span several blocks,
+  partitions and a ragged tail; sampled outputs at the full workload sizes in
+  the launch configuration the benchmark uses.  Tolerances in
+  gpu_harness.check_attention.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle_pins as pins
+from gpu_harness import GpuWorkload, check_attention, out_to_f64, to_bits
+from logical_model import oracle_pools
+from paged_kv_cache_334_amd.workloads import ORDER, WorkloadSpec, generate
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from paged_kv_cache_334_amd import ops  # noqa: F401  (fails loudly when the library is missing)
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+SMALL = {
+    # float32, the tiny configuration itself
+    "tiny-f32": lambda: generate("tiny-f32"),
+    # bf16 MHA, head_dim 128, block 16, ragged lengths up to 300
+    "mha-small": lambda: generate("mha-7b", num_seqs=5, ctx=(1, 300), num_heads=4, num_kv_heads=4),
+    # bf16, head_dim 64, two query heads per kv head
+    "g2-d64": lambda: generate("mha-7b", num_seqs=3, ctx=(1, 200), num_heads=4, num_kv_heads=2, head_dim=64),
+    # bf16 GQA, group 8, block 16
+    "gqa-small": lambda: generate("gqa-70b", num_seqs=4, ctx=(1, 600), num_heads=16, num_kv_heads=2),
+    # bf16 GQA, group 4, block 32, outlier keys
+    "long-small": lambda: generate("long-32k", num_seqs=2, ctx=(2000, 3000), num_heads=8, num_kv_heads=2,
+                                   outlier_fraction=0.01),
+    # shared prefix with copy-on-write, group 4
+    "prefix-small": lambda: generate("shared-prefix", num_seqs=12, shared_prefix=512, ctx=(16, 100),
+                                     num_heads=8, num_kv_heads=2, cow_fraction=0.25),
+    # float32 GQA, head_dim 128, block 32
+    "f32-g4-bs32": lambda: generate(WorkloadSpec("f32-g4", "f32", 3, 8, 2, 128, 32, (1, 150), seed=7)),
+}
+
+VARIANTS = [  # (kernel, partition tokens)
+    ("auto", 0),
+    ("vector", 1 << 30),
+    ("vector", 64),
+    ("mfma", 1 << 30),
+    ("mfma", 96),
+    ("auto", 32),
+]
+
+
+@pytest.fixture(scope="module", params=sorted(SMALL))
+def small_case(request):
+    name = request.param
+    _say(f"[small] building {name}")
+    wl = SMALL[name]()
+    gw = GpuWorkload(wl)
+    pools = oracle_pools(wl)
+    ref = oracle.paged_decode(wl.q, pools[1], pools[2], pools[0], wl.block_tables, wl.context_lens, wl.scale)
+    return name, wl, gw, pools, ref
+
+
+def test_small_cache_ops_bit_exact(small_case):
+    name, wl, gw, (desc, k_ref, v_ref), _ = small_case
+    _say(f"[small] cache ops {name}")
+    assert np.array_equal(to_bits(gw.k_pool), k_ref), "key pool differs"
+    assert np.array_equal(to_bits(gw.v_pool), v_ref), "value pool differs"
+
+
+@pytest.mark.parametrize("kernel,ptoks", VARIANTS)
+@pytest.mark.parametrize("out_dtype", ["same", "f32"])
+def test_small_decode(small_case, kernel, ptoks, out_dtype):
+    name, wl, gw, _, ref = small_case
+    g = wl.spec.group
+    if kernel == "mfma" and not (wl.dtype == "bf16" and wl.spec.head_dim == 128 and g in (4, 8)):
+        pytest.skip("MFMA kernel needs bf16, head_dim 128, group 4 or 8")
+    if out_dtype == "f32" and wl.dtype == "f32":
+        pytest.skip("same as 'same'")
+    _say(f"[small] decode {name} kernel={kernel} partition={ptoks} out={out_dtype}")
+    odt = torch.float32 if out_dtype == "f32" else None
+    out = gw.decode(kernel=kernel, partition_tokens=ptoks, out_dtype=odt)
+    torch.cuda.synchronize()
+    check_attention(out_to_f64(out), ref, wl.dtype, "f32" if (odt is not None or wl.dtype == "f32") else "bf16",
+                    f"{name}/{kernel}/{ptoks}")
+
+
+def test_small_deterministic(small_case):
+    name, wl, gw, _, _ = small_case
+    _say(f"[small] determinism {name}")
+    a = to_bits(gw.decode(partition_tokens=64))
+    b = to_bits(gw.decode(partition_tokens=64))
+    assert np.array_equal(a, b)
+
+
+def test_placement_invariance_gpu():
+    """Renaming physical blocks leaves the GPU output bit-identical (the kernel's
+    order of work follows logical positions, not physical ids)."""
+    wl = SMALL["gqa-small"]()
+    _say("[inv] placement")
+    a = to_bits(GpuWorkload(wl).decode(partition_tokens=128))
+    b = to_bits(GpuWorkload(pins.relabel_blocks(wl, 3)).decode(partition_tokens=128))
+    assert np.array_equal(a, b)
+
+
+def test_shared_equals_private_gpu():
+    wl = SMALL["prefix-small"]()
+    _say("[inv] shared vs private")
+    a = to_bits(GpuWorkload(wl).decode())
+    b = to_bits(GpuWorkload(pins.private_copy(wl)).decode())
+    assert np.array_equal(a, b)
+
+
+def test_single_token_exact_gpu():
+    """context length 1: the weight is exactly 1 and the output is the value row, bit for bit."""
+    wl = generate("gqa-70b", num_seqs=3, ctx=(1, 1, 1), ctx_is_list=True, num_heads=16, num_kv_heads=2)
+    _say("[edge] single token")
+    gw = GpuWorkload(wl)
+    for kernel in ("vector", "mfma"):
+        out = to_bits(gw.decode(kernel=kernel)).reshape(wl.q.shape)
+        for b in range(3):
+            v = wl.new_v[b]  # [Hkv, D] bits of the only token
+            assert np.array_equal(out[b], np.repeat(v, 8, axis=0)), kernel
+
+
+def test_empty_context_gives_zeros_gpu():
+    wl = SMALL["mha-small"]()
+    _say("[edge] empty context")
+    gw = GpuWorkload(wl)
+    ctx = gw.context_lens.clone()
+    ctx[2] = 0
+    gw.context_lens = ctx
+    for ptoks in (0, 32):
+        out = out_to_f64(gw.decode(partition_tokens=ptoks))
+        assert (out[2] == 0).all()
+        assert np.isfinite(out).all()
+
+
+def test_bad_block_id_gives_nan_not_a_fault():
+    """An out-of-range block id (a broken precondition) is caught by the
+    kernel's range check: that sequence's rows become NaN, others are intact."""
+    wl = SMALL["gqa-small"]()
+    _say("[edge] bad block id")
+    gw = GpuWorkload(wl)
+    good = gw.block_tables
+    bad = good.clone()
+    bad[1, 0] = wl.num_blocks + 5
+    for kernel in ("vector", "mfma"):
+        gw.block_tables = good
+        ref = out_to_f64(gw.decode(partition_tokens=64, kernel=kernel))
+        gw.block_tables = bad
+        out = out_to_f64(gw.decode(partition_tokens=64, kernel=kernel))
+        assert np.isnan(out[1]).all(), kernel
+        keep = [0, 2, 3]
+        assert np.array_equal(out[keep], ref[keep]), kernel
+
+
+# ---- full sizes ---------------------------------------------------------------------
+
+@pytest.fixture(scope="module", params=ORDER)
+def full_case(request):
+    name = request.param
+    _say(f"[full] building {name}")
+    wl = generate(name)
+    gw = GpuWorkload(wl)
+    _say(f"[full] oracle pools {name}")
+    pools = oracle_pools(wl)
+    return name, wl, gw, pools
+
+
+def _sample_pairs(wl, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    ctx = wl.context_lens
+    seqs = {int(np.argmax(ctx)), int(np.argmin(ctx))}
+    seqs |= set(rng.integers(0, wl.spec.num_seqs, size=n // 4).tolist())
+    pairs = set()
+    for b in seqs:
+        for h in rng.choice(wl.spec.num_heads, size=min(4, wl.spec.num_heads), replace=False).tolist():
+            pairs.add((b, int(h)))
+    first = int(np.argmax(ctx))
+    for h in range(wl.spec.num_heads):  # every head of the longest sequence
+        pairs.add((first, h))
+    return sorted(pairs)
+
+
+def test_full_cache_ops_bit_exact(full_case):
+    name, wl, gw, (desc, k_ref, v_ref) = full_case
+    _say(f"[full] cache ops {name}")
+    assert np.array_equal(to_bits(gw.k_pool), k_ref), "key pool differs"
+    assert np.array_equal(to_bits(gw.v_pool), v_ref), "value pool differs"
+
+
+@pytest.mark.parametrize("out_dtype", ["same", "f32"])
+def test_full_decode_sampled(full_case, out_dtype):
+    name, wl, gw, (desc, k_pool, v_pool) = full_case
+    if out_dtype == "f32" and wl.dtype == "f32":
+        pytest.skip("same")
+    _say(f"[full] decode {name} out={out_dtype}")
+    odt = torch.float32 if out_dtype == "f32" else None
+    out = out_to_f64(gw.decode(out_dtype=odt))  # the benchmark's launch configuration (automatic plan)
+    assert np.isfinite(out).all()
+    pairs = _sample_pairs(wl)
+    ref = oracle.paged_decode(wl.q, k_pool, v_pool, desc, wl.block_tables, wl.context_lens, wl.scale, pairs=pairs)
+    got = np.stack([out[b, h] for b, h in pairs])
+    check_attention(got, ref, wl.dtype, "f32" if (odt is not None or wl.dtype == "f32") else "bf16",
+                    f"{name}/full")
