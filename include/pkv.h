@@ -9,9 +9,9 @@
  *    Attention for LLM Inference", section "How Paged Attention Works: The
  *    Mechanics", items 1-3; "PagedAttention Explained", section "Block Tables
  *    and Non-Contiguous Storage").
- *  - Decode attention walks each sequence's block table, loads its blocks and
- *    attends over the concatenated keys and values, without first gathering
- *    them into contiguous memory ("PagedAttention Explained", sections "Block
+ *  - Decode attention follows each sequence's block table, reads its blocks and
+ *    attends over their keys and values in logical order, with no gather into
+ *    contiguous memory first ("PagedAttention Explained", sections "Block
  *    Tables and Non-Contiguous Storage" and the closing remark of
  *    "Implementing a Simplified Paged KV Cache").
  *  - A new token's key and value go to row `length % block_size` of the last

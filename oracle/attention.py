@@ -2,9 +2,10 @@
 
 Definition followed.  At a decode step the model produces one token per
 sequence and attends over every token the sequence already holds ("PagedAttention
-Explained", section "What Is the KV Cache?").  The kernel "walks the block
-table, loads the relevant blocks, and computes attention over the concatenated
-keys and values" (same page, "Block Tables and Non-Contiguous Storage"), and
+Explained", section "What Is the KV Cache?").  The attention kernel follows the
+block table, reads each block it names and attends over all of those keys and
+values joined in logical order (same page, "Block Tables and Non-Contiguous
+Storage"), and
 paging changes only where the cache lives, not what attention returns ("What is
 PagedAttention", aitechboss.com, "Step 3: Use Page Tables Instead of Continuous
 Memory"; "Master Paged Attention for LLM Inference", FAQ "Does Paged Attention

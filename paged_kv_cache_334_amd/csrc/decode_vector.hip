@@ -2,9 +2,9 @@
 // reductions, float32 online softmax.  Used for float32 pools and for small
 // query groups, where the grouped q x K tile is too thin for matrix cores.
 //
-// The kernel walks the block table of one (sequence, kv head, partition) and
-// reads each block's tile straight from the pool: attention over the
-// concatenated keys and values without gathering them first ("PagedAttention
+// The kernel follows the block table of one (sequence, kv head, partition) and
+// reads each block's tile straight from the pool, so attention covers the
+// sequence's keys and values in logical order with no gather step ("PagedAttention
 // Explained", "Block Tables and Non-Contiguous Storage").  The running
 // max / sum form of softmax is the exact tiling of FlashAttention ("Paged
 // Attention" glossary, related term "FlashAttention"; "Master Paged Attention

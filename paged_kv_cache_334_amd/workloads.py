@@ -13,7 +13,7 @@ Bookkeeping rules ("PagedAttention Explained", agentechip.com, section
 
 * a new block is taken from the front of the free list when a sequence's
   length is a multiple of ``block_size``; an empty free list raises
-  "KV cache exhausted";
+  an error (CacheExhausted);
 * the token goes to row ``length % block_size`` of the last block of the
   sequence's table; here that becomes its slot ``block * block_size + row``;
 * freeing a sequence decrements each block's reference count and returns the
@@ -61,7 +61,7 @@ class BlockManager:
 
     def _take(self) -> int:
         if not self.free:
-            raise CacheExhausted("KV cache exhausted: no free blocks available.")
+            raise CacheExhausted("block pool is empty: cannot give the sequence a new block")
         blk = self.free.popleft()
         self.ref[blk] += 1
         return blk

@@ -257,7 +257,7 @@ def test_cache_exhausted():
     mgr.allocate_sequence(0)
     for _ in range(32):
         mgr.append_slot(0)
-    with pytest.raises(CacheExhausted, match="KV cache exhausted"):
+    with pytest.raises(CacheExhausted, match="block pool is empty"):
         mgr.append_slot(0)
 
 
