@@ -92,6 +92,9 @@ typedef struct {
    * above max_context_len means one pass with no partials and no reduce. */
   int32_t partition_tokens;
   int32_t kernel; /* pkv_kernel */
+  /* Blocks whose key/value tiles one wave loads before it uses the first:
+   * 0 = chosen by the library, else 1 or 2. */
+  int32_t blocks_in_flight;
 } pkv_decode_opts;
 
 /* Bytes of workspace pkv_paged_attn_decode needs for these shapes and options

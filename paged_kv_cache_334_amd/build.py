@@ -29,6 +29,9 @@ FLAGS = [
     "-Wno-unused-result",
     # packed float32 instructions are left to no part of this library
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the decode kernels rescale and
+    # read them between instructions, which the AGPR form turns into copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -41,12 +41,17 @@ pkv_status check_pool(const pkv_pool_desc* pool) {
   return PKV_OK;
 }
 
+// Workgroups a decode launch should reach before it is worth splitting
+// sequences: two per CU of the 256 on MI355X.
+constexpr int64_t kTargetWorkgroups = 512;
+
 // Partition plan of one decode call.
 struct Plan {
   bool mfma = false;
   int group = 1;
   int blocks_per_part = 1;
   int num_parts = 1;
+  int inflight = 1;
 };
 
 pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_heads, int32_t max_context_len,
@@ -72,18 +77,35 @@ pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_he
 
   const int bs = pool->block_size;
   const int max_blocks = (max_context_len + bs - 1) / bs;
+  const int tile_bytes = bs * pool->head_dim * elt_bytes(pool->dtype);
+  const int inflight = opts ? opts->blocks_in_flight : 0;
+  if (inflight < 0 || inflight > 2) return fail(PKV_EINVAL, "blocks_in_flight must be 0, 1 or 2");
+  // two blocks of 4 KiB tiles in flight per wave, one block of larger tiles
+  plan->inflight = inflight ? inflight : (tile_bytes <= 4096 ? 2 : 1);
   int64_t part_tokens = opts ? opts->partition_tokens : 0;
   if (part_tokens < 0) return fail(PKV_EINVAL, "partition_tokens must be >= 0");
+  int64_t bpp;
   if (part_tokens == 0) {
-    // Automatic: aim for about 2048 workgroups (8 per CU) but never fewer than
-    // 2 blocks per wave; contexts up to 512 tokens stay in one pass.
+    // Automatic.  One pass per (sequence, kv head) when that already gives
+    // kTargetWorkgroups workgroups: a split costs a second kernel, the partials'
+    // traffic and a prologue/epilogue per workgroup, and measured slower than a
+    // single long walk whenever the GPU is already full.  Fewer units (long
+    // contexts, small batches) are split into equal partitions until about
+    // kTargetWorkgroups exist, each wave keeping at least two rounds of
+    // in-flight blocks.
     const int64_t units = (int64_t)num_seqs * pool->num_kv_heads;
-    int64_t want_parts = units > 0 ? (2048 + units - 1) / units : 1;
-    int64_t tokens = (max_context_len + want_parts - 1) / (want_parts > 0 ? want_parts : 1);
-    const int64_t floor_tokens = 512;
-    part_tokens = tokens < floor_tokens ? floor_tokens : tokens;
+    const int64_t round = (int64_t)pkv::kWaves * plan->inflight;
+    if (units >= kTargetWorkgroups || max_blocks <= 2 * round) {
+      bpp = max_blocks > 0 ? max_blocks : 1;
+    } else {
+      const int64_t parts = (kTargetWorkgroups + units - 1) / units;
+      bpp = (max_blocks + parts - 1) / parts;
+      if (bpp < 2 * round) bpp = 2 * round;
+      bpp = (bpp + round - 1) / round * round;
+    }
+  } else {
+    bpp = (part_tokens + bs - 1) / bs;
   }
-  int64_t bpp = (part_tokens + bs - 1) / bs;
   if (bpp < 1) bpp = 1;
   if (bpp >= max_blocks) bpp = max_blocks > 0 ? max_blocks : 1;
   plan->blocks_per_part = (int)bpp;
@@ -147,6 +169,7 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
   a.max_context = max_context_len;
   a.blocks_per_part = plan.blocks_per_part;
   a.num_parts = plan.num_parts;
+  a.longest_first = num_seqs > 1 && num_seqs <= pkv::kMaxRankSeqs;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = out;
   a.out_bf16 = out_dtype == PKV_BF16;
@@ -159,8 +182,9 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int bf16 = pool->dtype == PKV_BF16;
-  hipError_t e = plan.mfma ? pkv::launch_decode_mfma(a, pool->head_dim, pool->block_size, plan.group, s)
-                           : pkv::launch_decode_vector(a, bf16, pool->head_dim, pool->block_size, plan.group, s);
+  hipError_t e = plan.mfma ? pkv::launch_decode_mfma(a, pool->head_dim, pool->block_size, plan.group, plan.inflight, s)
+                           : pkv::launch_decode_vector(a, bf16, pool->head_dim, pool->block_size, plan.group,
+                                                       plan.inflight, s);
   if (e != hipSuccess) return fail(PKV_EHIP, std::string("decode launch: ") + hipGetErrorString(e));
   if (plan.num_parts > 1) {
     e = pkv::launch_splitk_reduce(a, pool->head_dim, pool->block_size, s);
@@ -222,6 +246,6 @@ const char* pkv_status_string(pkv_status status) {
 
 const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
-int32_t pkv_version(void) { return 100; }
+int32_t pkv_version(void) { return 200; }
 
 }  // extern "C"

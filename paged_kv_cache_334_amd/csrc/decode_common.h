@@ -1,0 +1,224 @@
+// Pieces shared by the two decode kernel families (vector and matrix-core):
+// the partition a workgroup owns, the block-id prefetch, and the merge of the
+// per-wave softmax states into an output row or a split-K partial.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+// Longest sequences first.  Workgroups are dispatched in grid order, so when
+// the sequence slot blockIdx.z names the slot-th longest sequence (ties by
+// index), the long walks start first and the tail of the launch is short ones
+// (largest-first scheduling).  Every workgroup ranks the context lengths itself
+// (one candidate per thread, num_seqs <= kMaxRankSeqs), which costs one
+// dependent load of the lengths; the host enables it for more than one sequence.
+
+struct SeqPick {
+  int b;
+  int ctx_raw;
+};
+
+__device__ __forceinline__ SeqPick pick_sequence(const DecodeArgs& a, int* sm_key, int* sm_pick) {
+  if (!a.longest_first) {
+    SeqPick p;
+    p.b = blockIdx.z;
+    p.ctx_raw = a.context_lens[p.b];
+    return p;
+  }
+  const int t = threadIdx.x;
+  const int nb = a.num_seqs;
+  int raw = 0, key = 0;
+  if (t < nb) {
+    raw = a.context_lens[t];
+    key = (raw < 0 || raw > a.max_context) ? -1 : raw;  // broken lengths rank last
+    sm_key[t] = key;
+  }
+  __syncthreads();
+  if (t < nb) {
+    int rank = 0;
+    for (int o = 0; o < nb; ++o) {
+      const int ko = sm_key[o];
+      rank += (ko > key) | ((ko == key) & (o < t));
+    }
+    if (rank == (int)blockIdx.z) {
+      sm_pick[0] = t;
+      sm_pick[1] = raw;
+    }
+  }
+  __syncthreads();
+  SeqPick p;
+  p.b = sm_pick[0];
+  p.ctx_raw = sm_pick[1];
+  return p;
+}
+
+// The (sequence, kv head, partition) a workgroup owns: grid = (partitions, kv
+// heads, sequence slots), the slot mapped to a sequence by pick_sequence.
+struct PartRange {
+  int b, kvh, part;
+  int ctx;      // context length (0 when context_lens[b] breaks its precondition)
+  bool ctx_bad; // context_lens[b] < 0 or > max_context: the rows become NaN and nothing is read
+  int nblocks;  // blocks of the sequence
+  int nparts;   // partitions the sequence spans
+  int blk_lo, blk_hi;
+};
+
+template <int BS>
+__device__ __forceinline__ PartRange part_range(const DecodeArgs& a, const SeqPick& s) {
+  PartRange r;
+  r.part = blockIdx.x;
+  r.kvh = blockIdx.y;
+  r.b = s.b;
+  const int ctx_raw = s.ctx_raw;
+  r.ctx_bad = ctx_raw < 0 || ctx_raw > a.max_context;
+  r.ctx = r.ctx_bad ? 0 : ctx_raw;
+  r.nblocks = (r.ctx + BS - 1) / BS;
+  r.nparts = (r.nblocks + a.blocks_per_part - 1) / a.blocks_per_part;
+  r.blk_lo = r.part * a.blocks_per_part;
+  r.blk_hi = min(r.nblocks, r.blk_lo + a.blocks_per_part);
+  return r;
+}
+
+// A workgroup past its sequence's last partition has nothing to read.  The one
+// at partition 0 of an empty context writes the all-zero rows (NaN rows for a
+// broken context length).  Returns true when the workgroup is done.
+template <int G, int HD>
+__device__ __forceinline__ bool finish_if_empty(const DecodeArgs& a, const PartRange& r) {
+  if (r.part < r.nparts) return false;
+  if (r.part == 0) {
+    for (int idx = threadIdx.x; idx < G * HD; idx += blockDim.x) {
+      const int64_t o = ((int64_t)r.b * a.num_heads + r.kvh * G + idx / HD) * HD + idx % HD;
+      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = r.ctx_bad ? 0x7fc0 : 0;
+      else reinterpret_cast<float*>(a.out)[o] = r.ctx_bad ? NAN : 0.f;
+    }
+  }
+  return true;
+}
+
+// Blocks of a partition are dealt to the waves round-robin: wave w takes
+// partition blocks w, w + kWaves, w + 2*kWaves, ...; this is how many it gets.
+__device__ __forceinline__ int wave_block_count(const PartRange& r, int wave) {
+  const int n = r.blk_hi - r.blk_lo;
+  return n > wave ? (n - wave + kWaves - 1) / kWaves : 0;
+}
+
+// Block ids of one wave's blocks, 64 at a time: lane l holds the id of the
+// wave's block 64*chunk + l.  One strided vector load per 64 blocks, then
+// readlane; no tile load waits on a table lookup.
+struct WaveIds {
+  const int32_t* row;  // table entry of the wave's first block
+  int limit;           // entries row[kWaves*i] with kWaves*i < limit lie inside the table row
+  int chunk;
+  int ids;
+};
+
+// Started before the context length is known, so the table load overlaps the
+// context-length load.  Entries past the sequence's last block may be read
+// (they are inside the row of max_blocks entries) but never used.
+__device__ __forceinline__ WaveIds wave_ids_begin(const DecodeArgs& a, int b, int wave, int lane) {
+  WaveIds w;
+  const int first = blockIdx.x * a.blocks_per_part + wave;
+  w.row = a.block_tables + (int64_t)b * a.max_blocks + first;
+  w.limit = a.max_blocks - first;
+  w.chunk = 0;
+  w.ids = kWaves * lane < w.limit ? w.row[kWaves * lane] : 0;
+  return w;
+}
+
+// Checks the ids of the current chunk that the wave will use (its first cnt
+// blocks): returns 1 when one lies outside the pool, and replaces it by block 0
+// so that no load ever leaves the pool (the row turns NaN instead).
+__device__ __forceinline__ int wave_ids_check(const DecodeArgs& a, WaveIds* w, int cnt, int lane) {
+  const int used = cnt - 64 * w->chunk;
+  const bool out = lane < used && (unsigned)w->ids >= (unsigned)a.num_blocks;
+  if (out) w->ids = 0;
+  return __ballot(out) != 0;
+}
+
+// Id of the wave's block i (i never decreases between calls).
+__device__ __forceinline__ int wave_id_at(const DecodeArgs& a, WaveIds* w, int i, int cnt, int lane, int* bad) {
+  const int c = i >> 6;
+  if (c != w->chunk) {
+    w->chunk = c;
+    const int idx = kWaves * (64 * c + lane);
+    w->ids = idx < w->limit ? w->row[idx] : 0;
+    *bad |= wave_ids_check(a, w, cnt, lane);
+  }
+  return __builtin_amdgcn_readlane(w->ids, i & 63);
+}
+
+// Double-buffered walk over a wave's rounds of tiles: the loads of the next
+// round are in flight while the current one is computed.  The steady-state
+// loop always issues before it computes, and the last one or two rounds are
+// peeled, so every path into a compute has the same number of younger loads
+// outstanding and the wait before it covers only the round it uses.
+template <typename Tile, typename Issue, typename Compute>
+__device__ __forceinline__ void pipelined_rounds(int rounds, Tile* ta, Tile* tb, Issue&& issue, Compute&& compute) {
+  if (rounds <= 0) return;
+  issue(ta, 0);
+  int rnd = 0;
+  for (; rnd + 2 < rounds; rnd += 2) {
+    issue(tb, rnd + 1);
+    compute(ta, rnd);
+    issue(ta, rnd + 2);
+    compute(tb, rnd + 1);
+  }
+  if (rnd + 1 < rounds) {
+    issue(tb, rnd + 1);
+    compute(ta, rnd);
+    compute(tb, rnd + 1);
+  } else {
+    compute(ta, rnd);
+  }
+}
+
+// Per-wave softmax states in LDS, merged by the whole workgroup:
+//   M = max_w m_w,  l = sum_w 2^(m_w - M) l_w,  acc = sum_w 2^(m_w - M) acc_w
+// (logits in base 2).  A sequence inside one partition gets its output row
+// acc / l (rounded to nearest even for bf16); otherwise the partial (M, l, acc)
+// goes to the workspace for the split-K merge.  A bad block id anywhere in the
+// partition turns the row into NaN.
+template <int G, int HD, int NW>
+__device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const PartRange& r,
+                                                      float (*sm_acc)[G][HD], float (*sm_m)[G], float (*sm_l)[G],
+                                                      const int* sm_bad) {
+  int any_bad = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) any_bad |= sm_bad[w];
+  const int h0 = r.kvh * G;
+  for (int idx = threadIdx.x; idx < G * HD; idx += 64 * NW) {
+    const int h = idx / HD, d = idx % HD;
+    float big_m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][h]);
+    float l = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = (sm_m[w][h] == -INFINITY) ? 0.f : fast_exp2(sm_m[w][h] - big_m);
+      l = fmaf(f, sm_l[w][h], l);
+      acc = fmaf(f, sm_acc[w][h][d], acc);
+    }
+    if (any_bad) {
+      big_m = NAN;
+      acc = NAN;
+    }
+    const int hq = h0 + h;
+    if (r.nparts == 1) {
+      const float o = acc / l;
+      const int64_t oi = ((int64_t)r.b * a.num_heads + hq) * HD + d;
+      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_rne(o);
+      else reinterpret_cast<float*>(a.out)[oi] = o;
+    } else {
+      const int64_t pi = ((int64_t)r.b * a.num_heads + hq) * a.num_parts + r.part;
+      a.ws_acc[pi * HD + d] = acc;
+      if (d == 0) {
+        a.ws_m[pi] = big_m;
+        a.ws_l[pi] = l;
+      }
+    }
+  }
+}
+
+}  // namespace pkv

@@ -25,57 +25,49 @@
 // G..2G-1 carry lo of the same heads (their q columns are duplicated), and the
 // two output columns are added at the end.  The weight then keeps ~16
 // significant bits instead of 8.
-#include "common.h"
-#include "kernels.h"
+//
+// Memory side as in the vector kernel (block ids per 64 blocks, broadcast with
+// readlane; double-buffered rounds), with the 16-token sub-tile as the unit: a
+// round is U sub-tiles, i.e. U blocks of 16 tokens or U/2 blocks of 32.
+#include "decode_common.h"
 
 namespace pkv {
 
-template <int BS, int G>
+template <int BS, int G, int U>
 __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NW = kWaves;
   constexpr int HD = 128;
-  constexpr int TILE_ELEMS = HD * BS;
+  constexpr int SUB = BS / 16;  // 16-token sub-tiles per block
+  constexpr int TILE_BYTES = HD * BS * 2;
   static_assert(2 * G <= 16, "group too large for one 16-column tile");
+  static_assert(64 % ((U + SUB - 1) / SUB) == 0, "a round must not straddle two id loads");
+
+  struct Tile {
+    uint4 k[4];  // keys of the sub-tile's 16 tokens, MFMA A-operand order
+    uint2 v[8];  // values, 16 dims x 4 tokens per instruction
+  };
 
   __shared__ float sm_acc[NW][G][HD];
   __shared__ float sm_m[NW][G];
   __shared__ float sm_l[NW][G];
   __shared__ int sm_bad[NW];
+  __shared__ int sm_key[kMaxRankSeqs];
+  __shared__ int sm_pick[2];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
-  const int ctx_raw = a.context_lens[b];
-  const bool ctx_bad = ctx_raw < 0 || ctx_raw > a.max_context;  // broken precondition: NaN rows, no reads
-  const int ctx = ctx_bad ? 0 : ctx_raw;
-  const int nblocks = (ctx + BS - 1) / BS;
-  const int nparts = (nblocks + a.blocks_per_part - 1) / a.blocks_per_part;
-  const int h0 = kvh * G;
-
-  if (part >= nparts) {
-    if (part == 0) {  // empty context: the output row is zero (NaN for a broken context length)
-      for (int idx = threadIdx.x; idx < G * HD; idx += 64 * NW) {
-        const int64_t o = ((int64_t)b * a.num_heads + h0 + idx / HD) * HD + idx % HD;
-        if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = ctx_bad ? 0x7fc0 : 0;
-        else reinterpret_cast<float*>(a.out)[o] = ctx_bad ? NAN : 0.f;
-      }
-    }
-    return;
-  }
-  const int blk_lo = part * a.blocks_per_part;
-  const int blk_hi = min(nblocks, blk_lo + a.blocks_per_part);
-
+  const int wave = uniform(threadIdx.x >> 6);
   const int n = lane & 15;   // MFMA column: head slot (S^T, O^T) / row: token (K) or dim (V)
   const int kg = lane >> 4;  // lane group
   const bool used = n < 2 * G;
   const bool lo_slot = n >= G;
   const int hslot = n % G;
 
+  const SeqPick seq = pick_sequence(a, sm_key, sm_pick);
+  WaveIds wids = wave_ids_begin(a, seq.b, wave, lane);
   bf16x8 qb[4];
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.num_heads + h0 + hslot) * HD;
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)seq.b * a.num_heads + blockIdx.y * G + hslot) * HD;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint4 w = used ? load16(qrow + 32 * i + 8 * kg) : make_uint4(0, 0, 0, 0);
@@ -83,54 +75,69 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
     }
   }
 
+  const PartRange r = part_range<BS>(a, seq);
+  if (finish_if_empty<G, HD>(a, r)) return;
+  const int cnt = wave_block_count(r, wave);
+  int bad = wave_ids_check(a, &wids, cnt, lane);
+
   f32x4 o[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
-  int bad = 0;
 
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
-  for (int j = blk_lo + wave; j < blk_hi; j += NW) {
-    const int blk = uniform(bt[j]);
-    if ((unsigned)blk >= (unsigned)a.num_blocks) {
-      bad = 1;
-      continue;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (int64_t)r.kvh * TILE_BYTES;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)r.kvh * TILE_BYTES;
+  const int64_t block_bytes = (int64_t)a.num_kv_heads * TILE_BYTES;
+  const int units = cnt * SUB;
+
+  // loads of round rnd: sub-tiles rnd*U .. rnd*U+U-1 of the wave (a missing one
+  // re-reads the wave's last sub-tile, a cache hit, and is not used)
+  auto issue = [&](Tile* T, int rnd) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int x = min(rnd * U + u, units - 1);
+      const int sub = x % SUB;
+      const int64_t off = (int64_t)wave_id_at(a, &wids, x / SUB, cnt, lane, &bad) * block_bytes;
+      const auto kt = tile_rsrc(kbase + off, TILE_BYTES);
+      const auto vt = tile_rsrc(vbase + off, TILE_BYTES);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) T[u].k[i] = bload16(kt, ((4 * i + kg) * BS + 16 * sub + n) * 16);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) T[u].v[nt] = bload8(vt, ((16 * nt + n) * BS + 16 * sub + 4 * kg) * 2);
     }
-    const int64_t tile = ((int64_t)blk * a.num_kv_heads + kvh) * TILE_ELEMS;
-    const uint16_t* kt = reinterpret_cast<const uint16_t*>(a.k_pool) + tile;
-    const uint16_t* vt = reinterpret_cast<const uint16_t*>(a.v_pool) + tile;
+  };
+
+  auto compute = [&](Tile* T, int rnd) {
 #pragma unroll
-    for (int half = 0; half < BS / 16; ++half) {
-      const int t0 = half * 16;
-      const int valid = ctx - j * BS - t0;
-      if (valid <= 0) break;
-      uint4 kr[4];
-      uint2 vr[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kr[i] = load16(kt + ((4 * i + kg) * BS + t0 + n) * 8);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) vr[nt] = load8(vt + (16 * nt + n) * BS + t0 + 4 * kg);
+    for (int u = 0; u < U; ++u) {
+      const int x = rnd * U + u;
+      if (x >= units) break;
+      const int j = r.blk_lo + wave + NW * (x / SUB);  // logical block
+      const int valid = r.ctx - j * BS - 16 * (x % SUB);
+      if (valid <= 0) continue;  // second half of a block past the context
 
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[i]), qb[i], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T[u].k[i]), qb[i], s, 0, 0, 0);
 
       float sr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sr[r] = (4 * kg + r < valid) ? s[r] * a.scale_log2 : -INFINITY;
+      for (int rr = 0; rr < 4; ++rr) sr[rr] = (4 * kg + rr < valid) ? s[rr] * a.scale_log2 : -INFINITY;
       float mx = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float mn = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - mn);
+      mx = max_xor32(max_xor16(mx));  // per column (head slot)
+      if (__ballot(mx > m + kRescaleSlack) != 0) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - mn);
+        lsum *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) o[nt] *= alpha;
+        m = mn;
+      }
       float p[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sr[r] - mn);
-      lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-      m = mn;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) o[nt] *= alpha;
+      for (int rr = 0; rr < 4; ++rr) p[rr] = fast_exp2(sr[rr] - m);
+      lsum += (p[0] + p[1]) + (p[2] + p[3]);
 
       uint32_t pw[2];
 #pragma unroll
@@ -151,29 +158,31 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
         const int first = 4 * kg;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
-          uint32_t w0 = vr[nt].x, w1 = vr[nt].y;
+          uint32_t w0 = T[u].v[nt].x, w1 = T[u].v[nt].y;
           if (first + 0 >= valid) w0 &= 0xffff0000u;
           if (first + 1 >= valid) w0 &= 0x0000ffffu;
           if (first + 2 >= valid) w1 &= 0xffff0000u;
           if (first + 3 >= valid) w1 &= 0x0000ffffu;
-          vr[nt] = make_uint2(w0, w1);
+          T[u].v[nt] = make_uint2(w0, w1);
         }
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt)
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vr[nt]), pb, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, T[u].v[nt]), pb, o[nt], 0, 0, 0);
     }
-  }
+  };
+
+  Tile ta[U], tb[U];
+  pipelined_rounds((units + U - 1) / U, ta, tb, issue, compute);
 
   // wave totals: weight sum over the 4 lane groups; hi + lo columns of each head
-  float l = lsum + shfl_xor(lsum, 16);
-  l += shfl_xor(l, 32);
+  const float l = sum_xor32(sum_xor16(lsum));
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float other = shfl(o[nt][r], (lane + G) & 63);
-      if (n < G) sm_acc[wave][n][16 * nt + 4 * kg + r] = o[nt][r] + other;
+    for (int rr = 0; rr < 4; ++rr) {
+      const float other = shfl(o[nt][rr], (lane + G) & 63);
+      if (n < G) sm_acc[wave][n][16 * nt + 4 * kg + rr] = o[nt][rr] + other;
     }
   }
   if (kg == 0 && n < G) {
@@ -182,57 +191,30 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
   }
   if (lane == 0) sm_bad[wave] = bad;
   __syncthreads();
-
-  int any_bad = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) any_bad |= sm_bad[w];
-  for (int idx = threadIdx.x; idx < G * HD; idx += 64 * NW) {
-    const int h = idx / HD, d = idx % HD;
-    float big_m = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][h]);
-    float lt = 0.f, r = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = (sm_m[w][h] == -INFINITY) ? 0.f : fast_exp2(sm_m[w][h] - big_m);
-      lt = fmaf(f, sm_l[w][h], lt);
-      r = fmaf(f, sm_acc[w][h][d], r);
-    }
-    if (any_bad) {
-      big_m = NAN;
-      r = NAN;
-    }
-    const int hq = h0 + h;
-    if (nparts == 1) {
-      const float ov = r / lt;
-      const int64_t oi = ((int64_t)b * a.num_heads + hq) * HD + d;
-      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_rne(ov);
-      else reinterpret_cast<float*>(a.out)[oi] = ov;
-    } else {
-      const int64_t pi = ((int64_t)b * a.num_heads + hq) * a.num_parts + part;
-      a.ws_acc[pi * HD + d] = r;
-      if (d == 0) {
-        a.ws_m[pi] = big_m;
-        a.ws_l[pi] = lt;
-      }
-    }
-  }
+  merge_waves_and_store<G, HD, NW>(a, r, sm_acc, sm_m, sm_l, sm_bad);
 }
 
 bool mfma_supported(int bf16, int hd, int bs, int g) {
   return bf16 && hd == 128 && (bs == 16 || bs == 32) && (g == 4 || g == 8);
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int hd, int bs, int g, hipStream_t s) {
-  if (hd != 128) return hipErrorInvalidValue;
+template <int U>
+static hipError_t launch_u(const DecodeArgs& a, int bs, int g, hipStream_t s) {
   const dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
   const dim3 block(64 * kWaves);
-  if (bs == 16 && g == 4) hipLaunchKernelGGL((decode_mfma_kernel<16, 4>), grid, block, 0, s, a);
-  else if (bs == 16 && g == 8) hipLaunchKernelGGL((decode_mfma_kernel<16, 8>), grid, block, 0, s, a);
-  else if (bs == 32 && g == 4) hipLaunchKernelGGL((decode_mfma_kernel<32, 4>), grid, block, 0, s, a);
-  else if (bs == 32 && g == 8) hipLaunchKernelGGL((decode_mfma_kernel<32, 8>), grid, block, 0, s, a);
+  if (bs == 16 && g == 4) hipLaunchKernelGGL((decode_mfma_kernel<16, 4, U>), grid, block, 0, s, a);
+  else if (bs == 16 && g == 8) hipLaunchKernelGGL((decode_mfma_kernel<16, 8, U>), grid, block, 0, s, a);
+  else if (bs == 32 && g == 4) hipLaunchKernelGGL((decode_mfma_kernel<32, 4, U>), grid, block, 0, s, a);
+  else if (bs == 32 && g == 8) hipLaunchKernelGGL((decode_mfma_kernel<32, 8, U>), grid, block, 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int hd, int bs, int g, int inflight, hipStream_t s) {
+  if (hd != 128) return hipErrorInvalidValue;
+  if (inflight == 1) return launch_u<1>(a, bs, g, s);
+  if (inflight == 2) return launch_u<2>(a, bs, g, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv

@@ -11,24 +11,31 @@
 // for LLM Inference", "Optimizing Further").
 //
 // Work split.  Workgroup = kWaves waves = one (partition, kv head, sequence).
-// Wave w takes blocks blk_lo + w, blk_lo + w + kWaves, ...  Within a wave:
+// Wave w takes the partition's blocks w, w + kWaves, ...  Their ids come in
+// with one vector load per 64 of them (lane l holds the id of the wave's l-th
+// block) and are broadcast with readlane, so no tile load waits on a table
+// lookup.  The wave works in rounds of U blocks, double-buffered: the tile
+// loads of round r+1 are issued before round r is computed, so the wave always
+// has loads in flight.  Within a round:
 //  * key pass: lane = (token t = lane % BS, lane group grp = lane / BS); the
 //    lane loads 16-byte chunks grp, grp + 64/BS, ... of token t's key row
-//    (each chunk is BS*16 bytes away from the next in the key tile, and the
-//    16 or 32 lanes of one chunk read BS*16 contiguous bytes), multiplies with
-//    q in float32, and the 64/BS lane groups are summed with xor shuffles;
+//    (the 16 or 32 lanes of one chunk read BS*16 contiguous bytes of the key
+//    tile), multiplies with q in float32 (bf16 pairs through the dot2
+//    instruction, which returns a float32 sum), and the 64/BS lane groups are
+//    summed with xor shuffles;
 //  * value pass: the tile is dim-major [D][BS]; lane reads 16-byte chunks
 //    lane, lane + 64, ... (fully contiguous per instruction), i.e. X tokens of
 //    one dim, and needs the weights of those X tokens, fetched by shuffles
 //    from the lanes that computed them.
 // Each wave keeps (max, sum, acc) per query head; the waves merge through LDS
 // and the workgroup writes the output row (one partition) or a partial.
-#include "common.h"
-#include "kernels.h"
+#include "decode_common.h"
 
 namespace pkv {
 
-template <bool BF16, int HD, int BS, int G>
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <bool BF16, int HD, int BS, int G, int U>
 __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a) {
   constexpr int NW = kWaves;
   constexpr int ELT = BF16 ? 2 : 4;
@@ -40,62 +47,50 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
   constexpr int VC = HD * RC / 64;  // value chunks per lane per block
   constexpr int TILE_BYTES = HD * BS * ELT;
   static_assert(NC % GK == 0 && (HD * RC) % 64 == 0 && RC >= 1, "shape");
+  static_assert(64 % U == 0, "a round must not straddle two id loads");
+
+  struct Tile {
+    uint4 k[KC];
+    uint4 v[VC];
+  };
 
   __shared__ float sm_acc[NW][G][HD];
   __shared__ float sm_m[NW][G];
   __shared__ float sm_l[NW][G];
   __shared__ int sm_bad[NW];
+  __shared__ int sm_key[kMaxRankSeqs];
+  __shared__ int sm_pick[2];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
-  const int ctx_raw = a.context_lens[b];
-  const bool ctx_bad = ctx_raw < 0 || ctx_raw > a.max_context;  // broken precondition: NaN rows, no reads
-  const int ctx = ctx_bad ? 0 : ctx_raw;
-  const int nblocks = (ctx + BS - 1) / BS;
-  const int nparts = (nblocks + a.blocks_per_part - 1) / a.blocks_per_part;
-  const int h0 = kvh * G;
-
-  if (part >= nparts) {
-    if (part == 0) {  // empty context: the output row is zero (NaN for a broken context length)
-      for (int idx = threadIdx.x; idx < G * HD; idx += 64 * NW) {
-        const int64_t o = ((int64_t)b * a.num_heads + h0 + idx / HD) * HD + idx % HD;
-        if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = ctx_bad ? 0x7fc0 : 0;
-        else reinterpret_cast<float*>(a.out)[o] = ctx_bad ? NAN : 0.f;
-      }
-    }
-    return;
-  }
-  const int blk_lo = part * a.blocks_per_part;
-  const int blk_hi = min(nblocks, blk_lo + a.blocks_per_part);
-
+  const int wave = uniform(threadIdx.x >> 6);
   const int t = lane % BS;
   const int grp = lane / BS;
   const int tk = (lane % RC) * X;  // first token of this lane's value chunks
 
-  // q in float32, the chunks this lane meets in the key pass
-  float qf[G][KC][X];
+  // Issued together before the context length is known: the wave's first
+  // block ids (table entries past the sequence's end may be read, never used)
+  // and q.
+  const SeqPick seq = pick_sequence(a, sm_key, sm_pick);
+  WaveIds wids = wave_ids_begin(a, seq.b, wave, lane);
+  uint32_t qw[G][KC][4];  // the q chunks this lane meets in the key pass (bf16 pairs kept packed)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const char* qrow = reinterpret_cast<const char*>(a.q) + ((int64_t)b * a.num_heads + h0 + h) * HD * ELT;
+    const char* qrow =
+        reinterpret_cast<const char*>(a.q) + ((int64_t)seq.b * a.num_heads + blockIdx.y * G + h) * HD * ELT;
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
       const uint4 w = load16(qrow + (grp + GK * i) * 16);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      if constexpr (BF16) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qf[h][i][2 * e] = bf16_lo(ws[e]);
-          qf[h][i][2 * e + 1] = bf16_hi(ws[e]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qf[h][i][e] = __uint_as_float(ws[e]);
-      }
+      qw[h][i][0] = w.x;
+      qw[h][i][1] = w.y;
+      qw[h][i][2] = w.z;
+      qw[h][i][3] = w.w;
     }
   }
+
+  const PartRange r = part_range<BS>(a, seq);
+  if (finish_if_empty<G, HD>(a, r)) return;
+  const int cnt = wave_block_count(r, wave);  // blocks of this wave
+  int bad = wave_ids_check(a, &wids, cnt, lane);
 
   float m[G], lsum[G], acc[G][VC];
 #pragma unroll
@@ -105,102 +100,129 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
 #pragma unroll
     for (int j = 0; j < VC; ++j) acc[h][j] = 0.f;
   }
-  int bad = 0;
 
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
-  for (int j = blk_lo + wave; j < blk_hi; j += NW) {
-    const int blk = uniform(bt[j]);
-    if ((unsigned)blk >= (unsigned)a.num_blocks) {
-      bad = 1;
-      continue;
-    }
-    const int64_t tile = ((int64_t)blk * a.num_kv_heads + kvh) * TILE_BYTES;
-    const char* kt = reinterpret_cast<const char*>(a.k_pool) + tile;
-    const char* vt = reinterpret_cast<const char*>(a.v_pool) + tile;
-    uint4 kr[KC], vr[VC];
-#pragma unroll
-    for (int i = 0; i < KC; ++i) kr[i] = load16(kt + ((grp + GK * i) * BS + t) * 16);
-#pragma unroll
-    for (int jv = 0; jv < VC; ++jv) vr[jv] = load16(vt + (lane + 64 * jv) * 16);
-    const int valid = ctx - j * BS;  // rows of this block inside the context, >= 1
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (int64_t)r.kvh * TILE_BYTES;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)r.kvh * TILE_BYTES;
+  const int64_t block_bytes = (int64_t)a.num_kv_heads * TILE_BYTES;
 
-    // value elements as float32, with rows past the context set to 0 (they may hold NaN)
-    float vf[VC][X];
+  // loads of round rnd: the wave's blocks rnd*U .. rnd*U+U-1 (a missing one
+  // re-reads the wave's last block, a cache hit, and is not used)
+  auto issue = [&](Tile* T, int rnd) {
 #pragma unroll
-    for (int jv = 0; jv < VC; ++jv) {
-      const uint32_t ws[4] = {vr[jv].x, vr[jv].y, vr[jv].z, vr[jv].w};
-      if constexpr (BF16) {
+    for (int u = 0; u < U; ++u) {
+      const int i = min(rnd * U + u, cnt - 1);
+      const int64_t off = (int64_t)wave_id_at(a, &wids, i, cnt, lane, &bad) * block_bytes;
+      const auto kt = tile_rsrc(kbase + off, TILE_BYTES);
+      const auto vt = tile_rsrc(vbase + off, TILE_BYTES);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vf[jv][2 * e] = bf16_lo(ws[e]);
-          vf[jv][2 * e + 1] = bf16_hi(ws[e]);
-        }
-      } else {
+      for (int c = 0; c < KC; ++c) T[u].k[c] = bload16(kt, ((grp + GK * c) * BS + t) * 16);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vf[jv][e] = __uint_as_float(ws[e]);
-      }
+      for (int c = 0; c < VC; ++c) T[u].v[c] = bload16(vt, (lane + 64 * c) * 16);
     }
-    if (valid < BS) {
-#pragma unroll
-      for (int jv = 0; jv < VC; ++jv)
-#pragma unroll
-        for (int e = 0; e < X; ++e) vf[jv][e] = (tk + e < valid) ? vf[jv][e] : 0.f;
-    }
+  };
 
+  auto compute = [&](Tile* T, int rnd) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float s = 0.f;
+    for (int u = 0; u < U; ++u) {
+      const int i = rnd * U + u;
+      if (i >= cnt) break;
+      const int valid = r.ctx - (r.blk_lo + wave + NW * i) * BS;  // rows of this block inside the context, >= 1
+
+      // value rows past the context may hold NaN: clear their bits (a zero weight is not enough)
+      if (valid < BS) {
 #pragma unroll
-      for (int i = 0; i < KC; ++i) {
-        const uint32_t ws[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-        if constexpr (BF16) {
+        for (int c = 0; c < VC; ++c) {
+          uint32_t ws[4] = {T[u].v[c].x, T[u].v[c].y, T[u].v[c].z, T[u].v[c].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            s = fmaf(qf[h][i][2 * e], bf16_lo(ws[e]), s);
-            s = fmaf(qf[h][i][2 * e + 1], bf16_hi(ws[e]), s);
+            if constexpr (BF16) {
+              if (tk + 2 * e >= valid) ws[e] &= 0xffff0000u;
+              if (tk + 2 * e + 1 >= valid) ws[e] &= 0x0000ffffu;
+            } else {
+              if (tk + e >= valid) ws[e] = 0u;
+            }
           }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s = fmaf(qf[h][i][e], __uint_as_float(ws[e]), s);
+          T[u].v[c] = make_uint4(ws[0], ws[1], ws[2], ws[3]);
         }
       }
-#pragma unroll
-      for (int off = BS; off < 64; off <<= 1) s += shfl_xor(s, off);
-      s = (t < valid) ? s * a.scale_log2 : -INFINITY;
 
-      float mx = s;
 #pragma unroll
-      for (int off = 1; off < BS; off <<= 1) mx = fmaxf(mx, shfl_xor(mx, off));
-      const float mn = fmaxf(m[h], mx);
-      const float alpha = fast_exp2(m[h] - mn);
-      const float p = fast_exp2(s - mn);
-      lsum[h] = lsum[h] * alpha + p;
-      m[h] = mn;
-      float pv[X];
+      for (int h = 0; h < G; ++h) {
+        float s = 0.f, s2 = 0.f;
 #pragma unroll
-      for (int e = 0; e < X; ++e) pv[e] = shfl(p, tk + e);
+        for (int c = 0; c < KC; ++c) {
+          const uint32_t ws[4] = {T[u].k[c].x, T[u].k[c].y, T[u].k[c].z, T[u].k[c].w};
+          if constexpr (BF16) {
 #pragma unroll
-      for (int jv = 0; jv < VC; ++jv) {
-        float r = acc[h][jv] * alpha;
+            for (int e = 0; e < 4; e += 2) {
+              s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][c][e]),
+                                                  __builtin_bit_cast(bf16x2, ws[e]), s, false);
+              s2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][c][e + 1]),
+                                                   __builtin_bit_cast(bf16x2, ws[e + 1]), s2, false);
+            }
+          } else {
 #pragma unroll
-        for (int e = 0; e < X; ++e) r = fmaf(pv[e], vf[jv][e], r);
-        acc[h][jv] = r;
+            for (int e = 0; e < 4; e += 2) {
+              s = fmaf(__uint_as_float(qw[h][c][e]), __uint_as_float(ws[e]), s);
+              s2 = fmaf(__uint_as_float(qw[h][c][e + 1]), __uint_as_float(ws[e + 1]), s2);
+            }
+          }
+        }
+        s += s2;
+        // sum the lane groups of one token: lanes t, t+BS, ...
+        if constexpr (BS == 16) s = sum_xor32(sum_xor16(s));
+        else s = sum_xor32(s);
+        s = (t < valid) ? s * a.scale_log2 : -INFINITY;
+
+        float mx = row_max16(s);
+        if constexpr (BS == 32) mx = max_xor16(mx);
+        mx = __builtin_amdgcn_readfirstlane(mx);  // the same in every lane
+        if (mx > m[h] + kRescaleSlack) {
+          const float alpha = fast_exp2(m[h] - mx);
+          lsum[h] *= alpha;
+#pragma unroll
+          for (int c = 0; c < VC; ++c) acc[h][c] *= alpha;
+          m[h] = mx;
+        }
+        const float p = fast_exp2(s - m[h]);
+        lsum[h] += p;
+        float pv[X];
+#pragma unroll
+        for (int e = 0; e < X; ++e) pv[e] = shfl(p, tk + e);
+#pragma unroll
+        for (int c = 0; c < VC; ++c) {
+          const uint32_t ws[4] = {T[u].v[c].x, T[u].v[c].y, T[u].v[c].z, T[u].v[c].w};
+          float racc = acc[h][c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (BF16) {
+              racc = fmaf(pv[2 * e], bf16_lo(ws[e]), racc);
+              racc = fmaf(pv[2 * e + 1], bf16_hi(ws[e]), racc);
+            } else {
+              racc = fmaf(pv[e], __uint_as_float(ws[e]), racc);
+            }
+          }
+          acc[h][c] = racc;
+        }
       }
     }
-  }
+  };
 
-  // wave totals: sum over the BS token lanes and over the RC lanes sharing a dim
+  Tile ta[U], tb[U];
+  pipelined_rounds((cnt + U - 1) / U, ta, tb, issue, compute);
+
+  // wave totals: the weight sum over the tokens of lane group 0 (every group
+  // holds the same weights), and the RC lanes sharing a dim add their partial sums
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float l = lsum[h];
+    float l = row_sum16(lsum[h]);
+    if constexpr (BS == 32) l = sum_xor16(l);
 #pragma unroll
-    for (int off = 1; off < BS; off <<= 1) l += shfl_xor(l, off);
+    for (int c = 0; c < VC; ++c) {
+      float racc = acc[h][c];
 #pragma unroll
-    for (int jv = 0; jv < VC; ++jv) {
-      float r = acc[h][jv];
-#pragma unroll
-      for (int off = 1; off < RC; off <<= 1) r += shfl_xor(r, off);
-      if (lane % RC == 0) sm_acc[wave][h][(lane + 64 * jv) / RC] = r;
+      for (int off = 1; off < RC; off <<= 1) racc += shfl_xor(racc, off);
+      if (lane % RC == 0) sm_acc[wave][h][(lane + 64 * c) / RC] = racc;
     }
     if (lane == 0) {
       sm_m[wave][h] = m[h];
@@ -209,41 +231,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
   }
   if (lane == 0) sm_bad[wave] = bad;
   __syncthreads();
-
-  int any_bad = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) any_bad |= sm_bad[w];
-  for (int idx = threadIdx.x; idx < G * HD; idx += 64 * NW) {
-    const int h = idx / HD, d = idx % HD;
-    float big_m = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][h]);
-    float l = 0.f, r = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = (sm_m[w][h] == -INFINITY) ? 0.f : fast_exp2(sm_m[w][h] - big_m);
-      l = fmaf(f, sm_l[w][h], l);
-      r = fmaf(f, sm_acc[w][h][d], r);
-    }
-    if (any_bad) {
-      big_m = NAN;
-      r = NAN;
-    }
-    const int hq = h0 + h;
-    if (nparts == 1) {
-      const float o = r / l;
-      const int64_t oi = ((int64_t)b * a.num_heads + hq) * HD + d;
-      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_rne(o);
-      else reinterpret_cast<float*>(a.out)[oi] = o;
-    } else {
-      const int64_t pi = ((int64_t)b * a.num_heads + hq) * a.num_parts + part;
-      a.ws_acc[pi * HD + d] = r;
-      if (d == 0) {
-        a.ws_m[pi] = big_m;
-        a.ws_l[pi] = l;
-      }
-    }
-  }
+  merge_waves_and_store<G, HD, NW>(a, r, sm_acc, sm_m, sm_l, sm_bad);
 }
 
 bool vector_supported(int bf16, int hd, int bs, int g) {
@@ -251,31 +239,34 @@ bool vector_supported(int bf16, int hd, int bs, int g) {
   return (hd == 64 || hd == 128) && (bs == 16 || bs == 32) && (g == 1 || g == 2 || g == 4 || g == 8);
 }
 
-template <bool BF16, int HD, int BS>
+template <bool BF16, int HD, int BS, int U>
 static hipError_t dispatch_g(const DecodeArgs& a, int g, hipStream_t s) {
   const dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
   const dim3 block(64 * kWaves);
   switch (g) {
-    case 1: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 8>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 1, U>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 2, U>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 4, U>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 8, U>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <bool BF16>
+template <bool BF16, int U>
 static hipError_t dispatch_shape(const DecodeArgs& a, int hd, int bs, int g, hipStream_t s) {
-  if (hd == 64 && bs == 16) return dispatch_g<BF16, 64, 16>(a, g, s);
-  if (hd == 64 && bs == 32) return dispatch_g<BF16, 64, 32>(a, g, s);
-  if (hd == 128 && bs == 16) return dispatch_g<BF16, 128, 16>(a, g, s);
-  if (hd == 128 && bs == 32) return dispatch_g<BF16, 128, 32>(a, g, s);
+  if (hd == 64 && bs == 16) return dispatch_g<BF16, 64, 16, U>(a, g, s);
+  if (hd == 64 && bs == 32) return dispatch_g<BF16, 64, 32, U>(a, g, s);
+  if (hd == 128 && bs == 16) return dispatch_g<BF16, 128, 16, U>(a, g, s);
+  if (hd == 128 && bs == 32) return dispatch_g<BF16, 128, 32, U>(a, g, s);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode_vector(const DecodeArgs& a, int bf16, int hd, int bs, int g, hipStream_t s) {
-  return bf16 ? dispatch_shape<true>(a, hd, bs, g, s) : dispatch_shape<false>(a, hd, bs, g, s);
+hipError_t launch_decode_vector(const DecodeArgs& a, int bf16, int hd, int bs, int g, int inflight,
+                                hipStream_t s) {
+  if (inflight == 1) return bf16 ? dispatch_shape<true, 1>(a, hd, bs, g, s) : dispatch_shape<false, 1>(a, hd, bs, g, s);
+  if (inflight == 2) return bf16 ? dispatch_shape<true, 2>(a, hd, bs, g, s) : dispatch_shape<false, 2>(a, hd, bs, g, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv

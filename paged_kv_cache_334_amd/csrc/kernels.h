@@ -6,7 +6,8 @@
 
 namespace pkv {
 
-constexpr int kWaves = 4;  // waves per workgroup in the decode kernels
+constexpr int kWaves = 4;          // waves per workgroup in the decode kernels
+constexpr int kMaxRankSeqs = 256;  // most sequences the decode kernels order longest-first (one per thread)
 
 // Everything a decode kernel reads, passed by value as the kernel argument.
 struct DecodeArgs {
@@ -23,6 +24,7 @@ struct DecodeArgs {
   int32_t max_context;      // host bound of context_lens; a longer context makes its rows NaN
   int32_t blocks_per_part;  // split-K partition length in blocks
   int32_t num_parts;        // partitions allotted per sequence (grid x)
+  int32_t longest_first;    // map sequence slots to sequences by decreasing context length
   float scale_log2;         // scale * log2(e): logits are kept in the base-2 domain
   void* out;
   int32_t out_bf16;
@@ -36,9 +38,11 @@ struct DecodeArgs {
 bool vector_supported(int dtype_bf16, int head_dim, int block_size, int group);
 bool mfma_supported(int dtype_bf16, int head_dim, int block_size, int group);
 
+// inflight = blocks whose tiles one wave loads before using the first (1 or 2)
 hipError_t launch_decode_vector(const DecodeArgs& a, int dtype_bf16, int head_dim, int block_size, int group,
-                                hipStream_t stream);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, int block_size, int group, hipStream_t stream);
+                                int inflight, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, int block_size, int group, int inflight,
+                              hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeArgs& a, int head_dim, int block_size, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, int64_t k_stride, int64_t v_stride,

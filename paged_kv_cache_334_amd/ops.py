@@ -36,7 +36,7 @@ class PoolDesc(ctypes.Structure):
 
 
 class DecodeOpts(ctypes.Structure):
-    _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+    _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("blocks_in_flight", ctypes.c_int32)]
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -123,15 +123,16 @@ def new_pools(num_blocks, num_kv_heads, block_size, head_dim, dtype=torch.bfloat
 
 
 def paged_attn_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, max_context_len, partition_tokens=0,
-                               kernel="auto") -> int:
+                               kernel="auto", blocks_in_flight=0) -> int:
     desc = pool_desc(k_pool, v_pool)
-    opts = DecodeOpts(partition_tokens, KERNELS[kernel])
+    opts = DecodeOpts(partition_tokens, KERNELS[kernel], blocks_in_flight)
     return int(lib.pkv_paged_attn_workspace_bytes(ctypes.byref(desc), num_seqs, num_heads, max_context_len,
                                                   ctypes.byref(opts)))
 
 
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, max_context_len=None,
-                      workspace=None, partition_tokens=0, kernel="auto", out_dtype=None, stream=None):
+                      workspace=None, partition_tokens=0, kernel="auto", out_dtype=None, stream=None,
+                      blocks_in_flight=0):
     """``out[b, h] = softmax(scale * q[b, h] . K^T) . V`` over sequence b's
     paged keys/values.  ``q`` is ``[B, Hq, D]``; ``block_tables`` ``[B, max_blocks]``
     int32; ``context_lens`` ``[B]`` int32.  ``max_context_len`` is a host-side
@@ -152,7 +153,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=
         odt = q.dtype if out_dtype is None else out_dtype
         out = torch.empty((nseq, nh, hd), dtype=odt, device=q.device)
     odt_code = PKV_BF16 if out.dtype == torch.bfloat16 else PKV_F32
-    opts = DecodeOpts(int(partition_tokens), KERNELS[kernel])
+    opts = DecodeOpts(int(partition_tokens), KERNELS[kernel], int(blocks_in_flight))
     need = int(lib.pkv_paged_attn_workspace_bytes(ctypes.byref(desc), nseq, nh, int(max_context_len),
                                                   ctypes.byref(opts)))
     if workspace is None and need > 0:
@@ -193,3 +194,38 @@ def copy_blocks(k_pool, v_pool, src_dst_pairs, stream=None):
     st = lib.pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(src_dst_pairs) if p else None, p, ctypes.byref(desc),
                              _stream(stream))
     _check(st, "pkv_copy_blocks")
+
+
+# measurement kernels (include/pkv_probe.h)
+lib.pkv_probe_read.restype = _i32
+lib.pkv_probe_read.argtypes = [_vp, _sz, _vp, _i32, _vp]
+lib.pkv_probe_gather.restype = _i32
+lib.pkv_probe_gather.argtypes = [_vp, _vp, _i32, _i32, _vp, _i32, _vp]
+lib.pkv_probe_copy.restype = _i32
+lib.pkv_probe_copy.argtypes = [_vp, _vp, _sz, _i32, _vp]
+
+
+def _probe_check(st, where):
+    if st != 0:
+        raise RuntimeError(f"{where} returned {st}")
+
+
+def probe_read(buf, sink, num_workgroups, stream=None):
+    """Stream ``buf`` (any contiguous device tensor) once; ``sink`` holds
+    ``num_workgroups`` 32-bit words."""
+    _probe_check(lib.pkv_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), num_workgroups,
+                                    _stream(stream)), "pkv_probe_read")
+
+
+def probe_gather(pool, tile_ids, tile_bytes, sink, num_workgroups, stream=None):
+    """Read ``tile_ids.numel()`` tiles of ``tile_bytes`` from ``pool``."""
+    _probe_check(lib.pkv_probe_gather(_ptr(pool), _ptr(tile_ids), tile_ids.numel(), tile_bytes, _ptr(sink),
+                                      num_workgroups, _stream(stream)), "pkv_probe_gather")
+
+
+def probe_copy(src, dst, num_workgroups, stream=None):
+    """Copy ``src`` into ``dst`` (same byte size)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst sizes differ")
+    _probe_check(lib.pkv_probe_copy(_ptr(src), _ptr(dst), nbytes, num_workgroups, _stream(stream)), "pkv_probe_copy")

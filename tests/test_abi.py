@@ -9,14 +9,15 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pkv.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 LIB = os.path.join(ROOT, "paged_kv_cache_334_amd", "libpkv.so")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libpkv.so not built")
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
 
@@ -83,18 +84,18 @@ def test_bad_decode_arguments(ops):
     assert _decode(ops, d, max_ctx=16 * 16 + 1) == 1     # beyond max_blocks * block_size
     assert _decode(ops, d, scale=float("inf")) == 1
     assert _decode(ops, _desc(ops, dtype=ops.PKV_F32), out_dtype=ops.PKV_BF16) == 2
-    assert _decode(ops, d, opts=ops.DecodeOpts(0, 9)) == 1
-    assert _decode(ops, _desc(ops, num_kv_heads=32), opts=ops.DecodeOpts(0, 2)) == 2  # MFMA needs a group of 4/8
+    assert _decode(ops, d, opts=ops.DecodeOpts(0, 9, 0)) == 1
+    assert _decode(ops, _desc(ops, num_kv_heads=32), opts=ops.DecodeOpts(0, 2, 0)) == 2  # MFMA needs a group of 4/8
 
 
 def test_workspace_is_required_for_split(ops):
     d = _desc(ops)
-    opts = ops.DecodeOpts(64, 0)
+    opts = ops.DecodeOpts(64, 0, 0)
     need = ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(opts))
     assert need == 4 * 32 * 4 * (128 + 2) * 4  # 4 partitions of 64 tokens
     assert _decode(ops, d, opts=opts) == 3
     assert _decode(ops, d, opts=opts, ws=16, ws_bytes=need - 4) == 3
-    single = ops.DecodeOpts(1 << 30, 0)
+    single = ops.DecodeOpts(1 << 30, 0, 0)
     assert ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(single)) == 0
 
 
@@ -115,3 +116,23 @@ def test_cache_op_arguments(ops):
     assert ops.lib.pkv_copy_blocks(p, p, None, 3, ctypes.byref(d), None) == 1
     assert ops.lib.pkv_copy_blocks(p, p, p, -2, ctypes.byref(d), None) == 1
     assert ops.lib.pkv_copy_blocks(p, p, None, 0, ctypes.byref(d), None) == 0
+
+
+def test_blocks_in_flight_range(ops):
+    d = _desc(ops)
+    assert _decode(ops, d, opts=ops.DecodeOpts(0, 0, 3)) == 1
+    assert _decode(ops, d, opts=ops.DecodeOpts(0, 0, -1)) == 1
+
+
+def test_probe_arguments_rejected_without_launch():
+    lib = ctypes.CDLL(LIB)
+    lib.pkv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    lib.pkv_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]
+    lib.pkv_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    p = ctypes.c_void_p(16)
+    assert lib.pkv_probe_read(None, 1024, p, 8, None) == 1
+    assert lib.pkv_probe_read(p, 1000, p, 8, None) == 1       # not a multiple of 16
+    assert lib.pkv_probe_copy(p, ctypes.c_void_p(24), 1024, 8, None) == 1  # misaligned
+    assert lib.pkv_probe_gather(p, p, 4, 100, p, 8, None) == 1  # tile size not a multiple of 16
+    assert lib.pkv_probe_gather(p, p, 0, 4096, p, 8, None) == 1
