@@ -95,7 +95,43 @@ typedef struct {
   /* Blocks whose key/value tiles one wave loads before it uses the first:
    * 0 = chosen by the library, else 1 or 2. */
   int32_t blocks_in_flight;
+  /* Cascade decode over shared prefixes (bf16, head_dim 128): the plan words
+   * pkv_plan_shared_prefix() wrote for these block tables and context lengths,
+   * in HOST memory (read during the call) and the same words copied to DEVICE
+   * memory by the caller (read by the kernels).  NULL / 0 = no cascade. */
+  const int32_t* prefix_plan;
+  const int32_t* prefix_plan_dev;
+  size_t prefix_plan_words;
 } pkv_decode_opts;
+
+/*
+ * Shared-prefix plan for cascade decode.  Sequences whose block tables start
+ * with the same physical blocks share those tokens' keys and values (a common
+ * system prompt, forked sequences sharing their history through copy-on-write:
+ * "PagedAttention Explained", "Shared Prefix Caching"; "Paged Attention"
+ * glossary, "Example").  Attention over such a prefix is computed once for all
+ * query rows of the group on matrix cores, each prefix tile read once instead
+ * of once per sequence; the rest of each sequence goes through the ordinary
+ * paged walk, and the two are merged by their softmax (max, sum) states.  The
+ * result equals the plain decode up to rounding.
+ *
+ * Groups: sequences with at least min_prefix_blocks full blocks whose first
+ * block ids agree; the group's prefix is the longest run of identical block ids
+ * at the start of every member's table, counting only blocks fully inside every
+ * member's context.  Groups with fewer than min_group_seqs members (at least 2)
+ * or a prefix shorter than min_prefix_blocks are dropped.
+ *
+ *  block_tables  HOST [num_seqs][max_blocks_per_seq] int32
+ *  context_lens  HOST [num_seqs] int32
+ *  plan          HOST output of plan_words int32 words, or NULL to query the size
+ * Returns the number of words the plan needs (written only when plan is not
+ * NULL and plan_words is at least that), or 0 for invalid arguments.  The plan
+ * stays valid while the tables' prefix entries and the context lengths do not
+ * change; pass it (and a device copy) through pkv_decode_opts.
+ */
+size_t pkv_plan_shared_prefix(const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                              int32_t max_blocks_per_seq, int32_t block_size, int32_t min_group_seqs,
+                              int32_t min_prefix_blocks, int32_t* plan, size_t plan_words);
 
 /* Bytes of workspace pkv_paged_attn_decode needs for these shapes and options
  * (0 when the call runs as a single pass).  Returns 0 for invalid shapes. */

@@ -52,9 +52,72 @@ struct Plan {
   int blocks_per_part = 1;
   int num_parts = 1;
   int inflight = 1;
+  // cascade over shared prefixes
+  bool cascade = false;
+  int prefix_tiles = 0;         // 128-row tiles over all groups
+  int prefix_chunk_blocks = 0;  // prefix blocks per workgroup
+  int prefix_chunks = 0;        // chunk slots per (sequence, query head)
 };
 
+// Prefix-pass workgroups to aim for (two per CU).
+constexpr int64_t kPrefixTargetWorkgroups = 512;
+
+// Reads the host plan words: checks them against the call and sizes the
+// prefix pass.  Sets plan->cascade when at least one group exists.
+pkv_status plan_cascade(const pkv_pool_desc* pool, int32_t num_seqs, int32_t max_blocks_per_seq, int g,
+                        const pkv_decode_opts* opts, Plan* plan) {
+  const int32_t* w = opts->prefix_plan;
+  const size_t nw = opts->prefix_plan_words;
+  if (nw < (size_t)pkv::kPlanHeader || w[0] != pkv::kPlanMagic) return fail(PKV_EINVAL, "prefix plan: bad header");
+  if (w[pkv::kPlanSeqs] != num_seqs) return fail(PKV_EINVAL, "prefix plan: made for another number of sequences");
+  if (w[pkv::kPlanBlockSize] != pool->block_size) return fail(PKV_EINVAL, "prefix plan: made for another block size");
+  const int64_t groups = w[pkv::kPlanGroups], members = w[pkv::kPlanMembers];
+  if (groups < 0 || members < 0 ||
+      nw < (size_t)(pkv::kPlanHeader + num_seqs + pkv::kGroupWords * groups + members))
+    return fail(PKV_EINVAL, "prefix plan: truncated");
+  if (!opts->prefix_plan_dev) return fail(PKV_EINVAL, "prefix plan: device copy missing");
+  if (groups == 0) return PKV_OK;
+  if (pool->dtype != PKV_BF16 || pool->head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "cascade decode needs bf16 pools with head_dim 128");
+  // every index the kernels take from the plan is checked here, once, on the host
+  const int32_t* start = w + pkv::kPlanHeader;
+  const int32_t* gw = start + num_seqs;
+  const int32_t* mw = gw + pkv::kGroupWords * groups;
+  int64_t tiles = 0, max_prefix = 0;
+  for (int64_t gi = 0; gi < groups; ++gi) {
+    const int32_t prefix = gw[pkv::kGroupWords * gi], begin = gw[pkv::kGroupWords * gi + 1];
+    const int32_t count = gw[pkv::kGroupWords * gi + 2], leader = gw[pkv::kGroupWords * gi + 3];
+    if (prefix <= 0 || count <= 0 || begin < 0 || (int64_t)begin + count > members)
+      return fail(PKV_EINVAL, "prefix plan: bad group");
+    if (prefix > max_blocks_per_seq || leader < 0 || leader >= num_seqs)
+      return fail(PKV_EINVAL, "prefix plan: group does not fit the block tables");
+    for (int32_t k = 0; k < count; ++k) {
+      const int32_t b = mw[begin + k];
+      if (b < 0 || b >= num_seqs || start[b] != prefix)
+        return fail(PKV_EINVAL, "prefix plan: member outside the batch or with another prefix");
+    }
+    tiles += ((int64_t)count * g + 127) / 128;
+    max_prefix = prefix > max_prefix ? prefix : max_prefix;
+  }
+  for (int32_t b = 0; b < num_seqs; ++b)
+    if (start[b] < 0 || start[b] > max_prefix) return fail(PKV_EINVAL, "prefix plan: bad per-sequence prefix");
+  if (tiles > 0x7fffffff) return fail(PKV_EUNSUPPORTED, "prefix plan: too many rows");
+  const int64_t per_iter = 64 / pool->block_size;  // blocks the prefix kernel moves per iteration
+  const int64_t units = tiles * pool->num_kv_heads;
+  const int64_t want = (kPrefixTargetWorkgroups + units - 1) / units;
+  int64_t cb = (max_prefix + want - 1) / want;
+  cb = (cb + per_iter - 1) / per_iter * per_iter;
+  plan->cascade = true;
+  plan->prefix_tiles = (int)tiles;
+  plan->prefix_chunk_blocks = (int)cb;
+  plan->prefix_chunks = (int)((max_prefix + cb - 1) / cb);
+  if (plan->prefix_chunks > 65535) return fail(PKV_EUNSUPPORTED, "prefix plan: too many chunks");
+  return PKV_OK;
+}
+
+// max_blocks_per_seq: the block tables' row length (INT32_MAX when only sizing the workspace).
 pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_heads, int32_t max_context_len,
+                     int32_t max_blocks_per_seq,
                      const pkv_decode_opts* opts, Plan* plan) {
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
@@ -77,6 +140,10 @@ pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_he
 
   const int bs = pool->block_size;
   const int max_blocks = (max_context_len + bs - 1) / bs;
+  if (opts && opts->prefix_plan) {
+    st = plan_cascade(pool, num_seqs, max_blocks_per_seq, g, opts, plan);
+    if (st != PKV_OK) return st;
+  }
   const int tile_bytes = bs * pool->head_dim * elt_bytes(pool->dtype);
   const int inflight = opts ? opts->blocks_in_flight : 0;
   if (inflight < 0 || inflight > 2) return fail(PKV_EINVAL, "blocks_in_flight must be 0, 1 or 2");
@@ -85,7 +152,10 @@ pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_he
   int64_t part_tokens = opts ? opts->partition_tokens : 0;
   if (part_tokens < 0) return fail(PKV_EINVAL, "partition_tokens must be >= 0");
   int64_t bpp;
-  if (part_tokens == 0) {
+  if (plan->cascade) {
+    // the suffix after a shared prefix is short: one pass, merged with the prefix partials in place
+    bpp = max_blocks > 0 ? max_blocks : 1;
+  } else if (part_tokens == 0) {
     // Automatic.  One pass per (sequence, kv head) when that already gives
     // kTargetWorkgroups workgroups: a split costs a second kernel, the partials'
     // traffic and a prologue/epilogue per workgroup, and measured slower than a
@@ -114,10 +184,21 @@ pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_he
   return PKV_OK;
 }
 
-size_t workspace_for(const Plan& plan, int32_t num_seqs, int32_t num_heads, int32_t head_dim) {
+// Workspace: split-K partials (num_parts > 1), then the prefix-pass partials.
+size_t split_bytes(const Plan& plan, int32_t num_seqs, int32_t num_heads, int32_t head_dim) {
   if (plan.num_parts <= 1) return 0;
   const size_t rows = (size_t)num_seqs * num_heads * plan.num_parts;
   return rows * (2 + (size_t)head_dim) * sizeof(float);
+}
+
+size_t prefix_bytes(const Plan& plan, int32_t num_seqs, int32_t num_heads, int32_t head_dim) {
+  if (!plan.cascade) return 0;
+  const size_t rows = (size_t)num_seqs * num_heads * plan.prefix_chunks;
+  return rows * (2 + (size_t)head_dim) * sizeof(float);
+}
+
+size_t workspace_for(const Plan& plan, int32_t num_seqs, int32_t num_heads, int32_t head_dim) {
+  return split_bytes(plan, num_seqs, num_heads, head_dim) + prefix_bytes(plan, num_seqs, num_heads, head_dim);
 }
 
 }  // namespace
@@ -127,7 +208,7 @@ extern "C" {
 size_t pkv_paged_attn_workspace_bytes(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_heads,
                                       int32_t max_context_len, const pkv_decode_opts* opts) {
   Plan plan;
-  if (make_plan(pool, num_seqs, num_heads, max_context_len, opts, &plan) != PKV_OK) return 0;
+  if (make_plan(pool, num_seqs, num_heads, max_context_len, INT32_MAX, opts, &plan) != PKV_OK) return 0;
   return workspace_for(plan, num_seqs, num_heads, pool->head_dim);
 }
 
@@ -138,7 +219,7 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
                                  void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts,
                                  void* stream) {
   Plan plan;
-  pkv_status st = make_plan(pool, num_seqs, num_heads, max_context_len, opts, &plan);
+  pkv_status st = make_plan(pool, num_seqs, num_heads, max_context_len, max_blocks_per_seq, opts, &plan);
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return ok();
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
@@ -182,6 +263,35 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int bf16 = pool->dtype == PKV_BF16;
+  if (plan.cascade) {
+    const size_t rows = (size_t)num_seqs * num_heads * plan.prefix_chunks;
+    float* pre = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          split_bytes(plan, num_seqs, num_heads, pool->head_dim));
+    pkv::PrefixArgs p{};
+    p.q = q;
+    p.k_pool = k_pool;
+    p.v_pool = v_pool;
+    p.block_tables = block_tables;
+    p.plan = opts->prefix_plan_dev;
+    p.num_heads = num_heads;
+    p.num_kv_heads = pool->num_kv_heads;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = pool->num_blocks;
+    p.chunk_blocks = plan.prefix_chunk_blocks;
+    p.num_chunks = plan.prefix_chunks;
+    p.scale_log2 = a.scale_log2;
+    p.ws_m = pre;
+    p.ws_l = pre + rows;
+    p.ws_acc = pre + 2 * rows;
+    hipError_t pe = pkv::launch_prefix(p, pool->block_size, plan.group, plan.prefix_tiles, s);
+    if (pe != hipSuccess) return fail(PKV_EHIP, std::string("prefix launch: ") + hipGetErrorString(pe));
+    a.start_blocks = opts->prefix_plan_dev + pkv::kPlanHeader;
+    a.prefix_chunks = plan.prefix_chunks;
+    a.prefix_chunk_blocks = plan.prefix_chunk_blocks;
+    a.pre_m = p.ws_m;
+    a.pre_l = p.ws_l;
+    a.pre_acc = p.ws_acc;
+  }
   hipError_t e = plan.mfma ? pkv::launch_decode_mfma(a, pool->head_dim, pool->block_size, plan.group, plan.inflight, s)
                            : pkv::launch_decode_vector(a, bf16, pool->head_dim, pool->block_size, plan.group,
                                                        plan.inflight, s);
@@ -246,6 +356,6 @@ const char* pkv_status_string(pkv_status status) {
 
 const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
-int32_t pkv_version(void) { return 200; }
+int32_t pkv_version(void) { return 300; }
 
 }  // extern "C"

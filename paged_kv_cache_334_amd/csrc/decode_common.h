@@ -18,6 +18,7 @@ namespace pkv {
 struct SeqPick {
   int b;
   int ctx_raw;
+  int start;  // blocks covered by a shared-prefix pass (0 without one)
 };
 
 __device__ __forceinline__ SeqPick pick_sequence(const DecodeArgs& a, int* sm_key, int* sm_pick) {
@@ -25,6 +26,7 @@ __device__ __forceinline__ SeqPick pick_sequence(const DecodeArgs& a, int* sm_ke
     SeqPick p;
     p.b = blockIdx.z;
     p.ctx_raw = a.context_lens[p.b];
+    p.start = a.start_blocks ? a.start_blocks[p.b] : 0;
     return p;
   }
   const int t = threadIdx.x;
@@ -51,6 +53,7 @@ __device__ __forceinline__ SeqPick pick_sequence(const DecodeArgs& a, int* sm_ke
   SeqPick p;
   p.b = sm_pick[0];
   p.ctx_raw = sm_pick[1];
+  p.start = a.start_blocks ? a.start_blocks[p.b] : 0;
   return p;
 }
 
@@ -58,6 +61,7 @@ __device__ __forceinline__ SeqPick pick_sequence(const DecodeArgs& a, int* sm_ke
 // heads, sequence slots), the slot mapped to a sequence by pick_sequence.
 struct PartRange {
   int b, kvh, part;
+  int start;    // first block of this pass (after a shared prefix)
   int ctx;      // context length (0 when context_lens[b] breaks its precondition)
   bool ctx_bad; // context_lens[b] < 0 or > max_context: the rows become NaN and nothing is read
   int nblocks;  // blocks of the sequence
@@ -75,8 +79,11 @@ __device__ __forceinline__ PartRange part_range(const DecodeArgs& a, const SeqPi
   r.ctx_bad = ctx_raw < 0 || ctx_raw > a.max_context;
   r.ctx = r.ctx_bad ? 0 : ctx_raw;
   r.nblocks = (r.ctx + BS - 1) / BS;
-  r.nparts = (r.nblocks + a.blocks_per_part - 1) / a.blocks_per_part;
-  r.blk_lo = r.part * a.blocks_per_part;
+  r.start = min(max(s.start, 0), r.nblocks);
+  const int rest = r.nblocks - r.start;
+  r.nparts = (rest + a.blocks_per_part - 1) / a.blocks_per_part;
+  if (r.start > 0 && r.nparts == 0) r.nparts = 1;  // an empty suffix still merges the prefix partials
+  r.blk_lo = r.start + r.part * a.blocks_per_part;
   r.blk_hi = min(r.nblocks, r.blk_lo + a.blocks_per_part);
   return r;
 }
@@ -100,7 +107,7 @@ __device__ __forceinline__ bool finish_if_empty(const DecodeArgs& a, const PartR
 // Blocks of a partition are dealt to the waves round-robin: wave w takes
 // partition blocks w, w + kWaves, w + 2*kWaves, ...; this is how many it gets.
 __device__ __forceinline__ int wave_block_count(const PartRange& r, int wave) {
-  const int n = r.blk_hi - r.blk_lo;
+  const int n = max(r.blk_hi - r.blk_lo, 0);
   return n > wave ? (n - wave + kWaves - 1) / kWaves : 0;
 }
 
@@ -117,9 +124,10 @@ struct WaveIds {
 // Started before the context length is known, so the table load overlaps the
 // context-length load.  Entries past the sequence's last block may be read
 // (they are inside the row of max_blocks entries) but never used.
-__device__ __forceinline__ WaveIds wave_ids_begin(const DecodeArgs& a, int b, int wave, int lane) {
+__device__ __forceinline__ WaveIds wave_ids_begin(const DecodeArgs& a, const SeqPick& s, int wave, int lane) {
   WaveIds w;
-  const int first = blockIdx.x * a.blocks_per_part + wave;
+  const int b = s.b;
+  const int first = max(s.start, 0) + blockIdx.x * a.blocks_per_part + wave;
   w.row = a.block_tables + (int64_t)b * a.max_blocks + first;
   w.limit = a.max_blocks - first;
   w.chunk = 0;
@@ -190,9 +198,14 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
   const int h0 = r.kvh * G;
   for (int idx = threadIdx.x; idx < G * HD; idx += 64 * NW) {
     const int h = idx / HD, d = idx % HD;
+    const int hq = h0 + h;
+    // partials of the shared-prefix pass, merged here when this pass is the only suffix partition
+    const int pre = (r.start > 0 && r.nparts == 1) ? (r.start + a.prefix_chunk_blocks - 1) / a.prefix_chunk_blocks : 0;
+    const int64_t pre_base = ((int64_t)r.b * a.num_heads + hq) * a.prefix_chunks;
     float big_m = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][h]);
+    for (int c = 0; c < pre; ++c) big_m = fmaxf(big_m, a.pre_m[pre_base + c]);
     float l = 0.f, acc = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -200,11 +213,15 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
       l = fmaf(f, sm_l[w][h], l);
       acc = fmaf(f, sm_acc[w][h][d], acc);
     }
+    for (int c = 0; c < pre; ++c) {
+      const float f = fast_exp2(a.pre_m[pre_base + c] - big_m);
+      l = fmaf(f, a.pre_l[pre_base + c], l);
+      acc = fmaf(f, a.pre_acc[(pre_base + c) * HD + d], acc);
+    }
     if (any_bad) {
       big_m = NAN;
       acc = NAN;
     }
-    const int hq = h0 + h;
     if (r.nparts == 1) {
       const float o = acc / l;
       const int64_t oi = ((int64_t)r.b * a.num_heads + hq) * HD + d;

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
   // block ids (table entries past the sequence's end may be read, never used)
   // and q.
   const SeqPick seq = pick_sequence(a, sm_key, sm_pick);
-  WaveIds wids = wave_ids_begin(a, seq.b, wave, lane);
+  WaveIds wids = wave_ids_begin(a, seq, wave, lane);
   uint32_t qw[G][KC][4];  // the q chunks this lane meets in the key pass (bf16 pairs kept packed)
 #pragma unroll
   for (int h = 0; h < G; ++h) {

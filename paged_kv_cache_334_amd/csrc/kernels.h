@@ -33,6 +33,47 @@ struct DecodeArgs {
   float* ws_m;
   float* ws_l;
   float* ws_acc;
+  // Cascade (shared-prefix) mode: start_blocks[b] = blocks of sequence b already
+  // covered by the prefix pass (NULL: none).  Its partials for chunk c < ceil(start /
+  // prefix_chunk_blocks) sit at (b*num_heads + h)*prefix_chunks + c of pre_*.
+  const int32_t* start_blocks;
+  int32_t prefix_chunks;
+  int32_t prefix_chunk_blocks;
+  const float* pre_m;
+  const float* pre_l;
+  const float* pre_acc;
+};
+
+// Shared-prefix plan words (built on the host by pkv_plan_shared_prefix):
+//   [0] magic  [1] num_seqs  [2] block_size  [3] num_groups  [4] max prefix blocks
+//   [5] total members, then prefix_blocks[num_seqs], then per group
+//   {prefix_blocks, member_begin, member_count, leader}, then the member lists.
+constexpr int32_t kPlanMagic = 0x504b5650;  // "PKVP"
+constexpr int kPlanSeqs = 1;
+constexpr int kPlanBlockSize = 2;
+constexpr int kPlanGroups = 3;
+constexpr int kPlanMaxPrefix = 4;
+constexpr int kPlanMembers = 5;
+constexpr int kPlanHeader = 6;
+constexpr int kGroupWords = 4;
+
+// Everything the shared-prefix kernel reads.
+struct PrefixArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* plan;  // device copy of the plan words
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t chunk_blocks;  // prefix blocks per workgroup
+  int32_t num_chunks;    // chunk slots per (sequence, query head)
+  float scale_log2;
+  float* ws_m;
+  float* ws_l;
+  float* ws_acc;
 };
 
 bool vector_supported(int dtype_bf16, int head_dim, int block_size, int group);
@@ -43,6 +84,7 @@ hipError_t launch_decode_vector(const DecodeArgs& a, int dtype_bf16, int head_di
                                 int inflight, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, int block_size, int group, int inflight,
                               hipStream_t stream);
+hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, int num_tiles, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeArgs& a, int head_dim, int block_size, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, int64_t k_stride, int64_t v_stride,

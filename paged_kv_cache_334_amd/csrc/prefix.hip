@@ -1,0 +1,279 @@
+// Shared-prefix pass of cascade decode (bf16, head_dim 128).
+//
+// Sequences that reference the same physical blocks for their first P blocks
+// (a shared system prompt, a forked beam; "PagedAttention Explained", "Shared
+// Prefix Caching"; "Paged Attention" glossary, "Example") would each read
+// those blocks again in a per-sequence decode.  Here the prefix is read once
+// per kv head for all query rows of the group: rows = (member sequence, query
+// head of the kv head), so the per-tile work becomes a dense contraction
+// [rows x tokens] = Q . K^T and [rows x D] += P . V, done on matrix cores,
+// FlashAttention-style (tiles streamed through LDS, float32 online softmax;
+// "Paged Attention" glossary, related term "FlashAttention").  Each workgroup
+// covers 128 rows of one group and kv head and one chunk of the prefix, and
+// writes a partial (max, sum, acc) per row; the suffix pass merges them.
+//
+// Workgroup = 4 waves x 32 query rows (two 16-column MFMA tiles per wave).
+// Per iteration 64 prefix tokens: every thread loads four 16-byte key chunks
+// and four value chunks of the next iteration into registers while the
+// current one is computed from LDS, then stores them to the other LDS buffer
+// (two buffers, one barrier per iteration).  The LDS copy keeps the pool's
+// tile layout (keys chunk-major, values dim-major) except that a 32-token
+// value tile is split into two 16-token halves, so the matrix-core operand
+// reads below are conflict-free for both block sizes:
+//  * S^T = K . Q^T, v_mfma_f32_16x16x32_bf16: A = keys (lane: token n, lane
+//    group kg -> 16-byte chunk 4i+kg), B = queries (lane: column n, dims
+//    32i+8kg..+7); lane gets S^T[token 4kg+r][column n].
+//  * O^T += V^T . P^T, v_mfma_f32_16x16x16_bf16: A = values (lane: dim
+//    16nt+n, tokens 4kg..4kg+3, 8 bytes), B = the lane's own 4 weights.
+//    Weights go in as bf16 hi + lo parts (two instructions), keeping ~16
+//    significant bits.
+#include "decode_common.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int HD = 128;
+constexpr int TOK = 64;           // prefix tokens per iteration
+constexpr int NW = kWaves;        // 4
+constexpr int ROWS_PER_WAVE = 32; // two MFMA column tiles
+constexpr int STAGE_HALF = TOK * HD * 2;  // bytes of keys (or values) per iteration: 16 KiB
+constexpr int CHUNKS_PER_THREAD = STAGE_HALF / 16 / (64 * NW);  // 4
+
+template <int BS, int G>
+__global__ __launch_bounds__(64 * NW) void prefix_kernel(PrefixArgs p) {
+  constexpr int NB = TOK / BS;          // blocks per iteration
+  constexpr int TILE = BS * HD * 2;     // bytes of one (block, kv head) tile
+  constexpr int SUBB = BS / 16;         // 16-token sub-tiles per block
+  static_assert(NB * TILE == STAGE_HALF, "stage size");
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][STAGE_HALF];  // [buffer][K=0/V=1]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int kg = lane >> 4;
+  const int kvh = blockIdx.y;
+  const int chunk = blockIdx.z;
+
+  // which group and 128-row tile: groups hold their tiles in order
+  const int32_t* plan = p.plan;
+  const int num_groups = plan[kPlanGroups];
+  const int32_t* groups = plan + kPlanHeader + plan[kPlanSeqs];
+  int tile = blockIdx.x, gi = 0;
+  int gprefix = 0, gbegin = 0, gcount = 0, leader = 0;
+  for (; gi < num_groups; ++gi) {
+    const int32_t* gr = groups + kGroupWords * gi;
+    const int tiles = (gr[2] * G + 127) / 128;
+    if (tile < tiles) {
+      gprefix = gr[0];
+      gbegin = gr[1];
+      gcount = gr[2];
+      leader = gr[3];
+      break;
+    }
+    tile -= tiles;
+  }
+  if (gi == num_groups) return;
+  const int32_t* members = groups + kGroupWords * num_groups + gbegin;
+  const int blk_lo = chunk * p.chunk_blocks;
+  const int blk_hi = min(gprefix, blk_lo + p.chunk_blocks);
+  if (blk_lo >= blk_hi) return;  // the merge counts only the chunks the group's prefix reaches
+  const int rows = gcount * G;
+  const int row0 = tile * 128 + ROWS_PER_WAVE * wave;  // this wave's first row
+  const bool wave_active = row0 < rows;
+
+  // queries: column tile ct, lane column n -> row row0 + 16ct + n
+  bf16x8 qb[2][4];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int row = row0 + 16 * ct + n;
+    const bool ok = row < rows;
+    const int b = ok ? members[row / G] : 0;
+    const int h = kvh * G + row % G;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)b * p.num_heads + h) * HD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      qb[ct][i] = __builtin_bit_cast(bf16x8, ok ? load16(qrow + 32 * i + 8 * kg) : make_uint4(0, 0, 0, 0));
+  }
+
+  // block ids of the chunk, 64 at a time (lane l: block c0 + l); ids outside the pool -> block 0 and NaN rows
+  const int32_t* bt = p.block_tables + (int64_t)leader * p.max_blocks;
+  int bad = 0;
+  int id_base = blk_lo;
+  auto load_ids = [&](int base) {
+    const int idx = base + lane;
+    int id = idx < blk_hi ? bt[idx] : 0;
+    const bool out = idx < blk_hi && (unsigned)id >= (unsigned)p.num_blocks;
+    bad |= __ballot(out) != 0;
+    return out ? 0 : id;
+  };
+  int ids = load_ids(id_base);
+
+  const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (int64_t)kvh * TILE;
+  const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (int64_t)kvh * TILE;
+  const int64_t block_bytes = (int64_t)p.num_kv_heads * TILE;
+  const int iters = (blk_hi - blk_lo + NB - 1) / NB;
+
+  // staging: thread t moves chunk t + 256*k (k < 4) of the keys and of the values
+  uint4 sk[CHUNKS_PER_THREAD], sv[CHUNKS_PER_THREAD];
+  auto stage_load = [&](int it) {
+    const int first = blk_lo + it * NB;
+    if (first - id_base >= 64) {  // next 64 ids
+      id_base += 64;
+      ids = load_ids(id_base);
+    }
+#pragma unroll
+    for (int k = 0; k < CHUNKS_PER_THREAD; ++k) {
+      const int c = threadIdx.x + 64 * NW * k;  // chunk of the stage
+      const int kb = c / (TILE / 16);           // block within the iteration
+      const int off = (c % (TILE / 16)) * 16;   // byte offset within the tile
+      const int j = min(first + kb, blk_hi - 1);  // past the chunk's end: re-read, never used
+      const int64_t base = (int64_t)__builtin_amdgcn_readlane(ids, j - id_base) * block_bytes;
+      sk[k] = load16(kpool + base + off);
+      sv[k] = load16(vpool + base + off);
+    }
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < CHUNKS_PER_THREAD; ++k) {
+      const int c = threadIdx.x + 64 * NW * k;
+      const int kb = c / (TILE / 16);
+      const int off = (c % (TILE / 16)) * 16;
+      *reinterpret_cast<uint4*>(&lds[buf][0][kb * TILE + off]) = sk[k];
+      // values: dim d, tokens 8q..8q+7 of the block -> half q/2 (16-token [D][16] tile), position 8*(q%2)
+      const int d = off / (BS * 2);
+      const int q8 = (off % (BS * 2)) / 16;
+      const int voff = kb * TILE + (q8 / 2) * (HD * 32) + d * 32 + (q8 % 2) * 16;
+      *reinterpret_cast<uint4*>(&lds[buf][1][voff]) = sv[k];
+    }
+  };
+
+  f32x4 o[2][8];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+  for (int it = 0; it < iters; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < iters;
+    if (more) stage_load(it + 1);
+    if (wave_active) {
+      const int valid_tokens = min(TOK, (blk_hi - blk_lo - it * NB) * BS);
+#pragma unroll
+      for (int sub = 0; sub < TOK / 16; ++sub) {
+        if (16 * sub >= valid_tokens) break;
+        const int kb = sub / SUBB;
+        const int ts = (sub % SUBB) * 16;
+        const unsigned char* kt = &lds[buf][0][kb * TILE];
+        const unsigned char* vt = &lds[buf][1][kb * TILE + (sub % SUBB) * (HD * 32)];
+        bf16x8 ka[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ka[i] = *reinterpret_cast<const bf16x8*>(kt + ((4 * i + kg) * BS + ts + n) * 16);
+        s16x4 pb_hi[2], pb_lo[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i], qb[ct][i], s, 0, 0, 0);
+          float sr[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sr[r] = s[r] * p.scale_log2;
+          float mx = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
+          mx = max_xor32(max_xor16(mx));
+          if (__ballot(mx > m[ct] + kRescaleSlack) != 0) {
+            const float mn = fmaxf(m[ct], mx);
+            const float alpha = fast_exp2(m[ct] - mn);
+            lsum[ct] *= alpha;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) o[ct][nt] *= alpha;
+            m[ct] = mn;
+          }
+          float pr[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sr[r] - m[ct]);
+          lsum[ct] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+          uint32_t hi[4], lo[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            hi[r] = f32_to_bf16_rne(pr[r]);
+            lo[r] = f32_to_bf16_rne(pr[r] - __uint_as_float(hi[r] << 16));
+          }
+          pb_hi[ct] = __builtin_bit_cast(s16x4, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
+          pb_lo[ct] = __builtin_bit_cast(s16x4, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const s16x4 va = *reinterpret_cast<const s16x4*>(vt + ((16 * nt + n) * 16 + 4 * kg) * 2);
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_hi[ct], o[ct][nt], 0, 0, 0);
+            o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_lo[ct], o[ct][nt], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (more) stage_store(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+  // partials: row -> (member sequence, query head); slot (b, h, chunk)
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const float l = sum_xor32(sum_xor16(lsum[ct]));
+    const int row = row0 + 16 * ct + n;
+    if (row >= rows) continue;
+    const int b = members[row / G];
+    const int h = kvh * G + row % G;
+    const int64_t pi = ((int64_t)b * p.num_heads + h) * p.num_chunks + chunk;
+    float* acc = p.ws_acc + pi * HD;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      f32x4 v = o[ct][nt];
+      if (bad) v = f32x4{NAN, NAN, NAN, NAN};
+      *reinterpret_cast<f32x4*>(acc + 16 * nt + 4 * kg) = v;
+    }
+    if (kg == 0) {
+      p.ws_m[pi] = bad ? NAN : m[ct];
+      p.ws_l[pi] = bad ? NAN : l;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, int num_tiles, hipStream_t s) {
+  const dim3 grid(num_tiles, p.num_kv_heads, p.num_chunks);
+  const dim3 block(64 * NW);
+#define PKV_PREFIX(BS, G) hipLaunchKernelGGL((prefix_kernel<BS, G>), grid, block, 0, s, p)
+  if (block_size == 16) {
+    switch (group) {
+      case 1: PKV_PREFIX(16, 1); break;
+      case 2: PKV_PREFIX(16, 2); break;
+      case 4: PKV_PREFIX(16, 4); break;
+      case 8: PKV_PREFIX(16, 8); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (block_size == 32) {
+    switch (group) {
+      case 1: PKV_PREFIX(32, 1); break;
+      case 2: PKV_PREFIX(32, 2); break;
+      case 4: PKV_PREFIX(32, 4); break;
+      case 8: PKV_PREFIX(32, 8); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef PKV_PREFIX
+  return hipGetLastError();
+}
+
+}  // namespace pkv

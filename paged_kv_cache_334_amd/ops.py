@@ -36,7 +36,14 @@ class PoolDesc(ctypes.Structure):
 
 
 class DecodeOpts(ctypes.Structure):
-    _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32), ("blocks_in_flight", ctypes.c_int32)]
+    _fields_ = [
+        ("partition_tokens", ctypes.c_int32),
+        ("kernel", ctypes.c_int32),
+        ("blocks_in_flight", ctypes.c_int32),
+        ("prefix_plan", ctypes.c_void_p),
+        ("prefix_plan_dev", ctypes.c_void_p),
+        ("prefix_plan_words", ctypes.c_size_t),
+    ]
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -51,6 +58,8 @@ lib.pkv_reshape_and_cache.restype = _i32
 lib.pkv_reshape_and_cache.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp, ctypes.POINTER(PoolDesc), _vp]
 lib.pkv_copy_blocks.restype = _i32
 lib.pkv_copy_blocks.argtypes = [_vp, _vp, _vp, _i32, ctypes.POINTER(PoolDesc), _vp]
+lib.pkv_plan_shared_prefix.restype = _sz
+lib.pkv_plan_shared_prefix.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz]
 lib.pkv_status_string.restype = ctypes.c_char_p
 lib.pkv_status_string.argtypes = [_i32]
 lib.pkv_last_error.restype = ctypes.c_char_p
@@ -122,17 +131,68 @@ def new_pools(num_blocks, num_kv_heads, block_size, head_dim, dtype=torch.bfloat
     return k, v
 
 
+class PrefixPlan:
+    """Plan words of pkv_plan_shared_prefix: ``host`` (a NumPy int32 array the
+    library reads during each call) and ``dev`` (their device copy, read by the
+    kernels).  ``groups`` is the number of shared-prefix groups found."""
+
+    def __init__(self, host, dev):
+        self.host = host
+        self.dev = dev
+
+    @property
+    def groups(self) -> int:
+        return int(self.host[3])
+
+    def prefix_blocks(self):
+        """Blocks of each sequence covered by a shared prefix (0 = none)."""
+        n = int(self.host[1])
+        return self.host[6:6 + n]
+
+
+def plan_shared_prefix(block_tables, context_lens, block_size, min_group_seqs=4, min_prefix_blocks=8,
+                       device="cuda") -> PrefixPlan:
+    """Find sequences sharing a block-table prefix.  ``block_tables`` and
+    ``context_lens`` are host (NumPy or CPU tensor) int32 arrays."""
+    import numpy as np
+
+    bt = np.ascontiguousarray(np.asarray(block_tables.cpu() if hasattr(block_tables, "cpu") else block_tables),
+                              dtype=np.int32)
+    cl = np.ascontiguousarray(np.asarray(context_lens.cpu() if hasattr(context_lens, "cpu") else context_lens),
+                              dtype=np.int32)
+    nseq, mb = bt.shape
+    if cl.shape != (nseq,):
+        raise ValueError("context_lens does not match block_tables")
+    args = (bt.ctypes.data, cl.ctypes.data, nseq, mb, block_size, min_group_seqs, min_prefix_blocks)
+    need = int(lib.pkv_plan_shared_prefix(*args, None, 0))
+    if need == 0:
+        raise ValueError("pkv_plan_shared_prefix rejected its arguments")
+    host = np.zeros(need, dtype=np.int32)
+    got = int(lib.pkv_plan_shared_prefix(*args, host.ctypes.data, need))
+    if got != need:
+        raise RuntimeError("plan size changed between calls")
+    dev = torch.from_numpy(host).to(device) if device is not None else None
+    return PrefixPlan(host, dev)
+
+
+def _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan):
+    if prefix_plan is None:
+        return DecodeOpts(int(partition_tokens), KERNELS[kernel], int(blocks_in_flight), None, None, 0)
+    return DecodeOpts(int(partition_tokens), KERNELS[kernel], int(blocks_in_flight), prefix_plan.host.ctypes.data,
+                      _ptr(prefix_plan.dev), prefix_plan.host.size)
+
+
 def paged_attn_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, max_context_len, partition_tokens=0,
-                               kernel="auto", blocks_in_flight=0) -> int:
+                               kernel="auto", blocks_in_flight=0, prefix_plan=None) -> int:
     desc = pool_desc(k_pool, v_pool)
-    opts = DecodeOpts(partition_tokens, KERNELS[kernel], blocks_in_flight)
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan)
     return int(lib.pkv_paged_attn_workspace_bytes(ctypes.byref(desc), num_seqs, num_heads, max_context_len,
                                                   ctypes.byref(opts)))
 
 
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, max_context_len=None,
                       workspace=None, partition_tokens=0, kernel="auto", out_dtype=None, stream=None,
-                      blocks_in_flight=0):
+                      blocks_in_flight=0, prefix_plan=None):
     """``out[b, h] = softmax(scale * q[b, h] . K^T) . V`` over sequence b's
     paged keys/values.  ``q`` is ``[B, Hq, D]``; ``block_tables`` ``[B, max_blocks]``
     int32; ``context_lens`` ``[B]`` int32.  ``max_context_len`` is a host-side
@@ -153,7 +213,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=
         odt = q.dtype if out_dtype is None else out_dtype
         out = torch.empty((nseq, nh, hd), dtype=odt, device=q.device)
     odt_code = PKV_BF16 if out.dtype == torch.bfloat16 else PKV_F32
-    opts = DecodeOpts(int(partition_tokens), KERNELS[kernel], int(blocks_in_flight))
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan)
     need = int(lib.pkv_paged_attn_workspace_bytes(ctypes.byref(desc), nseq, nh, int(max_context_len),
                                                   ctypes.byref(opts)))
     if workspace is None and need > 0:

@@ -128,7 +128,9 @@ class WorkloadSpec:
     block_size: int
     ctx: Union[Tuple[int, int], Tuple[int, ...]]  # (lo, hi) inclusive uniform, or explicit lengths
     ctx_is_list: bool = False
-    shared_prefix: int = 0  # tokens every sequence shares (block aligned)
+    shared_prefix: int = 0  # tokens every sequence of a prefix group shares (block aligned)
+    prefix_groups: int = 1  # sequence b < num_seqs - unshared_seqs joins group b % prefix_groups
+    unshared_seqs: int = 0  # trailing sequences with no shared prefix
     cow_fraction: float = 0.0  # fraction of sequences whose last block was just forked
     outlier_fraction: float = 0.0  # key rows scaled by ``outlier_scale``
     outlier_scale: float = 8.0
@@ -219,6 +221,13 @@ def _normal_bits(rng, shape, dtype, chunk_rows: int = 1 << 14, scale_rows=None):
     return out.reshape(shape)
 
 
+def prefix_group_of(spec: WorkloadSpec, b: int) -> int:
+    """Prefix group of sequence b, or -1 when it shares no prefix."""
+    if not spec.shared_prefix or b >= spec.num_seqs - spec.unshared_seqs:
+        return -1
+    return b % spec.prefix_groups
+
+
 def context_lengths(spec: WorkloadSpec) -> np.ndarray:
     """Context length of every sequence (shared prefix and newest token included)."""
     if spec.ctx_is_list:
@@ -229,7 +238,8 @@ def context_lengths(spec: WorkloadSpec) -> np.ndarray:
         lo, hi = spec.ctx
         ctx = np.random.default_rng([spec.seed, _CTX]).integers(lo, hi, size=spec.num_seqs, endpoint=True)
         ctx = ctx.astype(np.int64)
-    return ctx + spec.shared_prefix
+    shared = np.array([prefix_group_of(spec, b) >= 0 for b in range(spec.num_seqs)], dtype=bool)
+    return ctx + np.where(shared, spec.shared_prefix, 0)
 
 
 def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overrides) -> Workload:
@@ -262,31 +272,35 @@ def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overri
 
     # pool size
     prefix_blocks = spec.shared_prefix // bs
-    needed = prefix_blocks + int(sum(-(-(int(n) - spec.shared_prefix) // bs) for n in ctx)) + len(cow_seqs)
+    groups = spec.prefix_groups if spec.shared_prefix else 0
+    own = [int(n) - (spec.shared_prefix if prefix_group_of(spec, b) >= 0 else 0) for b, n in enumerate(ctx)]
+    needed = prefix_blocks * groups + int(sum(-(-o // bs) for o in own)) + len(cow_seqs)
     num_blocks = spec.num_blocks if spec.num_blocks is not None else int(np.ceil(spec.pool_factor * needed))
     if num_blocks < needed + 1:
         raise ValueError("pool too small")
     free_order = rng(_PERM).permutation(num_blocks)
     mgr = BlockManager(num_blocks, bs, free_order)
 
-    # token order: shared prefix first, then each sequence's own tokens
+    # token order: the shared prefixes first, then each sequence's own tokens
     init_slots = []
-    init_owner = []  # (seq or -1, position)
-    if spec.shared_prefix:
-        mgr.allocate_sequence("prefix")
+    init_owner = []  # (seq, or -1 - group for a prefix token, position)
+    for gi in range(groups):
+        mgr.allocate_sequence(("prefix", gi))
         for pos in range(spec.shared_prefix):
-            init_slots.append(mgr.append_slot("prefix"))
-            init_owner.append((-1, pos))
+            init_slots.append(mgr.append_slot(("prefix", gi)))
+            init_owner.append((-1 - gi, pos))
     for b in range(nseq):
-        if spec.shared_prefix:
-            mgr.fork("prefix", b)
+        gi = prefix_group_of(spec, b)
+        if gi >= 0:
+            mgr.fork(("prefix", gi), b)
         else:
             mgr.allocate_sequence(b)
-        for pos in range(spec.shared_prefix, int(ctx[b]) - 1):
+        first = spec.shared_prefix if gi >= 0 else 0
+        for pos in range(first, int(ctx[b]) - 1):
             init_slots.append(mgr.append_slot(b))
             init_owner.append((b, pos))
-    if spec.shared_prefix:
-        mgr.free_sequence("prefix")
+    for gi in range(groups):
+        mgr.free_sequence(("prefix", gi))
     for b in cow_seqs:  # an implicit sibling keeps referencing every block of b
         mgr.fork(b, ("sibling", b))
     # the step: one new token per sequence (copy-on-write happens here)
@@ -319,8 +333,9 @@ def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overri
         for b in range(nseq):
             index_of[(b, int(ctx[b]) - 1)] = len(init_slots) + b
         for b in range(nseq):
-            n_out = int(np.floor(spec.outlier_fraction * (int(ctx[b]) - spec.shared_prefix)))
-            pos = np.sort(orng.choice(np.arange(spec.shared_prefix, int(ctx[b])), size=n_out, replace=False))
+            first = spec.shared_prefix if prefix_group_of(spec, b) >= 0 else 0
+            n_out = int(np.floor(spec.outlier_fraction * (int(ctx[b]) - first)))
+            pos = np.sort(orng.choice(np.arange(first, int(ctx[b])), size=n_out, replace=False))
             outliers[b] = pos
             for p in pos.tolist():
                 key_scale[index_of[(b, p)]] = spec.outlier_scale

@@ -136,3 +136,38 @@ def test_probe_arguments_rejected_without_launch():
     assert lib.pkv_probe_copy(p, ctypes.c_void_p(24), 1024, 8, None) == 1  # misaligned
     assert lib.pkv_probe_gather(p, p, 4, 100, p, 8, None) == 1  # tile size not a multiple of 16
     assert lib.pkv_probe_gather(p, p, 0, 4096, p, 8, None) == 1
+
+
+def test_prefix_plan_is_checked_before_launch(ops):
+    import numpy as np
+
+    d = _desc(ops)
+    tables = np.tile(np.arange(16, dtype=np.int32), (4, 1))  # 4 sequences sharing every block
+    ctx = np.full(4, 256, dtype=np.int32)
+    plan = ops.plan_shared_prefix(tables, ctx, 16, 2, 1, device=None)
+    assert plan.groups == 1
+    words = plan.host
+
+    def call(w, dev=16, desc=d, nwords=None):
+        opts = ops.DecodeOpts(0, 0, 0, w.ctypes.data, dev, w.size if nwords is None else nwords)
+        return _decode(ops, desc, opts=opts, ws=16, ws_bytes=1 << 30)
+
+    bad = words.copy()
+    bad[0] = 0
+    assert call(bad) == 1                                   # magic
+    assert call(words, nwords=5) == 1                       # truncated
+    assert call(words, dev=0) == 1                          # no device copy
+    bad = words.copy()
+    bad[1] = 5
+    assert call(bad) == 1                                   # other batch size
+    bad = words.copy()
+    bad[6 + 4 + 3] = 9
+    assert call(bad) == 1                                   # leader outside the batch
+    bad = words.copy()
+    bad[6 + 2] = 3
+    assert call(bad) == 1                                   # member with another prefix
+    assert call(words, desc=_desc(ops, dtype=ops.PKV_F32)) == 2  # cascade needs bf16
+    opts = ops.DecodeOpts(0, 0, 0, words.ctypes.data, 16, words.size)
+    ws = ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(opts))
+    assert ws > 0  # the prefix partials live in the workspace
+    assert _decode(ops, d, opts=opts, ws=16, ws_bytes=ws - 16) == 3

@@ -1,0 +1,150 @@
+"""Cascade decode (shared-prefix pass + suffix pass merged) against the CPU
+oracle, through the C ABI (needs an MI355X).
+
+The oracle knows nothing of prefixes: it resolves every sequence's table into
+contiguous keys/values and attends over all of them, so these tests check that
+splitting the walk at the shared prefix, computing the prefix once for the
+whole group on matrix cores and merging the softmax states changes nothing
+beyond rounding (tolerances in gpu_harness.check_attention).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import GpuWorkload, check_attention, out_to_f64
+from logical_model import oracle_pools
+from paged_kv_cache_334_amd.workloads import generate, prefix_group_of
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from paged_kv_cache_334_amd import ops
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+CASES = {
+    # group 4, block 16, copy-on-write of the last blocks
+    "g4-bs16": lambda: generate("shared-prefix", num_seqs=12, shared_prefix=512, ctx=(16, 100), num_heads=8,
+                                num_kv_heads=2, cow_fraction=0.25),
+    # group 8, three prefix groups and private sequences, ragged one-token suffixes
+    "g8-groups": lambda: generate("shared-prefix", num_seqs=23, shared_prefix=320, ctx=(1, 70), num_heads=16,
+                                  num_kv_heads=2, prefix_groups=3, unshared_seqs=5),
+    # group 1 (plain multi-head), block 32
+    "g1-bs32": lambda: generate("shared-prefix", num_seqs=9, shared_prefix=640, ctx=(1, 90), num_heads=4,
+                                num_kv_heads=4, block_size=32),
+    # group 2, block 32, outlier keys in the suffixes
+    "g2-bs32-outliers": lambda: generate("shared-prefix", num_seqs=10, shared_prefix=448, ctx=(20, 200),
+                                         num_heads=4, num_kv_heads=2, block_size=32, outlier_fraction=0.05),
+    # more rows than one 128-row tile (150 x 4 = 600 rows), a long prefix split into several chunks
+    "g4-many-rows": lambda: generate("shared-prefix", num_seqs=150, shared_prefix=2048, ctx=(1, 40), num_heads=8,
+                                     num_kv_heads=2),
+}
+
+
+@pytest.fixture(scope="module", params=sorted(CASES))
+def case(request):
+    name = request.param
+    _say(f"[cascade] building {name}")
+    wl = CASES[name]()
+    gw = GpuWorkload(wl)
+    desc, kp, vp = oracle_pools(wl)
+    ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale)
+    plan = ops.plan_shared_prefix(wl.block_tables, wl.context_lens, wl.spec.block_size, min_group_seqs=2,
+                                  min_prefix_blocks=1)
+    return name, wl, gw, ref, plan
+
+
+def test_plan_finds_the_generated_groups(case):
+    name, wl, _, _, plan = case
+    want = {prefix_group_of(wl.spec, b) for b in range(wl.spec.num_seqs)} - {-1}
+    assert plan.groups == len(want), name
+    pb = plan.prefix_blocks()
+    for b in range(wl.spec.num_seqs):
+        shared = prefix_group_of(wl.spec, b) >= 0
+        assert (pb[b] == wl.spec.shared_prefix // wl.spec.block_size) if shared else pb[b] == 0
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_cascade_matches_oracle(case, out_dtype):
+    name, wl, gw, ref, plan = case
+    _say(f"[cascade] decode {name} out={out_dtype}")
+    odt = torch.float32 if out_dtype == "f32" else None
+    out = gw.decode(prefix_plan=plan, out_dtype=odt)
+    torch.cuda.synchronize()
+    check_attention(out_to_f64(out), ref, "bf16", out_dtype, f"cascade/{name}")
+
+
+def test_cascade_close_to_plain_decode(case):
+    name, wl, gw, _, plan = case
+    _say(f"[cascade] vs plain {name}")
+    a = out_to_f64(gw.decode(prefix_plan=plan, out_dtype=torch.float32))
+    b = out_to_f64(gw.decode(out_dtype=torch.float32))
+    assert np.abs(a - b).max() <= 2e-3
+
+
+def test_cascade_deterministic(case):
+    name, wl, gw, _, plan = case
+    _say(f"[cascade] determinism {name}")
+    a = out_to_f64(gw.decode(prefix_plan=plan))
+    b = out_to_f64(gw.decode(prefix_plan=plan))
+    assert np.array_equal(a, b)
+
+
+def test_empty_suffix_merges_prefix_only():
+    """A sequence whose context ends exactly at the end of the shared prefix:
+    the suffix pass reads nothing and the output is the prefix alone."""
+    wl = CASES["g4-bs16"]()
+    _say("[cascade] empty suffix")
+    gw = GpuWorkload(wl)
+    desc, kp, vp = oracle_pools(wl)
+    ctx = wl.context_lens.copy()
+    ctx[[1, 4]] = wl.spec.shared_prefix
+    ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, ctx, wl.scale)
+    gw.context_lens = torch.from_numpy(ctx).cuda()
+    plan = ops.plan_shared_prefix(wl.block_tables, ctx, 16, min_group_seqs=2, min_prefix_blocks=1)
+    assert plan.prefix_blocks()[1] == wl.spec.shared_prefix // 16
+    out = gw.decode(prefix_plan=plan, out_dtype=torch.float32, max_context_len=int(ctx.max()))
+    check_attention(out_to_f64(out), ref, "bf16", "f32", "cascade/empty-suffix")
+
+
+def test_bad_prefix_block_gives_nan_rows_of_the_group_only():
+    wl = CASES["g8-groups"]()
+    _say("[cascade] bad prefix block id")
+    gw = GpuWorkload(wl)
+    plan = ops.plan_shared_prefix(wl.block_tables, wl.context_lens, 16, min_group_seqs=2, min_prefix_blocks=1)
+    good = out_to_f64(gw.decode(prefix_plan=plan))
+    # group 0's leader is sequence 0; its table supplies the prefix ids the prefix pass reads
+    bad = gw.block_tables.clone()
+    bad[0, 3] = wl.num_blocks + 7
+    gw.block_tables = bad
+    out = out_to_f64(gw.decode(prefix_plan=plan))
+    group0 = [b for b in range(wl.spec.num_seqs) if prefix_group_of(wl.spec, b) == 0]
+    others = [b for b in range(wl.spec.num_seqs) if prefix_group_of(wl.spec, b) != 0]
+    assert np.isnan(out[group0]).all()
+    assert np.array_equal(out[others], good[others])
+
+
+def test_full_shared_prefix_workload_sampled():
+    """The full shared-prefix workload (200 sequences, 30000 shared tokens) in the
+    benchmark's launch configuration: cascade with the default plan thresholds."""
+    _say("[cascade] full shared-prefix build")
+    wl = generate("shared-prefix")
+    gw = GpuWorkload(wl)
+    plan = ops.plan_shared_prefix(wl.block_tables, wl.context_lens, 16)
+    assert plan.groups == 1
+    out = out_to_f64(gw.decode(prefix_plan=plan))
+    assert np.isfinite(out).all()
+    desc, kp, vp = oracle_pools(wl)
+    rng = np.random.default_rng(5)
+    seqs = sorted({int(np.argmax(wl.context_lens)), int(np.argmin(wl.context_lens)),
+                   *rng.integers(0, 200, size=6).tolist()})
+    pairs = [(b, h) for b in seqs for h in rng.choice(32, size=4, replace=False).tolist()]
+    _say(f"[cascade] full oracle on {len(pairs)} rows")
+    ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale, pairs=pairs)
+    got = np.stack([out[b, h] for b, h in pairs])
+    check_attention(got, ref, "bf16", "bf16", "cascade/full")
