@@ -103,8 +103,10 @@ pkv_status plan_cascade(const pkv_pool_desc* pool, int32_t num_seqs, int32_t max
     if (start[b] < 0 || start[b] > max_prefix) return fail(PKV_EINVAL, "prefix plan: bad per-sequence prefix");
   if (tiles > 0x7fffffff) return fail(PKV_EUNSUPPORTED, "prefix plan: too many rows");
   const int64_t per_iter = 64 / pool->block_size;  // blocks the prefix kernel moves per iteration
+  // as many chunks as keep every workgroup of the pass resident at once (a
+  // second, partial round of workgroups would double the pass's time)
   const int64_t units = tiles * pool->num_kv_heads;
-  const int64_t want = (kPrefixTargetWorkgroups + units - 1) / units;
+  const int64_t want = units >= kPrefixTargetWorkgroups ? 1 : kPrefixTargetWorkgroups / units;
   int64_t cb = (max_prefix + want - 1) / want;
   cb = (cb + per_iter - 1) / per_iter * per_iter;
   plan->cascade = true;
@@ -147,8 +149,9 @@ pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_he
   const int tile_bytes = bs * pool->head_dim * elt_bytes(pool->dtype);
   const int inflight = opts ? opts->blocks_in_flight : 0;
   if (inflight < 0 || inflight > 2) return fail(PKV_EINVAL, "blocks_in_flight must be 0, 1 or 2");
-  // two blocks of 4 KiB tiles in flight per wave, one block of larger tiles
-  plan->inflight = inflight ? inflight : (tile_bytes <= 4096 ? 2 : 1);
+  // two blocks of 4 KiB tiles in flight per wave, one block of larger tiles; one
+  // for the short suffixes after a shared prefix (fewer registers, more waves)
+  plan->inflight = inflight ? inflight : ((tile_bytes <= 4096 && !plan->cascade) ? 2 : 1);
   int64_t part_tokens = opts ? opts->partition_tokens : 0;
   if (part_tokens < 0) return fail(PKV_EINVAL, "partition_tokens must be >= 0");
   int64_t bpp;
@@ -250,7 +253,8 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
   a.max_context = max_context_len;
   a.blocks_per_part = plan.blocks_per_part;
   a.num_parts = plan.num_parts;
-  a.longest_first = num_seqs > 1 && num_seqs <= pkv::kMaxRankSeqs;
+  // ordering pays for long walks; after a shared prefix the suffixes are short
+  a.longest_first = !plan.cascade && num_seqs > 1 && num_seqs <= pkv::kMaxRankSeqs;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = out;
   a.out_bf16 = out_dtype == PKV_BF16;
@@ -279,11 +283,12 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
     p.num_blocks = pool->num_blocks;
     p.chunk_blocks = plan.prefix_chunk_blocks;
     p.num_chunks = plan.prefix_chunks;
+    p.num_tiles = plan.prefix_tiles;
     p.scale_log2 = a.scale_log2;
     p.ws_m = pre;
     p.ws_l = pre + rows;
     p.ws_acc = pre + 2 * rows;
-    hipError_t pe = pkv::launch_prefix(p, pool->block_size, plan.group, plan.prefix_tiles, s);
+    hipError_t pe = pkv::launch_prefix(p, pool->block_size, plan.group, s);
     if (pe != hipSuccess) return fail(PKV_EHIP, std::string("prefix launch: ") + hipGetErrorString(pe));
     a.start_blocks = opts->prefix_plan_dev + pkv::kPlanHeader;
     a.prefix_chunks = plan.prefix_chunks;

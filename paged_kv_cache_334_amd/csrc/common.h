@@ -34,6 +34,22 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Two float32 -> packed bfloat16 (a in the low half), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+// Weights for the bf16 matrix cores as hi + lo parts: hi = bf16(p), lo =
+// bf16(p - hi); hi + lo keeps about 16 significant bits of p.
+__device__ __forceinline__ void split_bf16(float a, float b, uint32_t* hi, uint32_t* lo) {
+  const uint32_t h = pack_bf16(a, b);
+  *hi = h;
+  *lo = pack_bf16(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
+}
+
 // Wave-wide uniform value (the compiler keeps it in an SGPR).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

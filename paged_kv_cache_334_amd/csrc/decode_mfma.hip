@@ -121,11 +121,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
       for (int i = 0; i < 4; ++i)
         s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T[u].k[i]), qb[i], s, 0, 0, 0);
 
+      // raw logits; the scale (> 0) is applied to the maximum and inside the exponent
       float sr[4];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) sr[rr] = (4 * kg + rr < valid) ? s[rr] * a.scale_log2 : -INFINITY;
+      for (int rr = 0; rr < 4; ++rr) sr[rr] = (4 * kg + rr < valid) ? s[rr] : -INFINITY;
       float mx = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
-      mx = max_xor32(max_xor16(mx));  // per column (head slot)
+      mx = max_xor32(max_xor16(mx)) * a.scale_log2;  // per column (head slot)
       if (__ballot(mx > m + kRescaleSlack) != 0) {
         const float mn = fmaxf(m, mx);
         const float alpha = fast_exp2(m - mn);
@@ -136,21 +137,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
       }
       float p[4];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) p[rr] = fast_exp2(sr[rr] - m);
+      for (int rr = 0; rr < 4; ++rr) p[rr] = fast_exp2(fmaf(sr[rr], a.scale_log2, -m));
       lsum += (p[0] + p[1]) + (p[2] + p[3]);
 
+      // columns 0..G-1 take the weights' bf16 hi parts, G..2G-1 their lo parts
       uint32_t pw[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        uint32_t half2[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const float pr = p[2 * e + k];
-          const uint32_t hi = f32_to_bf16_rne(pr);
-          const uint32_t lo = f32_to_bf16_rne(pr - __uint_as_float(hi << 16));
-          half2[k] = used ? (lo_slot ? lo : hi) : 0u;
-        }
-        pw[e] = half2[0] | (half2[1] << 16);
+        uint32_t hi, lo;
+        split_bf16(p[2 * e], p[2 * e + 1], &hi, &lo);
+        pw[e] = used ? (lo_slot ? lo : hi) : 0u;
       }
       const s16x4 pb = __builtin_bit_cast(s16x4, make_uint2(pw[0], pw[1]));
 

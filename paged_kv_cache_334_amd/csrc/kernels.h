@@ -8,6 +8,7 @@ namespace pkv {
 
 constexpr int kWaves = 4;          // waves per workgroup in the decode kernels
 constexpr int kMaxRankSeqs = 256;  // most sequences the decode kernels order longest-first (one per thread)
+constexpr int kXcds = 8;           // MI355X dies (XCDs); workgroup i is dispatched to XCD i % 8
 
 // Everything a decode kernel reads, passed by value as the kernel argument.
 struct DecodeArgs {
@@ -70,6 +71,7 @@ struct PrefixArgs {
   int32_t num_blocks;
   int32_t chunk_blocks;  // prefix blocks per workgroup
   int32_t num_chunks;    // chunk slots per (sequence, query head)
+  int32_t num_tiles;     // 128-row tiles over all groups
   float scale_log2;
   float* ws_m;
   float* ws_l;
@@ -84,7 +86,7 @@ hipError_t launch_decode_vector(const DecodeArgs& a, int dtype_bf16, int head_di
                                 int inflight, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, int block_size, int group, int inflight,
                               hipStream_t stream);
-hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, int num_tiles, hipStream_t stream);
+hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeArgs& a, int head_dim, int block_size, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, int64_t k_stride, int64_t v_stride,

@@ -18,15 +18,19 @@
 // current one is computed from LDS, then stores them to the other LDS buffer
 // (two buffers, one barrier per iteration).  The LDS copy keeps the pool's
 // tile layout (keys chunk-major, values dim-major) except that a 32-token
-// value tile is split into two 16-token halves, so the matrix-core operand
-// reads below are conflict-free for both block sizes:
+// value tile is split into two 16-token halves and value rows are swizzled
+// (value_offset), so the matrix-core operand reads below are conflict-free
+// for both block sizes:
 //  * S^T = K . Q^T, v_mfma_f32_16x16x32_bf16: A = keys (lane: token n, lane
 //    group kg -> 16-byte chunk 4i+kg), B = queries (lane: column n, dims
 //    32i+8kg..+7); lane gets S^T[token 4kg+r][column n].
-//  * O^T += V^T . P^T, v_mfma_f32_16x16x16_bf16: A = values (lane: dim
-//    16nt+n, tokens 4kg..4kg+3, 8 bytes), B = the lane's own 4 weights.
-//    Weights go in as bf16 hi + lo parts (two instructions), keeping ~16
-//    significant bits.
+//  * O^T += V^T . P^T over 32 tokens (two sub-tiles), v_mfma_f32_16x16x32_bf16:
+//    the contraction index k = 8kg + j stands for token 4kg + j of the first
+//    sub-tile (j < 4) or of the second, so B = the lane's own 8 weights and
+//    A = values of dim 16nt+n at those tokens (two 8-byte reads).  Weights go
+//    in as bf16 hi + lo parts (two instructions), keeping ~16 significant bits.
+#include <type_traits>
+
 #include "decode_common.h"
 
 namespace pkv {
@@ -40,8 +44,14 @@ constexpr int ROWS_PER_WAVE = 32; // two MFMA column tiles
 constexpr int STAGE_HALF = TOK * HD * 2;  // bytes of keys (or values) per iteration: 16 KiB
 constexpr int CHUNKS_PER_THREAD = STAGE_HALF / 16 / (64 * NW);  // 4
 
+// Byte offset, inside a 16-token value tile in LDS, of dim d's 8-byte piece kg
+// (tokens 4kg..4kg+3).  Rows are 32 bytes; dims with bit 3 set have their two
+// 16-byte halves swapped, so the 32 lanes of one half-wave (16 dims, two
+// pieces each) hit all 64 banks once instead of dims d and d+8 sharing banks.
+__device__ __forceinline__ int value_offset(int d, int kg) { return d * 32 + ((kg ^ (((d >> 3) & 1) << 1)) * 8); }
+
 template <int BS, int G>
-__global__ __launch_bounds__(64 * NW) void prefix_kernel(PrefixArgs p) {
+__global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   constexpr int NB = TOK / BS;          // blocks per iteration
   constexpr int TILE = BS * HD * 2;     // bytes of one (block, kv head) tile
   constexpr int SUBB = BS / 16;         // 16-token sub-tiles per block
@@ -53,14 +63,21 @@ __global__ __launch_bounds__(64 * NW) void prefix_kernel(PrefixArgs p) {
   const int wave = uniform(threadIdx.x >> 6);
   const int n = lane & 15;
   const int kg = lane >> 4;
-  const int kvh = blockIdx.y;
-  const int chunk = blockIdx.z;
+  // XCD-aware order.  Workgroup i runs on XCD i % 8; a unit (kv head, chunk)
+  // keeps all its row tiles on one XCD, dispatched back to back, so the tiles
+  // after the first find the unit's keys and values in that XCD's L2.
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int unit = (slot / p.num_tiles) * kXcds + xcd;
+  if (unit >= p.num_kv_heads * p.num_chunks) return;
+  const int kvh = unit % p.num_kv_heads;
+  const int chunk = unit / p.num_kv_heads;
 
   // which group and 128-row tile: groups hold their tiles in order
   const int32_t* plan = p.plan;
   const int num_groups = plan[kPlanGroups];
   const int32_t* groups = plan + kPlanHeader + plan[kPlanSeqs];
-  int tile = blockIdx.x, gi = 0;
+  int tile = slot % p.num_tiles, gi = 0;
   int gprefix = 0, gbegin = 0, gcount = 0, leader = 0;
   for (; gi < num_groups; ++gi) {
     const int32_t* gr = groups + kGroupWords * gi;
@@ -141,10 +158,12 @@ __global__ __launch_bounds__(64 * NW) void prefix_kernel(PrefixArgs p) {
       const int kb = c / (TILE / 16);
       const int off = (c % (TILE / 16)) * 16;
       *reinterpret_cast<uint4*>(&lds[buf][0][kb * TILE + off]) = sk[k];
-      // values: dim d, tokens 8q..8q+7 of the block -> half q/2 (16-token [D][16] tile), position 8*(q%2)
+      // values: dim d, tokens 8q..8q+7 of the block -> half q/2 (a 16-token [D][16]
+      // tile), 16-byte slot (q%2) of the dim's 32-byte row, swapped for dims with
+      // bit 3 set (see value_offset)
       const int d = off / (BS * 2);
       const int q8 = (off % (BS * 2)) / 16;
-      const int voff = kb * TILE + (q8 / 2) * (HD * 32) + d * 32 + (q8 % 2) * 16;
+      const int voff = kb * TILE + (q8 / 2) * (HD * 32) + d * 32 + (((q8 % 2) ^ ((d >> 3) & 1)) * 16);
       *reinterpret_cast<uint4*>(&lds[buf][1][voff]) = sv[k];
     }
   };
@@ -156,6 +175,93 @@ __global__ __launch_bounds__(64 * NW) void prefix_kernel(PrefixArgs p) {
     for (int nt = 0; nt < 8; ++nt) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
 
+  // One iteration (64 tokens) of the wave's rows from LDS buffer `buf`, as two
+  // 32-token pairs: S^T for the pair's two sub-tiles, the online-softmax
+  // update, then P.V.  FULL: all 64 tokens present (every iteration but
+  // possibly a chunk's last), so no masking is compiled in.
+  auto compute = [&](auto full, int buf, int valid_tokens) {
+    constexpr bool FULL = decltype(full)::value;
+#pragma unroll
+    for (int pair = 0; pair < 2; ++pair) {
+      if (!FULL && 32 * pair >= valid_tokens) break;
+      f32x4 s[2][2];  // [sub-tile of the pair][column tile]
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int sub = 2 * pair + h2;
+        const unsigned char* kt = &lds[buf][0][(sub / SUBB) * TILE];
+        const int ts = (sub % SUBB) * 16;
+        bf16x8 ka[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ka[i] = *reinterpret_cast<const bf16x8*>(kt + ((4 * i + kg) * BS + ts + n) * 16);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          s[h2][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            s[h2][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i], qb[ct][i], s[h2][ct], 0, 0, 0);
+        }
+      }
+      if (!FULL && 32 * pair + 16 >= valid_tokens)  // second sub-tile past the chunk's end: no weight
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) s[1][ct] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      // column maxima of the raw logits (the scale, > 0, is applied after)
+      float mx[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const float a = fmaxf(fmaxf(fmaxf(s[0][ct][0], s[0][ct][1]), fmaxf(s[0][ct][2], s[0][ct][3])),
+                              fmaxf(fmaxf(s[1][ct][0], s[1][ct][1]), fmaxf(s[1][ct][2], s[1][ct][3])));
+        mx[ct] = max_xor32(max_xor16(a)) * p.scale_log2;
+      }
+      if (__ballot(mx[0] > m[0] + kRescaleSlack || mx[1] > m[1] + kRescaleSlack) != 0) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const float mn = fmaxf(m[ct], mx[ct]);
+          const float alpha = fast_exp2(m[ct] - mn);
+          lsum[ct] *= alpha;
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) o[ct][nt] *= alpha;
+          m[ct] = mn;
+        }
+      }
+      // the P.V contraction takes the pair's weights in the order k = 8kg + j <->
+      // token 4kg + j of the first sub-tile (j < 4) or of the second
+      bf16x8 pb_hi[2], pb_lo[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const float neg_m = -m[ct];
+        float pr[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pr[r] = fast_exp2(fmaf(s[0][ct][r], p.scale_log2, neg_m));
+          pr[4 + r] = fast_exp2(fmaf(s[1][ct][r], p.scale_log2, neg_m));
+        }
+        lsum[ct] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_bf16(pr[2 * e], pr[2 * e + 1], &hw[e], &lw[e]);
+        pb_hi[ct] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        pb_lo[ct] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      }
+      const int sub0 = 2 * pair, sub1 = 2 * pair + 1;
+      const unsigned char* v0 = &lds[buf][1][(sub0 / SUBB) * TILE + (sub0 % SUBB) * (HD * 32)];
+      const unsigned char* v1 = &lds[buf][1][(sub1 / SUBB) * TILE + (sub1 % SUBB) * (HD * 32)];
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        // a missing second sub-tile's LDS rows hold finite re-read data; its weights are 0
+        const int off = value_offset(16 * nt + n, kg);
+        const uint2 a0 = *reinterpret_cast<const uint2*>(v0 + off);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(v1 + off);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb_hi[ct], o[ct][nt], 0, 0, 0);
+          o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb_lo[ct], o[ct][nt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
   stage_load(0);
   stage_store(0);
   __syncthreads();
@@ -165,59 +271,8 @@ __global__ __launch_bounds__(64 * NW) void prefix_kernel(PrefixArgs p) {
     if (more) stage_load(it + 1);
     if (wave_active) {
       const int valid_tokens = min(TOK, (blk_hi - blk_lo - it * NB) * BS);
-#pragma unroll
-      for (int sub = 0; sub < TOK / 16; ++sub) {
-        if (16 * sub >= valid_tokens) break;
-        const int kb = sub / SUBB;
-        const int ts = (sub % SUBB) * 16;
-        const unsigned char* kt = &lds[buf][0][kb * TILE];
-        const unsigned char* vt = &lds[buf][1][kb * TILE + (sub % SUBB) * (HD * 32)];
-        bf16x8 ka[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ka[i] = *reinterpret_cast<const bf16x8*>(kt + ((4 * i + kg) * BS + ts + n) * 16);
-        s16x4 pb_hi[2], pb_lo[2];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i], qb[ct][i], s, 0, 0, 0);
-          float sr[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sr[r] = s[r] * p.scale_log2;
-          float mx = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
-          mx = max_xor32(max_xor16(mx));
-          if (__ballot(mx > m[ct] + kRescaleSlack) != 0) {
-            const float mn = fmaxf(m[ct], mx);
-            const float alpha = fast_exp2(m[ct] - mn);
-            lsum[ct] *= alpha;
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) o[ct][nt] *= alpha;
-            m[ct] = mn;
-          }
-          float pr[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sr[r] - m[ct]);
-          lsum[ct] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-          uint32_t hi[4], lo[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            hi[r] = f32_to_bf16_rne(pr[r]);
-            lo[r] = f32_to_bf16_rne(pr[r] - __uint_as_float(hi[r] << 16));
-          }
-          pb_hi[ct] = __builtin_bit_cast(s16x4, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
-          pb_lo[ct] = __builtin_bit_cast(s16x4, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
-        }
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const s16x4 va = *reinterpret_cast<const s16x4*>(vt + ((16 * nt + n) * 16 + 4 * kg) * 2);
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_hi[ct], o[ct][nt], 0, 0, 0);
-            o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_lo[ct], o[ct][nt], 0, 0, 0);
-          }
-        }
-      }
+      if (valid_tokens == TOK) compute(std::true_type{}, buf, TOK);
+      else compute(std::false_type{}, buf, valid_tokens);
     }
     if (more) stage_store(buf ^ 1);
     __syncthreads();
@@ -249,8 +304,11 @@ __global__ __launch_bounds__(64 * NW) void prefix_kernel(PrefixArgs p) {
 
 }  // namespace
 
-hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, int num_tiles, hipStream_t s) {
-  const dim3 grid(num_tiles, p.num_kv_heads, p.num_chunks);
+hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, hipStream_t s) {
+  const int64_t units = (int64_t)p.num_kv_heads * p.num_chunks;
+  const int64_t wgs = (units + kXcds - 1) / kXcds * kXcds * p.num_tiles;
+  if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs);
   const dim3 block(64 * NW);
 #define PKV_PREFIX(BS, G) hipLaunchKernelGGL((prefix_kernel<BS, G>), grid, block, 0, s, p)
   if (block_size == 16) {
