@@ -95,6 +95,10 @@ typedef struct {
   /* Blocks whose key/value tiles one wave loads before it uses the first:
    * 0 = chosen by the library, else 1 or 2. */
   int32_t blocks_in_flight;
+  /* Kv heads one workgroup walks together, sharing the block-id lookups:
+   * 0 = chosen by the library, 1, or 2 (one query head per kv head, an even
+   * number of kv heads, one block in flight, vector kernel). */
+  int32_t heads_per_workgroup;
   /* Cascade decode over shared prefixes (bf16, head_dim 128): the plan words
    * pkv_plan_shared_prefix() wrote for these block tables and context lengths,
    * in HOST memory (read during the call) and the same words copied to DEVICE

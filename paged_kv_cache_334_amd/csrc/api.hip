@@ -52,6 +52,7 @@ struct Plan {
   int blocks_per_part = 1;
   int num_parts = 1;
   int inflight = 1;
+  int heads_per_wg = 1;
   // cascade over shared prefixes
   bool cascade = false;
   int prefix_tiles = 0;         // 128-row tiles over all groups
@@ -97,10 +98,13 @@ pkv_status plan_cascade(const pkv_pool_desc* pool, int32_t num_seqs, int32_t max
         return fail(PKV_EINVAL, "prefix plan: member outside the batch or with another prefix");
     }
     tiles += ((int64_t)count * g + 127) / 128;
-    max_prefix = prefix > max_prefix ? prefix : max_prefix;
+    const int64_t covered = pkv::prefix_covered_blocks(prefix, pool->block_size);
+    max_prefix = covered > max_prefix ? covered : max_prefix;
   }
+  if (max_prefix == 0) return PKV_OK;  // every prefix shorter than one pass iteration: plain decode
   for (int32_t b = 0; b < num_seqs; ++b)
-    if (start[b] < 0 || start[b] > max_prefix) return fail(PKV_EINVAL, "prefix plan: bad per-sequence prefix");
+    if (start[b] < 0 || pkv::prefix_covered_blocks(start[b], pool->block_size) > max_prefix)
+      return fail(PKV_EINVAL, "prefix plan: bad per-sequence prefix");
   if (tiles > 0x7fffffff) return fail(PKV_EUNSUPPORTED, "prefix plan: too many rows");
   const int64_t per_iter = 64 / pool->block_size;  // blocks the prefix kernel moves per iteration
   // as many chunks as keep every workgroup of the pass resident at once (a
@@ -149,9 +153,19 @@ pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_he
   const int tile_bytes = bs * pool->head_dim * elt_bytes(pool->dtype);
   const int inflight = opts ? opts->blocks_in_flight : 0;
   if (inflight < 0 || inflight > 2) return fail(PKV_EINVAL, "blocks_in_flight must be 0, 1 or 2");
-  // two blocks of 4 KiB tiles in flight per wave, one block of larger tiles; one
-  // for the short suffixes after a shared prefix (fewer registers, more waves)
-  plan->inflight = inflight ? inflight : ((tile_bytes <= 4096 && !plan->cascade) ? 2 : 1);
+  // matrix-core kernel: two 4 KiB-tile blocks in flight per wave (its registers
+  // leave room), one for larger tiles and for the short suffixes after a shared
+  // prefix; vector kernel: one (measured 1-2% faster than two at occupancy 4 vs 2)
+  plan->inflight = inflight ? inflight : ((plan->mfma && tile_bytes <= 4096 && !plan->cascade) ? 2 : 1);
+  const int hpw = opts ? opts->heads_per_workgroup : 0;
+  if (hpw < 0 || hpw > 2) return fail(PKV_EINVAL, "heads_per_workgroup must be 0, 1 or 2");
+  const bool pairs_ok = !plan->mfma && g == 1 && pool->num_kv_heads % 2 == 0;
+  if (hpw == 2 && !pairs_ok) return fail(PKV_EUNSUPPORTED, "two kv heads per workgroup need the vector kernel, one query head per kv head and an even kv-head count");
+  if (hpw == 2) {
+    if (inflight == 2) return fail(PKV_EUNSUPPORTED, "two kv heads per workgroup take one block in flight");
+    plan->inflight = 1;
+  }
+  plan->heads_per_wg = hpw ? hpw : 1;
   int64_t part_tokens = opts ? opts->partition_tokens : 0;
   if (part_tokens < 0) return fail(PKV_EINVAL, "partition_tokens must be >= 0");
   int64_t bpp;
@@ -299,7 +313,7 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
   }
   hipError_t e = plan.mfma ? pkv::launch_decode_mfma(a, pool->head_dim, pool->block_size, plan.group, plan.inflight, s)
                            : pkv::launch_decode_vector(a, bf16, pool->head_dim, pool->block_size, plan.group,
-                                                       plan.inflight, s);
+                                                       plan.inflight, plan.heads_per_wg, s);
   if (e != hipSuccess) return fail(PKV_EHIP, std::string("decode launch: ") + hipGetErrorString(e));
   if (plan.num_parts > 1) {
     e = pkv::launch_splitk_reduce(a, pool->head_dim, pool->block_size, s);

@@ -18,15 +18,22 @@ namespace pkv {
 struct SeqPick {
   int b;
   int ctx_raw;
-  int start;  // blocks covered by a shared-prefix pass (0 without one)
+  int start;  // blocks covered by a shared-prefix pass (0 without one), not yet clipped to the context
 };
 
+// Blocks of sequence b that the shared-prefix pass covered (0 without one).
+template <int BS>
+__device__ __forceinline__ int covered_start(const DecodeArgs& a, int b) {
+  return a.start_blocks ? prefix_covered_blocks(max(a.start_blocks[b], 0), BS) : 0;
+}
+
+template <int BS>
 __device__ __forceinline__ SeqPick pick_sequence(const DecodeArgs& a, int* sm_key, int* sm_pick) {
   if (!a.longest_first) {
     SeqPick p;
     p.b = blockIdx.z;
     p.ctx_raw = a.context_lens[p.b];
-    p.start = a.start_blocks ? a.start_blocks[p.b] : 0;
+    p.start = covered_start<BS>(a, p.b);
     return p;
   }
   const int t = threadIdx.x;
@@ -53,7 +60,7 @@ __device__ __forceinline__ SeqPick pick_sequence(const DecodeArgs& a, int* sm_ke
   SeqPick p;
   p.b = sm_pick[0];
   p.ctx_raw = sm_pick[1];
-  p.start = a.start_blocks ? a.start_blocks[p.b] : 0;
+  p.start = covered_start<BS>(a, p.b);
   return p;
 }
 
@@ -79,7 +86,7 @@ __device__ __forceinline__ PartRange part_range(const DecodeArgs& a, const SeqPi
   r.ctx_bad = ctx_raw < 0 || ctx_raw > a.max_context;
   r.ctx = r.ctx_bad ? 0 : ctx_raw;
   r.nblocks = (r.ctx + BS - 1) / BS;
-  r.start = min(max(s.start, 0), r.nblocks);
+  r.start = min(s.start, r.nblocks);
   const int rest = r.nblocks - r.start;
   r.nparts = (rest + a.blocks_per_part - 1) / a.blocks_per_part;
   if (r.start > 0 && r.nparts == 0) r.nparts = 1;  // an empty suffix still merges the prefix partials
@@ -127,7 +134,7 @@ struct WaveIds {
 __device__ __forceinline__ WaveIds wave_ids_begin(const DecodeArgs& a, const SeqPick& s, int wave, int lane) {
   WaveIds w;
   const int b = s.b;
-  const int first = max(s.start, 0) + blockIdx.x * a.blocks_per_part + wave;
+  const int first = s.start + blockIdx.x * a.blocks_per_part + wave;
   w.row = a.block_tables + (int64_t)b * a.max_blocks + first;
   w.limit = a.max_blocks - first;
   w.chunk = 0;

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
   const bool lo_slot = n >= G;
   const int hslot = n % G;
 
-  const SeqPick seq = pick_sequence(a, sm_key, sm_pick);
+  const SeqPick seq = pick_sequence<BS>(a, sm_key, sm_pick);
   WaveIds wids = wave_ids_begin(a, seq, wave, lane);
   bf16x8 qb[4];
   {

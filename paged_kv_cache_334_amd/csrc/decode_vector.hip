@@ -35,8 +35,9 @@ namespace pkv {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-template <bool BF16, int HD, int BS, int G, int U>
+template <bool BF16, int HD, int BS, int G, int HP, int U>
 __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a) {
+  constexpr int R = HP * G;         // query heads of the workgroup: kv heads y*HP .. y*HP+HP-1
   constexpr int NW = kWaves;
   constexpr int ELT = BF16 ? 2 : 4;
   constexpr int X = 16 / ELT;       // elements per 16-byte chunk
@@ -50,13 +51,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
   static_assert(64 % U == 0, "a round must not straddle two id loads");
 
   struct Tile {
-    uint4 k[KC];
-    uint4 v[VC];
+    uint4 k[HP][KC];
+    uint4 v[HP][VC];
   };
 
-  __shared__ float sm_acc[NW][G][HD];
-  __shared__ float sm_m[NW][G];
-  __shared__ float sm_l[NW][G];
+  __shared__ float sm_acc[NW][R][HD];
+  __shared__ float sm_m[NW][R];
+  __shared__ float sm_l[NW][R];
   __shared__ int sm_bad[NW];
   __shared__ int sm_key[kMaxRankSeqs];
   __shared__ int sm_pick[2];
@@ -70,13 +71,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
   // Issued together before the context length is known: the wave's first
   // block ids (table entries past the sequence's end may be read, never used)
   // and q.
-  const SeqPick seq = pick_sequence(a, sm_key, sm_pick);
+  const SeqPick seq = pick_sequence<BS>(a, sm_key, sm_pick);
   WaveIds wids = wave_ids_begin(a, seq, wave, lane);
-  uint32_t qw[G][KC][4];  // the q chunks this lane meets in the key pass (bf16 pairs kept packed)
+  uint32_t qw[R][KC][4];  // the q chunks this lane meets in the key pass (bf16 pairs kept packed)
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < R; ++h) {
     const char* qrow =
-        reinterpret_cast<const char*>(a.q) + ((int64_t)seq.b * a.num_heads + blockIdx.y * G + h) * HD * ELT;
+        reinterpret_cast<const char*>(a.q) + ((int64_t)seq.b * a.num_heads + blockIdx.y * R + h) * HD * ELT;
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
       const uint4 w = load16(qrow + (grp + GK * i) * 16);
@@ -88,21 +89,22 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
   }
 
   const PartRange r = part_range<BS>(a, seq);
-  if (finish_if_empty<G, HD>(a, r)) return;
+  if (finish_if_empty<R, HD>(a, r)) return;
   const int cnt = wave_block_count(r, wave);  // blocks of this wave
   int bad = wave_ids_check(a, &wids, cnt, lane);
 
-  float m[G], lsum[G], acc[G][VC];
+  float m[R], lsum[R], acc[R][VC];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < R; ++h) {
     m[h] = -INFINITY;
     lsum[h] = 0.f;
 #pragma unroll
     for (int j = 0; j < VC; ++j) acc[h][j] = 0.f;
   }
 
-  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (int64_t)r.kvh * TILE_BYTES;
-  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)r.kvh * TILE_BYTES;
+  // the HP kv heads of one block are adjacent tiles
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (int64_t)r.kvh * HP * TILE_BYTES;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)r.kvh * HP * TILE_BYTES;
   const int64_t block_bytes = (int64_t)a.num_kv_heads * TILE_BYTES;
 
   // loads of round rnd: the wave's blocks rnd*U .. rnd*U+U-1 (a missing one
@@ -112,12 +114,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
     for (int u = 0; u < U; ++u) {
       const int i = min(rnd * U + u, cnt - 1);
       const int64_t off = (int64_t)wave_id_at(a, &wids, i, cnt, lane, &bad) * block_bytes;
-      const auto kt = tile_rsrc(kbase + off, TILE_BYTES);
-      const auto vt = tile_rsrc(vbase + off, TILE_BYTES);
+      const auto kt = tile_rsrc(kbase + off, HP * TILE_BYTES);
+      const auto vt = tile_rsrc(vbase + off, HP * TILE_BYTES);
 #pragma unroll
-      for (int c = 0; c < KC; ++c) T[u].k[c] = bload16(kt, ((grp + GK * c) * BS + t) * 16);
+      for (int hp = 0; hp < HP; ++hp) {
 #pragma unroll
-      for (int c = 0; c < VC; ++c) T[u].v[c] = bload16(vt, (lane + 64 * c) * 16);
+        for (int c = 0; c < KC; ++c) T[u].k[hp][c] = bload16(kt, hp * TILE_BYTES + ((grp + GK * c) * BS + t) * 16);
+#pragma unroll
+        for (int c = 0; c < VC; ++c) T[u].v[hp][c] = bload16(vt, hp * TILE_BYTES + (lane + 64 * c) * 16);
+      }
     }
   };
 
@@ -131,27 +136,30 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
       // value rows past the context may hold NaN: clear their bits (a zero weight is not enough)
       if (valid < BS) {
 #pragma unroll
-        for (int c = 0; c < VC; ++c) {
-          uint32_t ws[4] = {T[u].v[c].x, T[u].v[c].y, T[u].v[c].z, T[u].v[c].w};
+        for (int hp = 0; hp < HP; ++hp)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if constexpr (BF16) {
-              if (tk + 2 * e >= valid) ws[e] &= 0xffff0000u;
-              if (tk + 2 * e + 1 >= valid) ws[e] &= 0x0000ffffu;
-            } else {
-              if (tk + e >= valid) ws[e] = 0u;
+          for (int c = 0; c < VC; ++c) {
+            uint32_t ws[4] = {T[u].v[hp][c].x, T[u].v[hp][c].y, T[u].v[hp][c].z, T[u].v[hp][c].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if constexpr (BF16) {
+                if (tk + 2 * e >= valid) ws[e] &= 0xffff0000u;
+                if (tk + 2 * e + 1 >= valid) ws[e] &= 0x0000ffffu;
+              } else {
+                if (tk + e >= valid) ws[e] = 0u;
+              }
             }
+            T[u].v[hp][c] = make_uint4(ws[0], ws[1], ws[2], ws[3]);
           }
-          T[u].v[c] = make_uint4(ws[0], ws[1], ws[2], ws[3]);
-        }
       }
 
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int h = 0; h < R; ++h) {
+        const int hp = h / G;  // kv head (tile) of query head h
         float s = 0.f, s2 = 0.f;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-          const uint32_t ws[4] = {T[u].k[c].x, T[u].k[c].y, T[u].k[c].z, T[u].k[c].w};
+          const uint32_t ws[4] = {T[u].k[hp][c].x, T[u].k[hp][c].y, T[u].k[hp][c].z, T[u].k[hp][c].w};
           if constexpr (BF16) {
 #pragma unroll
             for (int e = 0; e < 4; e += 2) {
@@ -191,7 +199,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
         for (int e = 0; e < X; ++e) pv[e] = shfl(p, tk + e);
 #pragma unroll
         for (int c = 0; c < VC; ++c) {
-          const uint32_t ws[4] = {T[u].v[c].x, T[u].v[c].y, T[u].v[c].z, T[u].v[c].w};
+          const uint32_t ws[4] = {T[u].v[hp][c].x, T[u].v[hp][c].y, T[u].v[hp][c].z, T[u].v[hp][c].w};
           float racc = acc[h][c];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -214,7 +222,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
   // wave totals: the weight sum over the tokens of lane group 0 (every group
   // holds the same weights), and the RC lanes sharing a dim add their partial sums
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < R; ++h) {
     float l = row_sum16(lsum[h]);
     if constexpr (BS == 32) l = sum_xor16(l);
 #pragma unroll
@@ -231,7 +239,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
   }
   if (lane == 0) sm_bad[wave] = bad;
   __syncthreads();
-  merge_waves_and_store<G, HD, NW>(a, r, sm_acc, sm_m, sm_l, sm_bad);
+  merge_waves_and_store<R, HD, NW>(a, r, sm_acc, sm_m, sm_l, sm_bad);
 }
 
 bool vector_supported(int bf16, int hd, int bs, int g) {
@@ -239,33 +247,52 @@ bool vector_supported(int bf16, int hd, int bs, int g) {
   return (hd == 64 || hd == 128) && (bs == 16 || bs == 32) && (g == 1 || g == 2 || g == 4 || g == 8);
 }
 
-template <bool BF16, int HD, int BS, int U>
+template <bool BF16, int HD, int BS, int HP, int U>
 static hipError_t dispatch_g(const DecodeArgs& a, int g, hipStream_t s) {
-  const dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
+  const dim3 grid(a.num_parts, a.num_kv_heads / HP, a.num_seqs);
   const dim3 block(64 * kWaves);
   switch (g) {
-    case 1: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 1, U>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 2, U>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 4, U>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 8, U>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 1, HP, U>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 2, HP, U>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 4, HP, U>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 8, HP, U>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <bool BF16, int U>
+template <bool BF16, int HP, int U>
 static hipError_t dispatch_shape(const DecodeArgs& a, int hd, int bs, int g, hipStream_t s) {
-  if (hd == 64 && bs == 16) return dispatch_g<BF16, 64, 16, U>(a, g, s);
-  if (hd == 64 && bs == 32) return dispatch_g<BF16, 64, 32, U>(a, g, s);
-  if (hd == 128 && bs == 16) return dispatch_g<BF16, 128, 16, U>(a, g, s);
-  if (hd == 128 && bs == 32) return dispatch_g<BF16, 128, 32, U>(a, g, s);
+  if (hd == 64 && bs == 16) return dispatch_g<BF16, 64, 16, HP, U>(a, g, s);
+  if (hd == 64 && bs == 32) return dispatch_g<BF16, 64, 32, HP, U>(a, g, s);
+  if (hd == 128 && bs == 16) return dispatch_g<BF16, 128, 16, HP, U>(a, g, s);
+  if (hd == 128 && bs == 32) return dispatch_g<BF16, 128, 32, HP, U>(a, g, s);
   return hipErrorInvalidValue;
 }
 
+// two kv heads per workgroup (single-query groups only: their registers then
+// match a group of two); grid y runs over kv-head pairs
+template <bool BF16, int U>
+static hipError_t dispatch_pairs(const DecodeArgs& a, int hd, int bs, hipStream_t s) {
+  const dim3 grid(a.num_parts, a.num_kv_heads / 2, a.num_seqs);
+  const dim3 block(64 * kWaves);
+  if (hd == 64 && bs == 16) hipLaunchKernelGGL((decode_vector_kernel<BF16, 64, 16, 1, 2, U>), grid, block, 0, s, a);
+  else if (hd == 64 && bs == 32) hipLaunchKernelGGL((decode_vector_kernel<BF16, 64, 32, 1, 2, U>), grid, block, 0, s, a);
+  else if (hd == 128 && bs == 16) hipLaunchKernelGGL((decode_vector_kernel<BF16, 128, 16, 1, 2, U>), grid, block, 0, s, a);
+  else if (hd == 128 && bs == 32) hipLaunchKernelGGL((decode_vector_kernel<BF16, 128, 32, 1, 2, U>), grid, block, 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_vector(const DecodeArgs& a, int bf16, int hd, int bs, int g, int inflight,
-                                hipStream_t s) {
-  if (inflight == 1) return bf16 ? dispatch_shape<true, 1>(a, hd, bs, g, s) : dispatch_shape<false, 1>(a, hd, bs, g, s);
-  if (inflight == 2) return bf16 ? dispatch_shape<true, 2>(a, hd, bs, g, s) : dispatch_shape<false, 2>(a, hd, bs, g, s);
+                                int heads_per_wg, hipStream_t s) {
+  if (heads_per_wg == 2) {
+    if (g != 1 || a.num_kv_heads % 2 || inflight != 1) return hipErrorInvalidValue;
+    return bf16 ? dispatch_pairs<true, 1>(a, hd, bs, s) : dispatch_pairs<false, 1>(a, hd, bs, s);
+  }
+  if (heads_per_wg != 1) return hipErrorInvalidValue;
+  if (inflight == 1) return bf16 ? dispatch_shape<true, 1, 1>(a, hd, bs, g, s) : dispatch_shape<false, 1, 1>(a, hd, bs, g, s);
+  if (inflight == 2) return bf16 ? dispatch_shape<true, 1, 2>(a, hd, bs, g, s) : dispatch_shape<false, 1, 2>(a, hd, bs, g, s);
   return hipErrorInvalidValue;
 }
 

@@ -50,6 +50,15 @@ struct DecodeArgs {
 //   [5] total members, then prefix_blocks[num_seqs], then per group
 //   {prefix_blocks, member_begin, member_count, leader}, then the member lists.
 constexpr int32_t kPlanMagic = 0x504b5650;  // "PKVP"
+
+// The shared-prefix pass moves 64 tokens per iteration and handles whole
+// iterations only: it covers the largest multiple of 64/block_size blocks of
+// a group's prefix, and the suffix pass starts there (reading the at most
+// 64/block_size - 1 remaining prefix blocks per sequence, from cache).
+constexpr int kPrefixIterTokens = 64;
+__host__ __device__ constexpr int prefix_covered_blocks(int prefix_blocks, int block_size) {
+  return prefix_blocks / (kPrefixIterTokens / block_size) * (kPrefixIterTokens / block_size);
+}
 constexpr int kPlanSeqs = 1;
 constexpr int kPlanBlockSize = 2;
 constexpr int kPlanGroups = 3;
@@ -81,9 +90,10 @@ struct PrefixArgs {
 bool vector_supported(int dtype_bf16, int head_dim, int block_size, int group);
 bool mfma_supported(int dtype_bf16, int head_dim, int block_size, int group);
 
-// inflight = blocks whose tiles one wave loads before using the first (1 or 2)
+// inflight = blocks whose tiles one wave loads before using the first (1 or 2);
+// heads_per_wg = kv heads one workgroup walks together (2 only for group 1, inflight 1)
 hipError_t launch_decode_vector(const DecodeArgs& a, int dtype_bf16, int head_dim, int block_size, int group,
-                                int inflight, hipStream_t stream);
+                                int inflight, int heads_per_wg, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, int block_size, int group, int inflight,
                               hipStream_t stream);
 hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, hipStream_t stream);

@@ -13,10 +13,9 @@
 // writes a partial (max, sum, acc) per row; the suffix pass merges them.
 //
 // Workgroup = 4 waves x 32 query rows (two 16-column MFMA tiles per wave).
-// Per iteration 64 prefix tokens: every thread loads four 16-byte key chunks
-// and four value chunks of the next iteration into registers while the
-// current one is computed from LDS, then stores them to the other LDS buffer
-// (two buffers, one barrier per iteration).  The LDS copy keeps the pool's
+// Per iteration 64 prefix tokens: the next iteration's key and value tiles
+// travel from memory straight into the other LDS buffer (global_load_lds)
+// while the current one is computed (two buffers, one barrier per iteration).  The LDS copy keeps the pool's
 // tile layout (keys chunk-major, values dim-major) except that a 32-token
 // value tile is split into two 16-token halves and value rows are swizzled
 // (value_offset), so the matrix-core operand reads below are conflict-free
@@ -29,8 +28,6 @@
 //    sub-tile (j < 4) or of the second, so B = the lane's own 8 weights and
 //    A = values of dim 16nt+n at those tokens (two 8-byte reads).  Weights go
 //    in as bf16 hi + lo parts (two instructions), keeping ~16 significant bits.
-#include <type_traits>
-
 #include "decode_common.h"
 
 namespace pkv {
@@ -38,11 +35,30 @@ namespace pkv {
 namespace {
 
 constexpr int HD = 128;
-constexpr int TOK = 64;           // prefix tokens per iteration
+constexpr int TOK = kPrefixIterTokens;  // prefix tokens per iteration
 constexpr int NW = kWaves;        // 4
 constexpr int ROWS_PER_WAVE = 32; // two MFMA column tiles
 constexpr int STAGE_HALF = TOK * HD * 2;  // bytes of keys (or values) per iteration: 16 KiB
-constexpr int CHUNKS_PER_THREAD = STAGE_HALF / 16 / (64 * NW);  // 4
+
+// LDS byte address of a __shared__ location.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from gbase + voff (gbase wave-uniform) into LDS at
+// lds + 16*lane.  Issued as inline assembly so that the compiler's own
+// counter waits do not treat every LDS read as dependent on it; the caller
+// waits with lds_dma_wait_all() before a barrier.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, const void* gbase, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds), "v"(voff), "s"(gbase)
+      : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Byte offset, inside a 16-token value tile in LDS, of dim d's 8-byte piece kg
 // (tokens 4kg..4kg+3).  Rows are 32 bytes; dims with bit 3 set have their two
@@ -83,7 +99,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     const int32_t* gr = groups + kGroupWords * gi;
     const int tiles = (gr[2] * G + 127) / 128;
     if (tile < tiles) {
-      gprefix = gr[0];
+      gprefix = prefix_covered_blocks(gr[0], BS);
       gbegin = gr[1];
       gcount = gr[2];
       leader = gr[3];
@@ -132,39 +148,33 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   const int64_t block_bytes = (int64_t)p.num_kv_heads * TILE;
   const int iters = (blk_hi - blk_lo + NB - 1) / NB;
 
-  // staging: thread t moves chunk t + 256*k (k < 4) of the keys and of the values
-  uint4 sk[CHUNKS_PER_THREAD], sv[CHUNKS_PER_THREAD];
-  auto stage_load = [&](int it) {
+  // Staging: per iteration each wave moves four 1 KiB pieces of the keys and
+  // four of the values straight from HBM/L2 into LDS (global_load_lds: lane l
+  // lands at LDS base + 16*l, so a piece is a 1 KiB contiguous run of LDS and
+  // each lane picks the global chunk that belongs at its spot).  The loads
+  // take no registers; the wave waits for them with an explicit counter wait
+  // before the barrier that publishes the buffer.
+  auto stage_issue = [&](int it, int buf) {
     const int first = blk_lo + it * NB;
     if (first - id_base >= 64) {  // next 64 ids
       id_base += 64;
       ids = load_ids(id_base);
     }
 #pragma unroll
-    for (int k = 0; k < CHUNKS_PER_THREAD; ++k) {
-      const int c = threadIdx.x + 64 * NW * k;  // chunk of the stage
-      const int kb = c / (TILE / 16);           // block within the iteration
-      const int off = (c % (TILE / 16)) * 16;   // byte offset within the tile
-      const int j = min(first + kb, blk_hi - 1);  // past the chunk's end: re-read, never used
-      const int64_t base = (int64_t)__builtin_amdgcn_readlane(ids, j - id_base) * block_bytes;
-      sk[k] = load16(kpool + base + off);
-      sv[k] = load16(vpool + base + off);
-    }
-  };
-  auto stage_store = [&](int buf) {
-#pragma unroll
-    for (int k = 0; k < CHUNKS_PER_THREAD; ++k) {
-      const int c = threadIdx.x + 64 * NW * k;
-      const int kb = c / (TILE / 16);
-      const int off = (c % (TILE / 16)) * 16;
-      *reinterpret_cast<uint4*>(&lds[buf][0][kb * TILE + off]) = sk[k];
-      // values: dim d, tokens 8q..8q+7 of the block -> half q/2 (a 16-token [D][16]
-      // tile), 16-byte slot (q%2) of the dim's 32-byte row, swapped for dims with
-      // bit 3 set (see value_offset)
-      const int d = off / (BS * 2);
-      const int q8 = (off % (BS * 2)) / 16;
-      const int voff = kb * TILE + (q8 / 2) * (HD * 32) + d * 32 + (((q8 % 2) ^ ((d >> 3) & 1)) * 16);
-      *reinterpret_cast<uint4*>(&lds[buf][1][voff]) = sv[k];
+    for (int k = 0; k < STAGE_HALF / 1024 / NW; ++k) {
+      const int piece = wave + NW * k;  // 1 KiB piece of the stage
+      const int kb = piece * 1024 / TILE;
+      const int in_tile = piece * 1024 % TILE;
+      const int64_t base = (int64_t)__builtin_amdgcn_readlane(ids, first + kb - id_base) * block_bytes;
+      // keys: the LDS copy keeps the tile's byte order
+      lds_dma16(lds_addr(&lds[buf][0][piece * 1024]), kpool + base, in_tile + lane * 16);
+      // values: LDS position in_tile + 16*lane of a [half][D][16] tile with
+      // swizzled rows -> dim d, 8-token slot q8 of the pool's [D][BS] tile
+      const int half = in_tile / (HD * 32);
+      const int pos = in_tile % (HD * 32) + lane * 16;
+      const int d = pos / 32;
+      const int q8 = 2 * half + (((pos / 16) % 2) ^ ((d >> 3) & 1));
+      lds_dma16(lds_addr(&lds[buf][1][piece * 1024]), vpool + base, d * (BS * 2) + q8 * 16);
     }
   };
 
@@ -175,42 +185,38 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     for (int nt = 0; nt < 8; ++nt) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
 
-  // One iteration (64 tokens) of the wave's rows from LDS buffer `buf`, as two
-  // 32-token pairs: S^T for the pair's two sub-tiles, the online-softmax
-  // update, then P.V.  FULL: all 64 tokens present (every iteration but
-  // possibly a chunk's last), so no masking is compiled in.
-  auto compute = [&](auto full, int buf, int valid_tokens) {
-    constexpr bool FULL = decltype(full)::value;
+  // One iteration (64 tokens, always whole) of the wave's rows from LDS buffer
+  // `buf`.  Program order: S^T of both 32-token pairs (matrix cores), then per
+  // pair the online-softmax update and weights (vector unit) followed by its
+  // P.V (matrix cores).  The second pair's S^T runs while the first pair's
+  // weights are computed, and the first pair's P.V while the second's are.
+  auto compute = [&](int buf) {
+    f32x4 s[4][2];  // [sub-tile][column tile]
 #pragma unroll
-    for (int pair = 0; pair < 2; ++pair) {
-      if (!FULL && 32 * pair >= valid_tokens) break;
-      f32x4 s[2][2];  // [sub-tile of the pair][column tile]
+    for (int sub = 0; sub < 4; ++sub) {
+      const unsigned char* kt = &lds[buf][0][(sub / SUBB) * TILE];
+      const int ts = (sub % SUBB) * 16;
+      bf16x8 ka[4];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int sub = 2 * pair + h2;
-        const unsigned char* kt = &lds[buf][0][(sub / SUBB) * TILE];
-        const int ts = (sub % SUBB) * 16;
-        bf16x8 ka[4];
+      for (int i = 0; i < 4; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kt + ((4 * i + kg) * BS + ts + n) * 16);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          ka[i] = *reinterpret_cast<const bf16x8*>(kt + ((4 * i + kg) * BS + ts + n) * 16);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          s[h2][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            s[h2][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i], qb[ct][i], s[h2][ct], 0, 0, 0);
-        }
+          s[sub][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i], qb[ct][i], s[sub][ct], 0, 0, 0);
       }
-      if (!FULL && 32 * pair + 16 >= valid_tokens)  // second sub-tile past the chunk's end: no weight
+    }
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) s[1][ct] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      // column maxima of the raw logits (the scale, > 0, is applied after)
+    for (int pair = 0; pair < 2; ++pair) {
+      const f32x4* s0 = s[2 * pair];
+      const f32x4* s1 = s[2 * pair + 1];
+      // column maxima of the pair's raw logits (the scale, > 0, is applied after)
       float mx[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const float a = fmaxf(fmaxf(fmaxf(s[0][ct][0], s[0][ct][1]), fmaxf(s[0][ct][2], s[0][ct][3])),
-                              fmaxf(fmaxf(s[1][ct][0], s[1][ct][1]), fmaxf(s[1][ct][2], s[1][ct][3])));
+        const float a = fmaxf(fmaxf(fmaxf(s0[ct][0], s0[ct][1]), fmaxf(s0[ct][2], s0[ct][3])),
+                              fmaxf(fmaxf(s1[ct][0], s1[ct][1]), fmaxf(s1[ct][2], s1[ct][3])));
         mx[ct] = max_xor32(max_xor16(a)) * p.scale_log2;
       }
       if (__ballot(mx[0] > m[0] + kRescaleSlack || mx[1] > m[1] + kRescaleSlack) != 0) {
@@ -224,8 +230,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
           m[ct] = mn;
         }
       }
-      // the P.V contraction takes the pair's weights in the order k = 8kg + j <->
-      // token 4kg + j of the first sub-tile (j < 4) or of the second
+      // weights as bf16 hi/lo operands; the P.V contraction takes them in the
+      // order k = 8kg + j <-> token 4kg + j of the pair's first sub-tile (j < 4)
+      // or of its second
       bf16x8 pb_hi[2], pb_lo[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
@@ -233,8 +240,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
         float pr[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pr[r] = fast_exp2(fmaf(s[0][ct][r], p.scale_log2, neg_m));
-          pr[4 + r] = fast_exp2(fmaf(s[1][ct][r], p.scale_log2, neg_m));
+          pr[r] = fast_exp2(fmaf(s0[ct][r], p.scale_log2, neg_m));
+          pr[4 + r] = fast_exp2(fmaf(s1[ct][r], p.scale_log2, neg_m));
         }
         lsum[ct] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
         uint32_t hw[4], lw[4];
@@ -248,7 +255,6 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       const unsigned char* v1 = &lds[buf][1][(sub1 / SUBB) * TILE + (sub1 % SUBB) * (HD * 32)];
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        // a missing second sub-tile's LDS rows hold finite re-read data; its weights are 0
         const int off = value_offset(16 * nt + n, kg);
         const uint2 a0 = *reinterpret_cast<const uint2*>(v0 + off);
         const uint2 a1 = *reinterpret_cast<const uint2*>(v1 + off);
@@ -262,19 +268,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     }
   };
 
-  stage_load(0);
-  stage_store(0);
+  stage_issue(0, 0);
+  lds_dma_wait_all();
   __syncthreads();
   for (int it = 0; it < iters; ++it) {
     const int buf = it & 1;
     const bool more = it + 1 < iters;
-    if (more) stage_load(it + 1);
-    if (wave_active) {
-      const int valid_tokens = min(TOK, (blk_hi - blk_lo - it * NB) * BS);
-      if (valid_tokens == TOK) compute(std::true_type{}, buf, TOK);
-      else compute(std::false_type{}, buf, valid_tokens);
-    }
-    if (more) stage_store(buf ^ 1);
+    if (more) stage_issue(it + 1, buf ^ 1);  // buffer buf^1 was released by the last barrier
+    if (wave_active) compute(buf);
+    lds_dma_wait_all();
     __syncthreads();
   }
 

@@ -17,19 +17,27 @@ constexpr int kProbeUnroll = 8;  // 16-byte loads in flight per thread
 // is stored so the loads cannot be dropped.
 __device__ __forceinline__ uint32_t fold(uint4 w) { return w.x ^ w.y ^ w.z ^ w.w; }
 
+// Each wave streams whole 8 KiB pieces (kProbeUnroll loads of 1 KiB each in
+// flight), pieces dealt to the waves of the grid round-robin.
 __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const uint4* __restrict__ src, int64_t chunks,
                                                                    uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
-  int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  constexpr int PIECE = 64 * kProbeUnroll;  // 16-byte chunks per wave piece
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (kProbeThreads / 64);
   uint32_t acc = 0;
-  for (; i + (kProbeUnroll - 1) * stride < chunks; i += kProbeUnroll * stride) {
-    uint4 w[kProbeUnroll];
+  for (int64_t piece = (int64_t)blockIdx.x * (kProbeThreads / 64) + (threadIdx.x >> 6); piece * PIECE < chunks;
+       piece += waves) {
+    const int64_t base = piece * PIECE + lane;
+    if (base + (kProbeUnroll - 1) * 64 < chunks) {
+      uint4 w[kProbeUnroll];
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) w[u] = src[i + u * stride];
+      for (int u = 0; u < kProbeUnroll; ++u) w[u] = src[base + u * 64];
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) acc ^= fold(w[u]);
+      for (int u = 0; u < kProbeUnroll; ++u) acc ^= fold(w[u]);
+    } else {
+      for (int64_t i = base; i < chunks; i += 64) acc ^= fold(src[i]);
+    }
   }
-  for (; i < chunks; i += stride) acc ^= fold(src[i]);
   __shared__ uint32_t red[kProbeThreads];
   red[threadIdx.x] = acc;
   __syncthreads();

@@ -40,6 +40,7 @@ class DecodeOpts(ctypes.Structure):
         ("partition_tokens", ctypes.c_int32),
         ("kernel", ctypes.c_int32),
         ("blocks_in_flight", ctypes.c_int32),
+        ("heads_per_workgroup", ctypes.c_int32),
         ("prefix_plan", ctypes.c_void_p),
         ("prefix_plan_dev", ctypes.c_void_p),
         ("prefix_plan_words", ctypes.c_size_t),
@@ -175,24 +176,24 @@ def plan_shared_prefix(block_tables, context_lens, block_size, min_group_seqs=4,
     return PrefixPlan(host, dev)
 
 
-def _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan):
+def _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup=0):
+    base = (int(partition_tokens), KERNELS[kernel], int(blocks_in_flight), int(heads_per_workgroup))
     if prefix_plan is None:
-        return DecodeOpts(int(partition_tokens), KERNELS[kernel], int(blocks_in_flight), None, None, 0)
-    return DecodeOpts(int(partition_tokens), KERNELS[kernel], int(blocks_in_flight), prefix_plan.host.ctypes.data,
-                      _ptr(prefix_plan.dev), prefix_plan.host.size)
+        return DecodeOpts(*base, None, None, 0)
+    return DecodeOpts(*base, prefix_plan.host.ctypes.data, _ptr(prefix_plan.dev), prefix_plan.host.size)
 
 
 def paged_attn_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, max_context_len, partition_tokens=0,
-                               kernel="auto", blocks_in_flight=0, prefix_plan=None) -> int:
+                               kernel="auto", blocks_in_flight=0, prefix_plan=None, heads_per_workgroup=0) -> int:
     desc = pool_desc(k_pool, v_pool)
-    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan)
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup)
     return int(lib.pkv_paged_attn_workspace_bytes(ctypes.byref(desc), num_seqs, num_heads, max_context_len,
                                                   ctypes.byref(opts)))
 
 
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, max_context_len=None,
                       workspace=None, partition_tokens=0, kernel="auto", out_dtype=None, stream=None,
-                      blocks_in_flight=0, prefix_plan=None):
+                      blocks_in_flight=0, prefix_plan=None, heads_per_workgroup=0):
     """``out[b, h] = softmax(scale * q[b, h] . K^T) . V`` over sequence b's
     paged keys/values.  ``q`` is ``[B, Hq, D]``; ``block_tables`` ``[B, max_blocks]``
     int32; ``context_lens`` ``[B]`` int32.  ``max_context_len`` is a host-side
@@ -213,7 +214,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=
         odt = q.dtype if out_dtype is None else out_dtype
         out = torch.empty((nseq, nh, hd), dtype=odt, device=q.device)
     odt_code = PKV_BF16 if out.dtype == torch.bfloat16 else PKV_F32
-    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan)
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup)
     need = int(lib.pkv_paged_attn_workspace_bytes(ctypes.byref(desc), nseq, nh, int(max_context_len),
                                                   ctypes.byref(opts)))
     if workspace is None and need > 0:

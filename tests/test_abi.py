@@ -124,6 +124,14 @@ def test_blocks_in_flight_range(ops):
     assert _decode(ops, d, opts=ops.DecodeOpts(0, 0, -1)) == 1
 
 
+def test_heads_per_workgroup_checks(ops):
+    mha = _desc(ops, num_kv_heads=32)
+    assert _decode(ops, mha, opts=ops.DecodeOpts(0, 0, 0, 3)) == 1                   # out of range
+    assert _decode(ops, _desc(ops), opts=ops.DecodeOpts(0, 0, 0, 2)) == 2            # group of 4
+    assert _decode(ops, _desc(ops, num_kv_heads=31), num_heads=31, opts=ops.DecodeOpts(0, 0, 0, 2)) == 2  # odd
+    assert _decode(ops, mha, opts=ops.DecodeOpts(0, 0, 2, 2)) == 2                   # two blocks in flight
+
+
 def test_probe_arguments_rejected_without_launch():
     lib = ctypes.CDLL(LIB)
     lib.pkv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
@@ -149,7 +157,7 @@ def test_prefix_plan_is_checked_before_launch(ops):
     words = plan.host
 
     def call(w, dev=16, desc=d, nwords=None):
-        opts = ops.DecodeOpts(0, 0, 0, w.ctypes.data, dev, w.size if nwords is None else nwords)
+        opts = ops.DecodeOpts(0, 0, 0, 0, w.ctypes.data, dev, w.size if nwords is None else nwords)
         return _decode(ops, desc, opts=opts, ws=16, ws_bytes=1 << 30)
 
     bad = words.copy()
@@ -167,7 +175,7 @@ def test_prefix_plan_is_checked_before_launch(ops):
     bad[6 + 2] = 3
     assert call(bad) == 1                                   # member with another prefix
     assert call(words, desc=_desc(ops, dtype=ops.PKV_F32)) == 2  # cascade needs bf16
-    opts = ops.DecodeOpts(0, 0, 0, words.ctypes.data, 16, words.size)
+    opts = ops.DecodeOpts(0, 0, 0, 0, words.ctypes.data, 16, words.size)
     ws = ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(opts))
     assert ws > 0  # the prefix partials live in the workspace
     assert _decode(ops, d, opts=opts, ws=16, ws_bytes=ws - 16) == 3

@@ -40,6 +40,12 @@ CASES = {
     # group 2, block 32, outlier keys in the suffixes
     "g2-bs32-outliers": lambda: generate("shared-prefix", num_seqs=10, shared_prefix=448, ctx=(20, 200),
                                          num_heads=4, num_kv_heads=2, block_size=32, outlier_fraction=0.05),
+    # prefixes that are not a whole number of 64-token pass iterations: the suffix
+    # pass also reads the last 1 (block 16) or 1 (block 32) prefix blocks
+    "g4-bs16-remainder": lambda: generate("shared-prefix", num_seqs=10, shared_prefix=336, ctx=(1, 50),
+                                          num_heads=8, num_kv_heads=2),
+    "g2-bs32-remainder": lambda: generate("shared-prefix", num_seqs=7, shared_prefix=480, ctx=(5, 60),
+                                          num_heads=4, num_kv_heads=2, block_size=32),
     # more rows than one 128-row tile (150 x 4 = 600 rows), a long prefix split into several chunks
     "g4-many-rows": lambda: generate("shared-prefix", num_seqs=150, shared_prefix=2048, ctx=(1, 40), num_heads=8,
                                      num_kv_heads=2),
@@ -110,6 +116,22 @@ def test_empty_suffix_merges_prefix_only():
     assert plan.prefix_blocks()[1] == wl.spec.shared_prefix // 16
     out = gw.decode(prefix_plan=plan, out_dtype=torch.float32, max_context_len=int(ctx.max()))
     check_attention(out_to_f64(out), ref, "bf16", "f32", "cascade/empty-suffix")
+
+
+def test_empty_suffix_with_prefix_remainder():
+    """Context ending exactly at a prefix of 21 blocks: the pass covers 20, the
+    suffix pass reads the 21st and nothing else."""
+    wl = CASES["g4-bs16-remainder"]()
+    _say("[cascade] empty suffix, prefix remainder")
+    gw = GpuWorkload(wl)
+    desc, kp, vp = oracle_pools(wl)
+    ctx = wl.context_lens.copy()
+    ctx[[0, 5]] = wl.spec.shared_prefix
+    ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, ctx, wl.scale)
+    gw.context_lens = torch.from_numpy(ctx).cuda()
+    plan = ops.plan_shared_prefix(wl.block_tables, ctx, 16, min_group_seqs=2, min_prefix_blocks=1)
+    out = gw.decode(prefix_plan=plan, out_dtype=torch.float32, max_context_len=int(ctx.max()))
+    check_attention(out_to_f64(out), ref, "bf16", "f32", "cascade/empty-suffix-remainder")
 
 
 def test_bad_prefix_block_gives_nan_rows_of_the_group_only():

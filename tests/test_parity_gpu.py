@@ -93,6 +93,19 @@ def test_small_decode(small_case, kernel, ptoks, out_dtype):
                     f"{name}/{kernel}/{ptoks}")
 
 
+def test_small_two_heads_per_workgroup(small_case):
+    """Vector kernel walking two kv heads per workgroup (one query head per kv head)."""
+    name, wl, gw, _, ref = small_case
+    if wl.spec.group != 1 or wl.spec.num_kv_heads % 2:
+        pytest.skip("needs one query head per kv head and an even kv-head count")
+    _say(f"[small] two heads per workgroup {name}")
+    for ptoks in (0, 48):
+        out = gw.decode(kernel="vector", partition_tokens=ptoks, blocks_in_flight=1, heads_per_workgroup=2,
+                        out_dtype=torch.float32 if wl.dtype == "bf16" else None)
+        torch.cuda.synchronize()
+        check_attention(out_to_f64(out), ref, wl.dtype, "f32", f"{name}/hpw2/{ptoks}")
+
+
 def test_small_deterministic(small_case):
     name, wl, gw, _, _ = small_case
     _say(f"[small] determinism {name}")
