@@ -194,6 +194,26 @@ pkv_status pkv_reshape_and_cache(const void* k, const void* v, int64_t k_token_s
 pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_dst_pairs, int32_t num_pairs,
                            const pkv_pool_desc* pool, void* stream);
 
+/*
+ * Block swap between two pools of the same shape: for every pair i, block
+ * src_dst_pairs[2i+1] of (dst_k, dst_v) becomes a bit copy of block
+ * src_dst_pairs[2i] of (src_k, src_v), all kv heads.  This moves blocks of
+ * preempted sequences to a CPU-side pool and back (the swap space that
+ * offloads KV-cache blocks to CPU memory: "PagedAttention Explained", section
+ * "Programmatic Control Over KV Cache", engine argument swap_space).
+ *
+ * The two descriptors must agree in kv heads, block size, head dim and dtype
+ * (their block counts may differ).  The four pool pointers and src_dst_pairs
+ * ([num_pairs][2] int32) must be addressable by the device: device memory, or
+ * host memory pinned with hipHostMalloc (torch pin_memory=True), which the
+ * kernel reads or writes across the bus.  Destination blocks must be distinct
+ * and, when both sides are the same pool, no destination may be a source.  A
+ * pair with an id outside its pool is skipped.
+ */
+pkv_status pkv_swap_blocks(const void* src_k, const void* src_v, const pkv_pool_desc* src_pool, void* dst_k,
+                           void* dst_v, const pkv_pool_desc* dst_pool, const int32_t* src_dst_pairs,
+                           int32_t num_pairs, void* stream);
+
 /* Static text for a status code. */
 const char* pkv_status_string(pkv_status status);
 

@@ -22,6 +22,8 @@ What it computes, and where the pages state it:
   ("Master Paged Attention for LLM Inference", krapton.com, section "How Paged
   Attention Works: The Mechanics", item 4; "PagedAttention Explained",
   section "Shared Prefix Caching").
+* ``swap_blocks`` -- whole blocks between two pools of the same shape (the CPU
+  swap space; "PagedAttention Explained", "Programmatic Control Over KV Cache").
 
 Every function here is pinned by ``tests/test_oracle.py`` to values that do not
 come from the oracle itself (closed forms, a library attention routine, brute
@@ -36,7 +38,7 @@ from .attention import (
     paged_decode_bruteforce,
     partitioned_decode,
 )
-from .cache_ops import reshape_and_cache, copy_blocks, new_pools
+from .cache_ops import reshape_and_cache, copy_blocks, new_pools, swap_blocks
 
 __all__ = [
     "PoolDesc",
@@ -51,4 +53,5 @@ __all__ = [
     "reshape_and_cache",
     "copy_blocks",
     "new_pools",
+    "swap_blocks",
 ]

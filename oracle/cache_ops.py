@@ -14,7 +14,12 @@ copy-on-write behaviour that lets several sequences start from shared KV state
 Mechanics", item 4; "PagedAttention Explained", "Shared Prefix Caching").
 Every destination block receives the contents its source held before the call.
 
-Both work on the flat raw-bit pools and write through the oracle's own layout
+``swap_blocks`` moves whole blocks between two pools of the same shape, the
+CPU swap space that holds blocks of preempted sequences ("PagedAttention
+Explained", section "Programmatic Control Over KV Cache", engine argument
+``swap_space``): destination block = bit copy of the source block.
+
+All work on the flat raw-bit pools and write through the oracle's own layout
 formulas (``oracle.layout``); results are compared bit for bit.
 """
 
@@ -78,3 +83,27 @@ def copy_blocks(k_pool, v_pool, desc: PoolDesc, pairs):
         snapshot = view[src].copy()
         view[dst] = snapshot
     return k_pool, v_pool
+
+
+def swap_blocks(src_k, src_v, src_desc: PoolDesc, dst_k, dst_v, dst_desc: PoolDesc, pairs):
+    """For every ``(src, dst)`` row of ``pairs``, block ``dst`` of the destination
+    pools becomes a bit copy of block ``src`` of the source pools (in place).
+    Both descriptors must agree in everything but the block count; destinations
+    must be distinct."""
+    shape = (src_desc.num_kv_heads, src_desc.block_size, src_desc.head_dim, src_desc.dtype)
+    if shape != (dst_desc.num_kv_heads, dst_desc.block_size, dst_desc.head_dim, dst_desc.dtype):
+        raise ValueError("pools differ in shape or dtype")
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    if pairs.size == 0:
+        return dst_k, dst_v
+    src, dst = pairs[:, 0], pairs[:, 1]
+    if src.min() < 0 or src.max() >= src_desc.num_blocks or dst.min() < 0 or dst.max() >= dst_desc.num_blocks:
+        raise ValueError("block id outside its pool")
+    if np.unique(dst).size != dst.size:
+        raise ValueError("destinations must be distinct")
+    per_block = src_desc.num_kv_heads * src_desc.block_size * src_desc.head_dim
+    for s_pool, d_pool in ((src_k, dst_k), (src_v, dst_v)):
+        s_view = s_pool.reshape(src_desc.num_blocks, per_block)
+        d_view = d_pool.reshape(dst_desc.num_blocks, per_block)
+        d_view[dst] = s_view[src]
+    return dst_k, dst_v

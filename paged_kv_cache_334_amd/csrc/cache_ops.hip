@@ -68,6 +68,34 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
     to[i] = from[i];
 }
 
+// Like copy_blocks_kernel between two pools (either may live in pinned host
+// memory): grid.x = pair, grid.y = slice of the block, grid.z = keys/values.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(const uint4* __restrict__ src_k,
+                                                          const uint4* __restrict__ src_v, int32_t src_blocks,
+                                                          uint4* __restrict__ dst_k, uint4* __restrict__ dst_v,
+                                                          int32_t dst_blocks, const int32_t* __restrict__ pairs,
+                                                          int64_t chunks_per_block) {
+  const int32_t src = pairs[2 * (int64_t)blockIdx.x];
+  const int32_t dst = pairs[2 * (int64_t)blockIdx.x + 1];
+  if ((unsigned)src >= (unsigned)src_blocks || (unsigned)dst >= (unsigned)dst_blocks) return;
+  const uint4* from = (blockIdx.z ? src_v : src_k) + src * chunks_per_block;
+  uint4* to = (blockIdx.z ? dst_v : dst_k) + dst * chunks_per_block;
+  for (int64_t i = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; i < chunks_per_block;
+       i += (int64_t)gridDim.y * blockDim.x)
+    to[i] = from[i];
+}
+
+hipError_t launch_swap_blocks(const void* src_k, const void* src_v, int32_t src_blocks, void* dst_k, void* dst_v,
+                              int32_t dst_blocks, const int32_t* pairs, int32_t num_pairs, int64_t block_bytes,
+                              hipStream_t s) {
+  if (num_pairs == 0) return hipSuccess;
+  const int64_t chunks = block_bytes / 16;
+  const unsigned gy = (unsigned)((chunks + 255) / 256 < 8 ? (chunks + 255) / 256 : 8);
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3((unsigned)num_pairs, gy, 2), dim3(256), 0, s, (const uint4*)src_k,
+                     (const uint4*)src_v, src_blocks, (uint4*)dst_k, (uint4*)dst_v, dst_blocks, pairs, chunks);
+  return hipGetLastError();
+}
+
 hipError_t launch_reshape_and_cache(const void* k, const void* v, int64_t k_stride, int64_t v_stride,
                                     const int32_t* slots, int32_t num_tokens, void* k_pool, void* v_pool,
                                     int32_t num_blocks, int32_t hkv, int32_t bs, int32_t hd, int32_t elt,

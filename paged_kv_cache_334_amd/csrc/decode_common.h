@@ -36,21 +36,24 @@ __device__ __forceinline__ SeqPick pick_sequence(const DecodeArgs& a, int* sm_ke
     p.start = covered_start<BS>(a, p.b);
     return p;
   }
+  // key = (length + 1) * 256 + 255 - index: distinct, larger for longer
+  // sequences and, among equal lengths, for smaller indices (a broken length
+  // counts as -1); rank = how many keys are larger.  The host enables this
+  // only for max_context < 2^23, so keys stay below 2^31.
   const int t = threadIdx.x;
   const int nb = a.num_seqs;
-  int raw = 0, key = 0;
+  int raw = 0;
+  uint32_t key = 0;
   if (t < nb) {
     raw = a.context_lens[t];
-    key = (raw < 0 || raw > a.max_context) ? -1 : raw;  // broken lengths rank last
-    sm_key[t] = key;
+    const int len = (raw < 0 || raw > a.max_context) ? -1 : raw;
+    key = (uint32_t)(len + 1) * 256u + (uint32_t)(255 - t);
+    sm_key[t] = (int)key;
   }
   __syncthreads();
   if (t < nb) {
     int rank = 0;
-    for (int o = 0; o < nb; ++o) {
-      const int ko = sm_key[o];
-      rank += (ko > key) | ((ko == key) & (o < t));
-    }
+    for (int o = 0; o < nb; ++o) rank += (uint32_t)sm_key[o] > key;
     if (rank == (int)blockIdx.z) {
       sm_pick[0] = t;
       sm_pick[1] = raw;

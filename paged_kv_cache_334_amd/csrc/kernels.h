@@ -103,6 +103,9 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, int64_t k_stri
                                     const int32_t* slots, int32_t num_tokens, void* k_pool, void* v_pool,
                                     int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
                                     int32_t elt_bytes, hipStream_t stream);
+hipError_t launch_swap_blocks(const void* src_k, const void* src_v, int32_t src_blocks, void* dst_k, void* dst_v,
+                              int32_t dst_blocks, const int32_t* pairs, int32_t num_pairs, int64_t block_bytes,
+                              hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t num_pairs,
                               int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
 

@@ -59,6 +59,8 @@ lib.pkv_reshape_and_cache.restype = _i32
 lib.pkv_reshape_and_cache.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp, ctypes.POINTER(PoolDesc), _vp]
 lib.pkv_copy_blocks.restype = _i32
 lib.pkv_copy_blocks.argtypes = [_vp, _vp, _vp, _i32, ctypes.POINTER(PoolDesc), _vp]
+lib.pkv_swap_blocks.restype = _i32
+lib.pkv_swap_blocks.argtypes = [_vp, _vp, ctypes.POINTER(PoolDesc), _vp, _vp, ctypes.POINTER(PoolDesc), _vp, _i32, _vp]
 lib.pkv_plan_shared_prefix.restype = _sz
 lib.pkv_plan_shared_prefix.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz]
 lib.pkv_status_string.restype = ctypes.c_char_p
@@ -255,6 +257,24 @@ def copy_blocks(k_pool, v_pool, src_dst_pairs, stream=None):
     st = lib.pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(src_dst_pairs) if p else None, p, ctypes.byref(desc),
                              _stream(stream))
     _check(st, "pkv_copy_blocks")
+
+
+def swap_blocks(src_k_pool, src_v_pool, dst_k_pool, dst_v_pool, src_dst_pairs, stream=None):
+    """Copy whole blocks from one pool to another of the same shape (e.g. a
+    device pool and a pool in pinned host memory): ``src_dst_pairs [P, 2]`` int32,
+    device or pinned host."""
+    src = pool_desc(src_k_pool, src_v_pool)
+    dst = pool_desc(dst_k_pool, dst_v_pool)
+    for t in (src_k_pool, src_v_pool, dst_k_pool, dst_v_pool, src_dst_pairs):
+        if not t.is_cuda and not t.is_pinned():
+            raise ValueError("host-side pools and pairs must be pinned (pin_memory=True) so the device can reach them")
+    if src_dst_pairs.dtype != torch.int32 or not src_dst_pairs.is_contiguous():
+        raise TypeError("src_dst_pairs must be contiguous int32")
+    p = src_dst_pairs.shape[0] if src_dst_pairs.numel() else 0
+    st = lib.pkv_swap_blocks(_ptr(src_k_pool), _ptr(src_v_pool), ctypes.byref(src), _ptr(dst_k_pool),
+                             _ptr(dst_v_pool), ctypes.byref(dst), _ptr(src_dst_pairs) if p else None, p,
+                             _stream(stream))
+    _check(st, "pkv_swap_blocks")
 
 
 # measurement kernels (include/pkv_probe.h)

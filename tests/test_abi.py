@@ -179,3 +179,13 @@ def test_prefix_plan_is_checked_before_launch(ops):
     ws = ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(opts))
     assert ws > 0  # the prefix partials live in the workspace
     assert _decode(ops, d, opts=opts, ws=16, ws_bytes=ws - 16) == 3
+
+
+def test_swap_arguments(ops):
+    d = _desc(ops)
+    p = ctypes.c_void_p(16)
+    other = _desc(ops, block_size=32)
+    assert ops.lib.pkv_swap_blocks(p, p, ctypes.byref(d), p, p, ctypes.byref(other), p, 2, None) == 1  # shapes
+    assert ops.lib.pkv_swap_blocks(p, p, ctypes.byref(d), p, p, ctypes.byref(d), p, -1, None) == 1
+    assert ops.lib.pkv_swap_blocks(p, None, ctypes.byref(d), p, p, ctypes.byref(d), p, 2, None) == 1
+    assert ops.lib.pkv_swap_blocks(p, p, ctypes.byref(d), p, p, ctypes.byref(d), p, 0, None) == 0

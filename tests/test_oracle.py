@@ -298,3 +298,38 @@ def test_cow_pairs_keep_source(prefix):
         b = owners[0]
         assert prefix.new_slots[b] // bs == dst and prefix.new_slots[b] % bs != 0
         assert src not in prefix.block_tables[b].tolist()
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_swap_blocks_round_trip(dtype):
+    """Swap out to a smaller pool and back: the touched blocks return bit for
+    bit, every other block of both pools is untouched (checked element by
+    element through the layout formulas, not through the oracle's views)."""
+    rng = np.random.default_rng(3)
+    dev = oracle.PoolDesc(9, 2, 16, 16, dtype)
+    host = oracle.PoolDesc(4, 2, 16, 16, dtype)
+    bits = np.uint16 if dtype == BF16 else np.uint32
+    dk = rng.integers(0, 1 << 15, dev.elems, dtype=np.int64).astype(bits)
+    dv = rng.integers(0, 1 << 15, dev.elems, dtype=np.int64).astype(bits)
+    hk, hv = oracle.new_pools(host)
+    before_dk, before_hk = dk.copy(), hk.copy()
+    oracle.swap_blocks(dk, dv, dev, hk, hv, host, [(7, 0), (2, 3)])
+    for d_blk, h_blk in ((7, 0), (2, 3)):
+        for h in range(2):
+            for t in range(16):
+                for d in range(16):
+                    assert hk[oracle.k_offset(host, h_blk, h, t, d)] == dk[oracle.k_offset(dev, d_blk, h, t, d)]
+                    assert hv[oracle.v_offset(host, h_blk, h, t, d)] == dv[oracle.v_offset(dev, d_blk, h, t, d)]
+    per = 2 * 16 * 16
+    untouched = [1, 2]
+    for b in untouched:
+        assert np.array_equal(hk[b * per:(b + 1) * per], before_hk[b * per:(b + 1) * per])
+    assert np.array_equal(dk, before_dk)
+    dk2, dv2 = oracle.new_pools(dev)
+    oracle.swap_blocks(hk, hv, host, dk2, dv2, dev, [(0, 7), (3, 2)])
+    assert np.array_equal(dk2.reshape(9, per)[[7, 2]], dk.reshape(9, per)[[7, 2]])
+    assert np.array_equal(dv2.reshape(9, per)[[7, 2]], dv.reshape(9, per)[[7, 2]])
+    with pytest.raises(ValueError):
+        oracle.swap_blocks(dk, dv, dev, hk, hv, oracle.PoolDesc(4, 2, 32, 16, dtype), [(0, 0)])
+    with pytest.raises(ValueError):
+        oracle.swap_blocks(dk, dv, dev, hk, hv, host, [(0, 1), (2, 1)])

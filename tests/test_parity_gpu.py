@@ -225,3 +225,44 @@ def test_full_decode_sampled(full_case, out_dtype):
     got = np.stack([out[b, h] for b, h in pairs])
     check_attention(got, ref, wl.dtype, "f32" if (odt is not None or wl.dtype == "f32") else "bf16",
                     f"{name}/full")
+
+
+def test_swap_blocks_gpu():
+    """Blocks out to a pool in pinned host memory and back, and between two
+    device pools: bit-exact against the oracle's swap."""
+    wl = SMALL["gqa-small"]()
+    _say("[swap] build")
+    gw = GpuWorkload(wl)
+    s = wl.spec
+    desc_dev = oracle.PoolDesc(wl.num_blocks, s.num_kv_heads, s.block_size, s.head_dim, s.dtype)
+    desc_host = oracle.PoolDesc(12, s.num_kv_heads, s.block_size, s.head_dim, s.dtype)
+    dev_k, dev_v = to_bits(gw.k_pool), to_bits(gw.v_pool)
+    # pinned host pool, filled with NaN bits like a fresh pool
+    hk = torch.empty((12,) + tuple(gw.k_pool.shape[1:]), dtype=gw.k_pool.dtype, pin_memory=True)
+    hv = torch.empty((12,) + tuple(gw.v_pool.shape[1:]), dtype=gw.v_pool.dtype, pin_memory=True)
+    hk.view(torch.int16).fill_(0x7FC0)
+    hv.view(torch.int16).fill_(0x7FC0)
+    used = sorted({int(x) for x in wl.block_tables[:, 0]})[:5]
+    out_pairs = np.array([(b, i * 2) for i, b in enumerate(used)], dtype=np.int32)
+    _say("[swap] device -> pinned host")
+    ops.swap_blocks(gw.k_pool, gw.v_pool, hk, hv, torch.from_numpy(out_pairs).cuda())
+    torch.cuda.synchronize()
+    ref_hk, ref_hv = oracle.new_pools(desc_host)
+    oracle.swap_blocks(dev_k, dev_v, desc_dev, ref_hk, ref_hv, desc_host, out_pairs)
+    assert np.array_equal(to_bits(hk), ref_hk) and np.array_equal(to_bits(hv), ref_hv)
+    _say("[swap] pinned host -> device (other blocks)")
+    back = np.array([(i * 2, wl.num_blocks - 1 - i) for i in range(len(used))], dtype=np.int32)
+    pairs_host = torch.from_numpy(back).pin_memory()
+    ops.swap_blocks(hk, hv, gw.k_pool, gw.v_pool, pairs_host)
+    torch.cuda.synchronize()
+    oracle.swap_blocks(ref_hk, ref_hv, desc_host, dev_k, dev_v, desc_dev, back)
+    assert np.array_equal(to_bits(gw.k_pool), dev_k) and np.array_equal(to_bits(gw.v_pool), dev_v)
+    _say("[swap] device -> device, pair outside the pool skipped")
+    k2, v2 = ops.new_pools(4, s.num_kv_heads, s.block_size, s.head_dim, gw.k_pool.dtype, "cuda", fill=0x7FC0)
+    pairs = np.array([(used[0], 1), (wl.num_blocks + 3, 2)], dtype=np.int32)
+    ops.swap_blocks(gw.k_pool, gw.v_pool, k2, v2, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    rk, rv = oracle.new_pools(oracle.PoolDesc(4, s.num_kv_heads, s.block_size, s.head_dim, s.dtype))
+    oracle.swap_blocks(dev_k, dev_v, desc_dev, rk, rv, oracle.PoolDesc(4, s.num_kv_heads, s.block_size,
+                                                                          s.head_dim, s.dtype), pairs[:1])
+    assert np.array_equal(to_bits(k2), rk) and np.array_equal(to_bits(v2), rv)
