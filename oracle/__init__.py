@@ -14,6 +14,9 @@ What it computes, and where the pages state it:
   sections "Block Tables and Non-Contiguous Storage" and "Implementing a
   Simplified Paged KV Cache", method ``get_keys_values``), then plain two-pass
   softmax attention in float64.
+* ``paged_attend_causal`` -- several new tokens per sequence, each attending
+  causally over the cached prefix up to itself (speculative verify, a prompt
+  chunk); the same single-query attention over each token's visible prefix.
 * ``partitioned_decode`` -- the same result reached through per-partition
   (max, sum, acc) partials and a max-rescaled merge (the split-K form).
 * ``reshape_and_cache`` / ``copy_blocks`` -- the cache write of the newest
@@ -37,6 +40,7 @@ from .attention import (
     paged_decode,
     paged_decode_bruteforce,
     partitioned_decode,
+    paged_attend_causal,
 )
 from .cache_ops import reshape_and_cache, copy_blocks, new_pools, swap_blocks
 
@@ -50,6 +54,7 @@ __all__ = [
     "paged_decode",
     "paged_decode_bruteforce",
     "partitioned_decode",
+    "paged_attend_causal",
     "reshape_and_cache",
     "copy_blocks",
     "new_pools",

@@ -183,3 +183,51 @@ def partitioned_decode(q_bits, k_pool, v_pool, desc: PoolDesc, block_tables, con
             f = np.exp(ms - big_m)
             out[b, heads] = (f[:, :, None] * accs).sum(axis=0) / (f * ls).sum(axis=0)[:, None]
     return out
+
+
+def paged_attend_causal(q_bits, k_pool, v_pool, desc: PoolDesc, block_tables, context_lens, query_start,
+                        scale: float):
+    """Attention of several new tokens per sequence (a verify step of
+    speculative decoding, a chunk of a prompt) over the paged cache, causal
+    among the new tokens.
+
+    Sequence ``b`` holds ``context_lens[b]`` tokens, the last
+    ``n_b = query_start[b+1] - query_start[b]`` of them written this step; row
+    ``query_start[b] + i`` of ``q_bits [T, Hq, D]`` is the query of new token
+    ``i``, which sits at position ``context_lens[b] - n_b + i`` and attends to
+    the tokens at positions ``0 .. context_lens[b] - n_b + i`` (itself and
+    everything before it, nothing after).  Returns float64 ``out [T, Hq, D]``.
+
+    The pages name speculative decoding and forked sequences as users of the
+    shared paged cache ("Master Paged Attention for LLM Inference", "How Paged
+    Attention Works: The Mechanics", item 4; "What is PagedAttention",
+    "PagedAttention vs Speculative Decoding") and a prompt's prefill that
+    fills it ("PagedAttention Explained", "Enabling Automatic Prefix
+    Caching"), but give no formula: the reading here is the standard causal
+    mask of a decoder, each new token seeing the prefix up to itself.  Each
+    row is computed as the single-query attention above over its visible
+    prefix.
+    """
+    q = decode_bits(np.asarray(q_bits), desc.dtype)
+    total, num_heads, hd = q.shape
+    g = _check_heads(num_heads, desc)
+    starts = np.asarray(query_start, dtype=np.int64)
+    nseq = len(starts) - 1
+    if starts[0] < 0 or starts[-1] > total or (np.diff(starts) < 0).any():
+        raise ValueError("query_start must be non-decreasing within [0, T]")
+    out = np.zeros((total, num_heads, hd), dtype=np.float64)
+    for b in range(nseq):
+        first, n_new = int(starts[b]), int(starts[b + 1] - starts[b])
+        ctx = int(context_lens[b])
+        if n_new == 0:
+            continue
+        if n_new > ctx:
+            raise ValueError(f"sequence {b}: more new tokens than context")
+        for kvh in range(desc.num_kv_heads):
+            keys, values = resolve_sequence(k_pool, v_pool, desc, block_tables[b], ctx, kvh)
+            heads = np.arange(kvh * g, (kvh + 1) * g)
+            for i in range(n_new):
+                visible = ctx - n_new + i + 1
+                o, _ = _attend(q[first + i, heads], keys[:visible], values[:visible], scale)
+                out[first + i, heads] = o
+    return out

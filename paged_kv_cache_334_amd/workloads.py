@@ -39,7 +39,7 @@ F32 = "f32"
 _ELT = {BF16: 2, F32: 4}
 
 # purposes of the random streams
-_CTX, _PERM, _Q, _K, _V, _OUTLIER, _COW = 1, 2, 3, 4, 5, 6, 7
+_CTX, _PERM, _Q, _K, _V, _OUTLIER, _COW, _QLEN = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 class CacheExhausted(RuntimeError):
@@ -138,6 +138,10 @@ class WorkloadSpec:
     num_blocks: Optional[int] = None  # fixed pool size instead of pool_factor
     scale: Optional[float] = None  # default 1/sqrt(head_dim)
     seed: int = 0
+    # new tokens per sequence in the step (their keys/values are written, then
+    # each attends causally): an int, or (lo, hi) inclusive uniform; at most
+    # the context length
+    query_len: Union[int, Tuple[int, int]] = 1
 
     @property
     def group(self) -> int:
@@ -171,11 +175,21 @@ class Workload:
     init_k: np.ndarray  # [T0, Hkv, D] bits of every token written before the step
     init_v: np.ndarray
     init_slots: np.ndarray  # [T0] int32
-    new_k: np.ndarray  # [B, Hkv, D] bits of each sequence's newest token
+    new_k: np.ndarray  # [T, Hkv, D] bits of the step's new tokens (T = B with one per sequence)
     new_v: np.ndarray
-    new_slots: np.ndarray  # [B] int32
+    new_slots: np.ndarray  # [T] int32
     cow_pairs: np.ndarray  # [P, 2] int32 (src, dst) copied before the new tokens are written
     outlier_positions: dict = field(default_factory=dict)
+    # new tokens of sequence b: rows query_start[b] .. query_start[b+1]-1 of q and new_k/new_v
+    query_start: Optional[np.ndarray] = None
+
+    @property
+    def query_lens(self) -> np.ndarray:
+        return np.diff(self.query_start).astype(np.int32)
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max()) if len(self.query_lens) else 0
 
     @property
     def dtype(self) -> str:
@@ -242,6 +256,16 @@ def context_lengths(spec: WorkloadSpec) -> np.ndarray:
     return ctx + np.where(shared, spec.shared_prefix, 0)
 
 
+def query_lengths(spec: WorkloadSpec, ctx: np.ndarray) -> np.ndarray:
+    """New tokens per sequence this step (at least 1, at most the context)."""
+    if isinstance(spec.query_len, int):
+        qlen = np.full(spec.num_seqs, spec.query_len, dtype=np.int64)
+    else:
+        lo, hi = spec.query_len
+        qlen = np.random.default_rng([spec.seed, _QLEN]).integers(lo, hi, size=spec.num_seqs, endpoint=True)
+    return np.minimum(np.maximum(qlen, 1), ctx).astype(np.int64)
+
+
 def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overrides) -> Workload:
     """Build a workload: context lengths, block tables, the bits of every
     cached token, the step's new tokens, copy-on-write pairs and queries.
@@ -261,12 +285,17 @@ def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overri
 
     rng = lambda purpose: np.random.default_rng([spec.seed, purpose])  # noqa: E731
     ctx = context_lengths(spec)
+    qlen = query_lengths(spec, ctx)
+    # new tokens never reach back into a shared prefix
+    own_ctx = ctx - np.array([spec.shared_prefix if prefix_group_of(spec, b) >= 0 else 0 for b in range(nseq)])
+    qlen = np.minimum(qlen, np.maximum(own_ctx, 1))
+    query_start = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
 
-    # copy-on-write choice: sequences whose newest token lands inside a block
+    # copy-on-write choice: sequences whose first new token lands inside a block
     # that already holds rows, i.e. the block they would share with a sibling
     cow_seqs = []
     if spec.cow_fraction > 0:
-        candidates = np.nonzero(((ctx - 1) % bs) != 0)[0]
+        candidates = np.nonzero(((ctx - qlen) % bs) != 0)[0]
         k = int(round(spec.cow_fraction * nseq))
         cow_seqs = sorted(rng(_COW).choice(candidates, size=min(k, len(candidates)), replace=False).tolist())
 
@@ -296,15 +325,15 @@ def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overri
         else:
             mgr.allocate_sequence(b)
         first = spec.shared_prefix if gi >= 0 else 0
-        for pos in range(first, int(ctx[b]) - 1):
+        for pos in range(first, int(ctx[b] - qlen[b])):
             init_slots.append(mgr.append_slot(b))
             init_owner.append((b, pos))
     for gi in range(groups):
         mgr.free_sequence(("prefix", gi))
     for b in cow_seqs:  # an implicit sibling keeps referencing every block of b
         mgr.fork(b, ("sibling", b))
-    # the step: one new token per sequence (copy-on-write happens here)
-    new_slots = [mgr.append_slot(b) for b in range(nseq)]
+    # the step: each sequence's new tokens (copy-on-write happens at the first)
+    new_slots = [mgr.append_slot(b) for b in range(nseq) for _ in range(int(qlen[b]))]
     cow_pairs = np.asarray(mgr.take_copies(), dtype=np.int32).reshape(-1, 2)
 
     # block tables as the decode sees them
@@ -321,7 +350,7 @@ def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overri
 
     # token values, in the token order above, the new tokens last
     hkv, hd = spec.num_kv_heads, spec.head_dim
-    total = len(init_slots) + nseq
+    total = len(init_slots) + len(new_slots)
     key_scale = None
     outliers = {}
     if spec.outlier_fraction > 0:
@@ -331,7 +360,8 @@ def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overri
         for i, (b, pos) in enumerate(init_owner):
             index_of[(b, pos)] = i
         for b in range(nseq):
-            index_of[(b, int(ctx[b]) - 1)] = len(init_slots) + b
+            for i in range(int(qlen[b])):
+                index_of[(b, int(ctx[b] - qlen[b]) + i)] = len(init_slots) + int(query_start[b]) + i
         for b in range(nseq):
             first = spec.shared_prefix if prefix_group_of(spec, b) >= 0 else 0
             n_out = int(np.floor(spec.outlier_fraction * (int(ctx[b]) - first)))
@@ -341,7 +371,7 @@ def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overri
                 key_scale[index_of[(b, p)]] = spec.outlier_scale
     keys = _normal_bits(rng(_K), (total, hkv, hd), spec.dtype, scale_rows=key_scale)
     values = _normal_bits(rng(_V), (total, hkv, hd), spec.dtype)
-    q = _normal_bits(rng(_Q), (nseq, spec.num_heads, hd), spec.dtype)
+    q = _normal_bits(rng(_Q), (len(new_slots), spec.num_heads, hd), spec.dtype)
     t0 = len(init_slots)
     return Workload(
         spec=spec,
@@ -359,4 +389,5 @@ def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overri
         new_slots=np.asarray(new_slots, dtype=np.int32),
         cow_pairs=cow_pairs,
         outlier_positions=outliers,
+        query_start=query_start,
     )

@@ -84,3 +84,25 @@ def oracle_pools(wl, fill=None):
 def oracle_decode(wl, pools=None, **kw):
     desc, k_pool, v_pool = oracle_pools(wl) if pools is None else pools
     return oracle.paged_decode(wl.q, k_pool, v_pool, desc, wl.block_tables, wl.context_lens, wl.scale, **kw)
+
+
+def oracle_causal(wl, pools=None):
+    """The oracle's multi-token (causal) attention over the step's pools."""
+    desc, k_pool, v_pool = oracle_pools(wl) if pools is None else pools
+    return oracle.paged_attend_causal(wl.q, k_pool, v_pool, desc, wl.block_tables, wl.context_lens,
+                                      wl.query_start, wl.scale)
+
+
+def sdpa_causal_prompt(wl, b, smap=None):
+    """``out [n, Hq, D]`` of a sequence whose every token is new this step (a
+    whole prompt as one chunk), from torch's attention with its own causal
+    mask (``is_causal``: row i sees keys 0..i) on contiguous keys/values."""
+    g = wl.spec.group
+    first, last = int(wl.query_start[b]), int(wl.query_start[b + 1])
+    assert last - first == int(wl.context_lens[b])
+    k_bits, v_bits = contiguous_kv(wl, b, smap)
+    q = torch.from_numpy(to_f64(wl.q[first:last], wl.dtype)).permute(1, 0, 2)[None]  # [1, Hq, n, D]
+    k = torch.from_numpy(to_f64(k_bits, wl.dtype)).permute(1, 0, 2).repeat_interleave(g, dim=0)[None]
+    v = torch.from_numpy(to_f64(v_bits, wl.dtype)).permute(1, 0, 2).repeat_interleave(g, dim=0)[None]
+    out = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=wl.scale)
+    return out[0].permute(1, 0, 2).numpy()

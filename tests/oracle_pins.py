@@ -15,7 +15,10 @@ Sources of the pinned facts:
   ("PagedAttention Explained", "Block Tables and Non-Contiguous Storage");
   shared-prefix sequences reference the same physical blocks ("PagedAttention
   Explained", "Shared Prefix Caching");
-* brute force with Python scalars on tiny inputs.
+* brute force with Python scalars on tiny inputs;
+* for several new tokens per step: token-by-token decoding (the result a
+  verify pass must reproduce), torch's own causal mask when a whole prompt is
+  one chunk, and that no row depends on the tokens after it.
 """
 
 import numpy as np
@@ -24,8 +27,10 @@ import oracle
 from logical_model import (
     contiguous_kv,
     desc_of,
+    oracle_causal,
     oracle_decode,
     oracle_pools,
+    sdpa_causal_prompt,
     sdpa_reference,
     slot_map,
     to_f64,
@@ -263,3 +268,60 @@ def pin_copy_blocks(desc, pairs, seed=0):
             assert np.array_equal(k_pool[sl], k0[ssl]) and np.array_equal(v_pool[sl], v0[ssl])
         else:
             assert np.array_equal(k_pool[sl], k0[sl]) and np.array_equal(v_pool[sl], v0[sl])
+
+
+# ---- several new tokens per step (causal) -------------------------------------------
+
+def pin_causal_one_token_is_decode(wl):
+    """With one new token per sequence the causal form is the decode itself."""
+    assert (wl.query_lens == 1).all()
+    pools = oracle_pools(wl)
+    assert np.array_equal(oracle_causal(wl, pools), oracle_decode(wl, pools))
+
+
+def pin_causal_is_sequential_decode(wl):
+    """New token i of sequence b gets what a decode step computes for the same
+    sequence with its cache ending at that token (context_len cut to the
+    token's position + 1): a verify pass over draft tokens must reproduce
+    token-by-token decoding."""
+    pools = oracle_pools(wl)
+    desc, k_pool, v_pool = pools
+    out = oracle_causal(wl, pools)
+    for b in range(wl.spec.num_seqs):
+        first, last = int(wl.query_start[b]), int(wl.query_start[b + 1])
+        n, ctx = last - first, int(wl.context_lens[b])
+        for i in range(n):
+            cut = np.array([ctx - n + i + 1], dtype=np.int32)
+            one = oracle.paged_decode(wl.q[first + i][None], k_pool, v_pool, desc, wl.block_tables[b][None], cut,
+                                      wl.scale)
+            assert np.array_equal(out[first + i], one[0]), f"seq {b} token {i}"
+
+
+def pin_causal_whole_prompt(wl, atol=1e-12):
+    """Sequences whose every token is new: torch's attention with its own
+    causal mask on the contiguous keys/values."""
+    out = oracle_causal(wl)
+    smap = slot_map(wl)
+    whole = [b for b in range(wl.spec.num_seqs) if wl.query_lens[b] == wl.context_lens[b]]
+    assert whole, "no whole-prompt sequence in the workload"
+    for b in whole:
+        ref = sdpa_causal_prompt(wl, b, smap)
+        got = out[wl.query_start[b]:wl.query_start[b + 1]]
+        err = np.abs(got - ref).max()
+        assert err <= atol, f"seq {b}: max abs {err}"
+
+
+def pin_causal_future_invariance(wl, seed=0):
+    """Changing the key and value of each sequence's last new token changes
+    only that token's rows: nothing before a token sees it."""
+    rng = np.random.default_rng(seed)
+    last = wl.query_start[1:] - 1
+    new_k, new_v = wl.new_k.copy(), wl.new_v.copy()
+    new_k[last] = rng.permutation(new_k[last].reshape(-1)).reshape(new_k[last].shape) ^ new_k.dtype.type(1 << 3)
+    new_v[last] = new_v[last] ^ new_v.dtype.type(1 << 4)
+    other = Workload(**{**wl.__dict__, "new_k": new_k, "new_v": new_v})
+    a, b_out = oracle_causal(wl), oracle_causal(other)
+    before = np.ones(len(a), dtype=bool)
+    before[last] = False
+    assert np.array_equal(a[before], b_out[before]), "a row saw a later token"
+    assert not np.array_equal(a[last], b_out[last]), "the last token did not see itself"

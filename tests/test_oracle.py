@@ -333,3 +333,65 @@ def test_swap_blocks_round_trip(dtype):
         oracle.swap_blocks(dk, dv, dev, hk, hv, oracle.PoolDesc(4, 2, 32, 16, dtype), [(0, 0)])
     with pytest.raises(ValueError):
         oracle.swap_blocks(dk, dv, dev, hk, hv, host, [(0, 1), (2, 1)])
+
+
+# ---- several new tokens per step (causal) -------------------------------------------
+
+@pytest.fixture(scope="module")
+def causal_gqa():
+    return small("gqa-70b", num_seqs=4, ctx=(1, 70), num_heads=8, num_kv_heads=2, head_dim=64, query_len=(1, 9))
+
+
+@pytest.fixture(scope="module")
+def causal_prompt():
+    # query_len above every context: each sequence is one whole prompt chunk
+    return small("mha-7b", num_seqs=3, ctx=(1, 40), num_heads=4, num_kv_heads=2, head_dim=32, query_len=64)
+
+
+@pytest.fixture(scope="module")
+def causal_prefix():
+    return small("shared-prefix", num_seqs=6, shared_prefix=32, ctx=(2, 40), num_heads=4, num_kv_heads=2,
+                 head_dim=16, cow_fraction=0.34, query_len=(1, 6))
+
+
+def test_causal_workload_shapes(causal_gqa, causal_prefix):
+    for wl in (causal_gqa, causal_prefix):
+        n = wl.query_lens
+        assert (n >= 1).all() and (n <= wl.context_lens).all()
+        assert len(wl.q) == len(wl.new_slots) == int(wl.query_start[-1])
+        assert n.max() > 1
+    # copy-on-write still happens at the first new token of a forked sequence
+    assert len(causal_prefix.cow_pairs) > 0
+
+
+def test_causal_one_token_is_decode(gqa, prefix):
+    pins.pin_causal_one_token_is_decode(gqa)
+    pins.pin_causal_one_token_is_decode(prefix)
+
+
+@pytest.mark.parametrize("name", ["causal_gqa", "causal_prefix", "causal_prompt"])
+def test_causal_is_sequential_decode(name, request):
+    pins.pin_causal_is_sequential_decode(request.getfixturevalue(name))
+
+
+def test_causal_whole_prompt(causal_prompt):
+    pins.pin_causal_whole_prompt(causal_prompt)
+
+
+def test_causal_whole_prompt_f32():
+    wl = small("tiny-f32", num_seqs=2, ctx=(7, 21), query_len=64, num_blocks=8)
+    pins.pin_causal_whole_prompt(wl, atol=1e-13)
+
+
+@pytest.mark.parametrize("name", ["causal_gqa", "causal_prefix"])
+def test_causal_future_invariance(name, request):
+    pins.pin_causal_future_invariance(request.getfixturevalue(name))
+
+
+def test_causal_rejects_bad_query_start(causal_gqa):
+    desc, k_pool, v_pool = oracle_pools(causal_gqa)
+    bad = causal_gqa.query_start.copy()
+    bad[1], bad[2] = bad[2], bad[1]
+    with pytest.raises(ValueError):
+        oracle.paged_attend_causal(causal_gqa.q, k_pool, v_pool, desc, causal_gqa.block_tables,
+                                   causal_gqa.context_lens, bad, causal_gqa.scale)

@@ -20,6 +20,10 @@ def wls():
         "gqa": small("gqa-70b", num_seqs=3, ctx=(1, 70), num_heads=8, num_kv_heads=2, head_dim=64),
         "prefix": small("shared-prefix", num_seqs=6, shared_prefix=32, ctx=(2, 40), num_heads=4,
                         num_kv_heads=2, head_dim=16, cow_fraction=0.34),
+        "causal": small("gqa-70b", num_seqs=3, ctx=(1, 40), num_heads=4, num_kv_heads=2, head_dim=16,
+                        query_len=(2, 6)),
+        "prompt": small("mha-7b", num_seqs=2, ctx=(3, 20), num_heads=2, num_kv_heads=2, head_dim=16,
+                        query_len=64),
     }
 
 
@@ -43,6 +47,9 @@ def all_pins(w):
         lambda: pins.pin_partitions(w["gqa"], sizes=[7, 16]),
         lambda: pins.pin_layout_bruteforce(oracle.PoolDesc(4, 2, 16, 16, "bf16")),
         lambda: pins.pin_copy_blocks(oracle.PoolDesc(6, 2, 16, 16, "bf16"), [(1, 4), (0, 2)]),
+        lambda: pins.pin_causal_is_sequential_decode(w["causal"]),
+        lambda: pins.pin_causal_whole_prompt(w["prompt"]),
+        lambda: pins.pin_causal_future_invariance(w["causal"]),
     ]
 
 
@@ -133,6 +140,25 @@ def _partitioned_no_rescale(q_bits, k_pool, v_pool, desc, tables, ctx, scale, to
     return out
 
 
+def _causal_variant(visible_of, row_of=lambda first, n, i: first + i):
+    """The causal oracle with its visible-prefix length or its query row replaced."""
+    def fn(q_bits, k_pool, v_pool, desc, tables, ctx, query_start, scale):
+        q = olay.decode_bits(np.asarray(q_bits), desc.dtype)
+        g = q.shape[1] // desc.num_kv_heads
+        out = np.zeros(q.shape, dtype=np.float64)
+        for b in range(len(query_start) - 1):
+            first, n, c = int(query_start[b]), int(query_start[b + 1] - query_start[b]), int(ctx[b])
+            for kvh in range(desc.num_kv_heads):
+                keys, values = opd.resolve_sequence(k_pool, v_pool, desc, tables[b], c, kvh)
+                heads = np.arange(kvh * g, (kvh + 1) * g)
+                for i in range(n):
+                    vis = max(1, min(c, visible_of(c, n, i)))
+                    o, _ = opd._attend(q[row_of(first, n, i), heads], keys[:vis], values[:vis], scale)
+                    out[first + i, heads] = o
+        return out
+    return fn
+
+
 MUTATIONS = {
     "softmax without max shift": [(opd, "_attend", _attend_no_shift)],
     "softmax without normalisation": [(opd, "_attend", _attend_no_normalise)],
@@ -148,6 +174,12 @@ MUTATIONS = {
                                 (oco, "reshape_and_cache", _write_next_row)],
     "block copy reversed": [(oracle, "copy_blocks", _copy_reversed), (oco, "copy_blocks", _copy_reversed)],
     "partials merged without rescale": [(oracle, "partitioned_decode", _partitioned_no_rescale)],
+    "causal: token does not see itself": [(oracle, "paged_attend_causal", _causal_variant(lambda c, n, i: c - n + i))],
+    "causal: one token past itself": [(oracle, "paged_attend_causal", _causal_variant(lambda c, n, i: c - n + i + 2))],
+    "causal: no mask among new tokens": [(oracle, "paged_attend_causal", _causal_variant(lambda c, n, i: c))],
+    "causal: mask from the sequence start": [(oracle, "paged_attend_causal", _causal_variant(lambda c, n, i: i + 1))],
+    "causal: query rows reversed": [(oracle, "paged_attend_causal",
+                                     _causal_variant(lambda c, n, i: c - n + i + 1, lambda f, n, i: f + n - 1 - i))],
 }
 
 
