@@ -163,6 +163,8 @@ size_t pkv_paged_attn_workspace_bytes(const pkv_pool_desc* pool, int32_t num_seq
  *  out           [num_seqs][num_heads][head_dim] out_dtype; must not alias inputs
  *  workspace     device scratch of at least pkv_paged_attn_workspace_bytes(); may be
  *                NULL when that is 0.  Not aliased by other in-flight calls.
+ *  scale         finite and >= 0 (the kernels take the maximum of the unscaled
+ *                logits); negative values return PKV_EINVAL.
  */
 pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                                  const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
@@ -171,6 +173,49 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
                                  void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts,
                                  void* stream);
 
+/* Bytes of workspace pkv_paged_attn_multi_token needs (0 for a single pass). */
+size_t pkv_paged_attn_multi_token_workspace_bytes(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_heads,
+                                                  int32_t num_query_tokens, int32_t max_query_len,
+                                                  int32_t max_context_len, const pkv_decode_opts* opts);
+/*
+ * Paged attention for several new tokens per sequence, causal among them: the
+ * verify step of speculative decoding, or a chunk of a prompt, over the paged
+ * cache (the pages name speculative decoding and forked sequences as users of
+ * the shared blocks: "Master Paged Attention for LLM Inference", "How Paged
+ * Attention Works: The Mechanics", item 4; "What is PagedAttention",
+ * "PagedAttention vs Speculative Decoding"; and a prompt's prefill filling
+ * the cache: "PagedAttention Explained", "Enabling Automatic Prefix
+ * Caching").  The pages give no formula; the mask is the standard causal one.
+ *
+ * Sequence b has n_b = query_start[b+1] - query_start[b] new tokens, already
+ * written to the cache (pkv_reshape_and_cache) as its last n_b of
+ * context_lens[b] tokens.  New token i, at position context_lens[b] - n_b + i,
+ * has query row r = query_start[b] + i and gets, for every query head h,
+ *     out[r][h][:] = sum_t softmax_t(scale * <q[r][h], k_t>) * v_t
+ * over the tokens t <= context_lens[b] - n_b + i (itself and everything
+ * before it).  One new token per sequence is the decode step.  Arithmetic as
+ * in pkv_paged_attn_decode.
+ *
+ *  q              [num_query_tokens][num_heads][head_dim], pool->dtype
+ *  query_start    [num_seqs + 1] int32, device; non-decreasing, within [0, num_query_tokens]
+ *  max_query_len  host bound of n_b (the grid covers that many tokens per sequence)
+ *  out            [num_query_tokens][num_heads][head_dim] out_dtype
+ *  opts           partition_tokens, kernel (the matrix-core kernel takes bf16,
+ *                 head_dim 128 and 1, 2, 4 or 8 query heads per kv head) and
+ *                 blocks_in_flight; no shared-prefix plan, one kv head per workgroup
+ * Other arguments as in pkv_paged_attn_decode.  Device-side preconditions:
+ * n_b <= context_lens[b] <= max_context_len and n_b <= max_query_len; a
+ * sequence breaking them gets NaN in the rows the grid covers.  A sequence
+ * whose query_start entries are out of order or out of range gets nothing
+ * written.
+ */
+pkv_status pkv_paged_attn_multi_token(const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      const int32_t* query_start, int32_t num_seqs, int32_t num_heads,
+                                      int32_t num_query_tokens, int32_t max_query_len, int32_t max_blocks_per_seq,
+                                      int32_t max_context_len, const pkv_pool_desc* pool, float scale,
+                                      int32_t out_dtype, void* out, void* workspace, size_t workspace_bytes,
+                                      const pkv_decode_opts* opts, void* stream);
 /*
  * Cache write: for every token i < num_tokens with slot s = slot_mapping[i] >= 0,
  * copy the bits of k[i][h][:] / v[i][h][:] (all kv heads h) to row s % block_size

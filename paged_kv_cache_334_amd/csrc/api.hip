@@ -46,6 +46,21 @@ pkv_status check_pool(const pkv_pool_desc* pool) {
 // sequences: 256 partitions of 8192 tokens stream faster than 512 of 4096.
 constexpr int64_t kTargetWorkgroups = 256;
 
+// Automatic split-K partition length in blocks.  One pass per work unit
+// (sequence or row tile, kv head) when that already gives kTargetWorkgroups
+// workgroups: a split costs a second kernel, the partials' traffic and a
+// prologue/epilogue per workgroup, and measured slower than a single long walk
+// whenever the GPU is already full.  Fewer units (long contexts, small
+// batches) are split into equal partitions until about kTargetWorkgroups
+// exist, each wave keeping at least two rounds of in-flight blocks.
+int64_t auto_blocks_per_part(int64_t units, int64_t max_blocks, int64_t round) {
+  if (units >= kTargetWorkgroups || max_blocks <= 2 * round || units == 0) return max_blocks > 0 ? max_blocks : 1;
+  const int64_t parts = (kTargetWorkgroups + units - 1) / units;
+  int64_t bpp = (max_blocks + parts - 1) / parts;
+  if (bpp < 2 * round) bpp = 2 * round;
+  return (bpp + round - 1) / round * round;
+}
+
 // Partition plan of one decode call.
 struct Plan {
   bool mfma = false;
@@ -174,23 +189,8 @@ pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_he
     // the suffix after a shared prefix is short: one pass, merged with the prefix partials in place
     bpp = max_blocks > 0 ? max_blocks : 1;
   } else if (part_tokens == 0) {
-    // Automatic.  One pass per (sequence, kv head) when that already gives
-    // kTargetWorkgroups workgroups: a split costs a second kernel, the partials'
-    // traffic and a prologue/epilogue per workgroup, and measured slower than a
-    // single long walk whenever the GPU is already full.  Fewer units (long
-    // contexts, small batches) are split into equal partitions until about
-    // kTargetWorkgroups exist, each wave keeping at least two rounds of
-    // in-flight blocks.
-    const int64_t units = (int64_t)num_seqs * pool->num_kv_heads;
-    const int64_t round = (int64_t)pkv::kWaves * plan->inflight;
-    if (units >= kTargetWorkgroups || max_blocks <= 2 * round) {
-      bpp = max_blocks > 0 ? max_blocks : 1;
-    } else {
-      const int64_t parts = (kTargetWorkgroups + units - 1) / units;
-      bpp = (max_blocks + parts - 1) / parts;
-      if (bpp < 2 * round) bpp = 2 * round;
-      bpp = (bpp + round - 1) / round * round;
-    }
+    bpp = auto_blocks_per_part((int64_t)num_seqs * pool->num_kv_heads, max_blocks,
+                               (int64_t)pkv::kWaves * plan->inflight);
   } else {
     bpp = (part_tokens + bs - 1) / bs;
   }
@@ -200,6 +200,90 @@ pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_he
   plan->num_parts = max_blocks > 0 ? (int)((max_blocks + bpp - 1) / bpp) : 1;
   if (plan->num_parts > 65535) return fail(PKV_EUNSUPPORTED, "too many partitions; raise partition_tokens");
   return PKV_OK;
+}
+
+// Plan of one multi-token call (several new tokens per sequence).
+struct MultiPlan {
+  bool mfma = false;
+  int group = 1;
+  int col_tiles = 1;      // matrix-core kernel: 16-row column tiles per workgroup
+  int rows_per_tile = 1;  // (token, head) rows per workgroup
+  int row_tiles = 1;      // workgroup row tiles per (sequence, kv head)
+  int inflight = 1;
+  int blocks_per_part = 1;
+  int num_parts = 1;
+};
+
+pkv_status make_multi_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_heads, int32_t num_query_tokens,
+                           int32_t max_query_len, int32_t max_context_len, const pkv_decode_opts* opts,
+                           MultiPlan* plan) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || max_context_len < 0)
+    return fail(PKV_EINVAL, "num_seqs, num_query_tokens, max_query_len and max_context_len must be >= 0");
+  if (num_heads <= 0 || num_heads % pool->num_kv_heads != 0)
+    return fail(PKV_EINVAL, "num_heads must be a positive multiple of num_kv_heads");
+  if (num_seqs > 65535 || max_query_len > 65535)
+    return fail(PKV_EUNSUPPORTED, "num_seqs and max_query_len must stay below 65536");
+  const int g = num_heads / pool->num_kv_heads;
+  const int bf16 = pool->dtype == PKV_BF16;
+  const int kernel = opts ? opts->kernel : PKV_KERNEL_AUTO;
+  if (kernel != PKV_KERNEL_AUTO && kernel != PKV_KERNEL_VECTOR && kernel != PKV_KERNEL_MFMA)
+    return fail(PKV_EINVAL, "unknown kernel selector");
+  if (opts && (opts->prefix_plan || opts->prefix_plan_dev))
+    return fail(PKV_EUNSUPPORTED, "a shared-prefix plan is not taken with several new tokens per sequence");
+  if (opts && opts->heads_per_workgroup > 1)
+    return fail(PKV_EUNSUPPORTED, "several new tokens per sequence take one kv head per workgroup");
+  if (opts && opts->heads_per_workgroup < 0) return fail(PKV_EINVAL, "heads_per_workgroup must be 0, 1 or 2");
+  const int inflight = opts ? opts->blocks_in_flight : 0;
+  if (inflight < 0 || inflight > 2) return fail(PKV_EINVAL, "blocks_in_flight must be 0, 1 or 2");
+  const bool mfma_ok = pkv::multi_mfma_supported(bf16, pool->head_dim, pool->block_size, g);
+  if (kernel == PKV_KERNEL_MFMA && !mfma_ok)
+    return fail(PKV_EUNSUPPORTED, "the matrix-core kernel needs bf16, head_dim 128 and 1, 2, 4 or 8 query heads per kv head");
+  plan->mfma = kernel == PKV_KERNEL_MFMA || (kernel == PKV_KERNEL_AUTO && mfma_ok);
+  if (!plan->mfma && !pkv::vector_supported(bf16, pool->head_dim, pool->block_size, g))
+    return fail(PKV_EUNSUPPORTED, "query heads per kv head must be 1, 2, 4 or 8");
+  plan->group = g;
+  const int qmax = max_query_len > 0 ? max_query_len : 1;
+  const int tile_bytes = pool->block_size * pool->head_dim * elt_bytes(pool->dtype);
+  if (plan->mfma) {
+    const int64_t rows = (int64_t)qmax * g;
+    plan->col_tiles = rows <= 16 ? 1 : 2;
+    plan->rows_per_tile = 16 * plan->col_tiles;
+    plan->row_tiles = (int)((rows + plan->rows_per_tile - 1) / plan->rows_per_tile);
+    if (plan->col_tiles == 2 && inflight == 2)
+      return fail(PKV_EUNSUPPORTED, "row tiles of 32 take one block in flight");
+    plan->inflight = inflight ? inflight : (plan->col_tiles == 1 && tile_bytes <= 4096 ? 2 : 1);
+  } else {
+    plan->rows_per_tile = g;
+    plan->row_tiles = qmax;
+    plan->inflight = inflight ? inflight : 1;
+    if ((int64_t)num_seqs * qmax > 65535)
+      return fail(PKV_EUNSUPPORTED, "vector kernel: num_seqs * max_query_len must stay below 65536");
+  }
+  const int bs = pool->block_size;
+  const int64_t max_blocks = (max_context_len + bs - 1) / bs;
+  int64_t part_tokens = opts ? opts->partition_tokens : 0;
+  if (part_tokens < 0) return fail(PKV_EINVAL, "partition_tokens must be >= 0");
+  int64_t bpp = part_tokens == 0 ? auto_blocks_per_part((int64_t)num_seqs * pool->num_kv_heads * plan->row_tiles,
+                                                        max_blocks, (int64_t)pkv::kWaves * plan->inflight)
+                                 : (part_tokens + bs - 1) / bs;
+  if (bpp < 1) bpp = 1;
+  if (bpp >= max_blocks) bpp = max_blocks > 0 ? max_blocks : 1;
+  plan->blocks_per_part = (int)bpp;
+  plan->num_parts = max_blocks > 0 ? (int)((max_blocks + bpp - 1) / bpp) : 1;
+  if (plan->num_parts > 65535) return fail(PKV_EUNSUPPORTED, "too many partitions; raise partition_tokens");
+  if (plan->mfma) {
+    const int64_t units = (int64_t)plan->num_parts * pool->num_kv_heads * num_seqs;
+    if ((units + pkv::kXcds - 1) / pkv::kXcds * pkv::kXcds * plan->row_tiles > 0x7fffffff)
+      return fail(PKV_EUNSUPPORTED, "too many workgroups; raise partition_tokens");
+  }
+  return PKV_OK;
+}
+
+size_t multi_workspace(const MultiPlan& plan, int32_t num_query_tokens, int32_t num_heads, int32_t head_dim) {
+  if (plan.num_parts <= 1) return 0;
+  return (size_t)num_query_tokens * num_heads * plan.num_parts * (2 + (size_t)head_dim) * sizeof(float);
 }
 
 // Workspace: split-K partials (num_parts > 1), then the prefix-pass partials.
@@ -247,7 +331,7 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
   if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "max_blocks_per_seq must be positive");
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * pool->block_size)
     return fail(PKV_EINVAL, "max_context_len exceeds max_blocks_per_seq * block_size");
-  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale must be finite");
+  if (!std::isfinite(scale) || scale < 0.f) return fail(PKV_EINVAL, "scale must be finite and >= 0");
   if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return fail(PKV_EINVAL, "out_dtype must be F32 or BF16");
   if (pool->dtype == PKV_F32 && out_dtype != PKV_F32) return fail(PKV_EUNSUPPORTED, "f32 inputs need an f32 output");
   const size_t need = workspace_for(plan, num_seqs, num_heads, pool->head_dim);
@@ -319,6 +403,86 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
   if (plan.num_parts > 1) {
     e = pkv::launch_splitk_reduce(a, pool->head_dim, pool->block_size, s);
     if (e != hipSuccess) return fail(PKV_EHIP, std::string("reduce launch: ") + hipGetErrorString(e));
+  }
+  return ok();
+}
+
+size_t pkv_paged_attn_multi_token_workspace_bytes(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_heads,
+                                                  int32_t num_query_tokens, int32_t max_query_len,
+                                                  int32_t max_context_len, const pkv_decode_opts* opts) {
+  MultiPlan plan;
+  if (make_multi_plan(pool, num_seqs, num_heads, num_query_tokens, max_query_len, max_context_len, opts, &plan) !=
+      PKV_OK)
+    return 0;
+  return multi_workspace(plan, num_query_tokens, num_heads, pool->head_dim);
+}
+
+pkv_status pkv_paged_attn_multi_token(const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      const int32_t* query_start, int32_t num_seqs, int32_t num_heads,
+                                      int32_t num_query_tokens, int32_t max_query_len, int32_t max_blocks_per_seq,
+                                      int32_t max_context_len, const pkv_pool_desc* pool, float scale,
+                                      int32_t out_dtype, void* out, void* workspace, size_t workspace_bytes,
+                                      const pkv_decode_opts* opts, void* stream) {
+  MultiPlan plan;
+  pkv_status st =
+      make_multi_plan(pool, num_seqs, num_heads, num_query_tokens, max_query_len, max_context_len, opts, &plan);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return ok();
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start || !out)
+    return fail(PKV_EINVAL, "a data pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return fail(PKV_EINVAL, "q, pools and out must be 16-byte aligned");
+  if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "max_blocks_per_seq must be positive");
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * pool->block_size)
+    return fail(PKV_EINVAL, "max_context_len exceeds max_blocks_per_seq * block_size");
+  if (!std::isfinite(scale) || scale < 0.f) return fail(PKV_EINVAL, "scale must be finite and >= 0");
+  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return fail(PKV_EINVAL, "out_dtype must be F32 or BF16");
+  if (pool->dtype == PKV_F32 && out_dtype != PKV_F32) return fail(PKV_EUNSUPPORTED, "f32 inputs need an f32 output");
+  const size_t need = multi_workspace(plan, num_query_tokens, num_heads, pool->head_dim);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(PKV_EWORKSPACE,
+                "workspace missing, misaligned or smaller than pkv_paged_attn_multi_token_workspace_bytes()");
+
+  pkv::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = pool->num_blocks;
+  a.max_context = max_context_len;
+  a.blocks_per_part = plan.blocks_per_part;
+  a.num_parts = plan.num_parts;
+  a.longest_first = 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.out_bf16 = out_dtype == PKV_BF16;
+  a.query_start = query_start;
+  a.num_query_tokens = num_query_tokens;
+  a.max_query_len = max_query_len;
+  a.rows_per_tile = plan.rows_per_tile;
+  a.row_tiles = plan.row_tiles;
+  if (plan.num_parts > 1) {
+    const size_t rows = (size_t)num_query_tokens * num_heads * plan.num_parts;
+    float* ws = static_cast<float*>(workspace);
+    a.ws_m = ws;
+    a.ws_l = ws + rows;
+    a.ws_acc = ws + 2 * rows;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int bf16 = pool->dtype == PKV_BF16;
+  hipError_t e = plan.mfma ? pkv::launch_multi_mfma(a, pool->block_size, plan.group, plan.col_tiles, plan.inflight, s)
+                           : pkv::launch_decode_vector(a, bf16, pool->head_dim, pool->block_size, plan.group,
+                                                       plan.inflight, 1, s);
+  if (e != hipSuccess) return fail(PKV_EHIP, std::string("multi-token launch: ") + hipGetErrorString(e));
+  if (plan.num_parts > 1) {
+    e = pkv::launch_multi_reduce(a, pool->head_dim, pool->block_size, plan.group, s);
+    if (e != hipSuccess) return fail(PKV_EHIP, std::string("multi-token reduce launch: ") + hipGetErrorString(e));
   }
   return ok();
 }

@@ -17,8 +17,10 @@ namespace pkv {
 
 struct SeqPick {
   int b;
+  int qrow;   // row of q and out (b, or the new token's row with several per sequence)
   int ctx_raw;
   int start;  // blocks covered by a shared-prefix pass (0 without one), not yet clipped to the context
+  bool skip;  // the slot maps to no query row: the workgroup has nothing to do
 };
 
 // Blocks of sequence b that the shared-prefix pass covered (0 without one).
@@ -29,11 +31,31 @@ __device__ __forceinline__ int covered_start(const DecodeArgs& a, int b) {
 
 template <int BS>
 __device__ __forceinline__ SeqPick pick_sequence(const DecodeArgs& a, int* sm_key, int* sm_pick) {
+  if (a.query_start) {
+    // several new tokens per sequence, one per slot: slot = b * max_query_len + i.
+    // Token i sees context_lens[b] - n_b + i + 1 tokens, so it runs as a decode
+    // over that many; a broken length (n_b > context, context > max_context,
+    // n_b > max_query_len) turns the rows the grid covers into NaN.
+    SeqPick p;
+    p.b = blockIdx.z / a.max_query_len;
+    const int i = blockIdx.z % a.max_query_len;
+    const int qs = a.query_start[p.b], qe = a.query_start[p.b + 1];
+    const int ctx = a.context_lens[p.b];
+    const int qlen = qe - qs;
+    p.skip = qs < 0 || qs > qe || qe > a.num_query_tokens || i >= qlen;
+    p.qrow = qs + i;
+    p.start = 0;
+    const bool bad = ctx < qlen || ctx > a.max_context || qlen > a.max_query_len;
+    p.ctx_raw = bad ? -1 : ctx - qlen + i + 1;
+    return p;
+  }
   if (!a.longest_first) {
     SeqPick p;
     p.b = blockIdx.z;
+    p.qrow = p.b;
     p.ctx_raw = a.context_lens[p.b];
     p.start = covered_start<BS>(a, p.b);
+    p.skip = false;
     return p;
   }
   // key = (length + 1) * 256 + 255 - index: distinct, larger for longer
@@ -62,8 +84,10 @@ __device__ __forceinline__ SeqPick pick_sequence(const DecodeArgs& a, int* sm_ke
   __syncthreads();
   SeqPick p;
   p.b = sm_pick[0];
+  p.qrow = p.b;
   p.ctx_raw = sm_pick[1];
   p.start = covered_start<BS>(a, p.b);
+  p.skip = false;
   return p;
 }
 
@@ -71,6 +95,7 @@ __device__ __forceinline__ SeqPick pick_sequence(const DecodeArgs& a, int* sm_ke
 // heads, sequence slots), the slot mapped to a sequence by pick_sequence.
 struct PartRange {
   int b, kvh, part;
+  int qrow;     // row of q and out
   int start;    // first block of this pass (after a shared prefix)
   int ctx;      // context length (0 when context_lens[b] breaks its precondition)
   bool ctx_bad; // context_lens[b] < 0 or > max_context: the rows become NaN and nothing is read
@@ -85,6 +110,7 @@ __device__ __forceinline__ PartRange part_range(const DecodeArgs& a, const SeqPi
   r.part = blockIdx.x;
   r.kvh = blockIdx.y;
   r.b = s.b;
+  r.qrow = s.qrow;
   const int ctx_raw = s.ctx_raw;
   r.ctx_bad = ctx_raw < 0 || ctx_raw > a.max_context;
   r.ctx = r.ctx_bad ? 0 : ctx_raw;
@@ -106,7 +132,7 @@ __device__ __forceinline__ bool finish_if_empty(const DecodeArgs& a, const PartR
   if (r.part < r.nparts) return false;
   if (r.part == 0) {
     for (int idx = threadIdx.x; idx < G * HD; idx += blockDim.x) {
-      const int64_t o = ((int64_t)r.b * a.num_heads + r.kvh * G + idx / HD) * HD + idx % HD;
+      const int64_t o = ((int64_t)r.qrow * a.num_heads + r.kvh * G + idx / HD) * HD + idx % HD;
       if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = r.ctx_bad ? 0x7fc0 : 0;
       else reinterpret_cast<float*>(a.out)[o] = r.ctx_bad ? NAN : 0.f;
     }
@@ -131,18 +157,22 @@ struct WaveIds {
   int ids;
 };
 
-// Started before the context length is known, so the table load overlaps the
-// context-length load.  Entries past the sequence's last block may be read
-// (they are inside the row of max_blocks entries) but never used.
-__device__ __forceinline__ WaveIds wave_ids_begin(const DecodeArgs& a, const SeqPick& s, int wave, int lane) {
+// Ids of blocks first, first + kWaves, ... of sequence b's table row.  Entries
+// past the sequence's last block may be read (they are inside the row of
+// max_blocks entries) but never used.
+__device__ __forceinline__ WaveIds wave_ids_from(const DecodeArgs& a, int b, int first, int lane) {
   WaveIds w;
-  const int b = s.b;
-  const int first = s.start + blockIdx.x * a.blocks_per_part + wave;
   w.row = a.block_tables + (int64_t)b * a.max_blocks + first;
   w.limit = a.max_blocks - first;
   w.chunk = 0;
   w.ids = kWaves * lane < w.limit ? w.row[kWaves * lane] : 0;
   return w;
+}
+
+// Started before the context length is known, so the table load overlaps the
+// context-length load.
+__device__ __forceinline__ WaveIds wave_ids_begin(const DecodeArgs& a, const SeqPick& s, int wave, int lane) {
+  return wave_ids_from(a, s.b, s.start + blockIdx.x * a.blocks_per_part + wave, lane);
 }
 
 // Checks the ids of the current chunk that the wave will use (its first cnt
@@ -234,11 +264,11 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
     }
     if (r.nparts == 1) {
       const float o = acc / l;
-      const int64_t oi = ((int64_t)r.b * a.num_heads + hq) * HD + d;
+      const int64_t oi = ((int64_t)r.qrow * a.num_heads + hq) * HD + d;
       if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_rne(o);
       else reinterpret_cast<float*>(a.out)[oi] = o;
     } else {
-      const int64_t pi = ((int64_t)r.b * a.num_heads + hq) * a.num_parts + r.part;
+      const int64_t pi = ((int64_t)r.qrow * a.num_heads + hq) * a.num_parts + r.part;
       a.ws_acc[pi * HD + d] = acc;
       if (d == 0) {
         a.ws_m[pi] = big_m;

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
   bf16x8 qb[4];
   {
     const uint16_t* qrow =
-        reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)seq.b * a.num_heads + blockIdx.y * G + hslot) * HD;
+        reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)seq.qrow * a.num_heads + blockIdx.y * G + hslot) * HD;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint4 w = used ? load16(qrow + 32 * i + 8 * kg) : make_uint4(0, 0, 0, 0);
@@ -135,9 +135,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
         for (int nt = 0; nt < 8; ++nt) o[nt] *= alpha;
         m = mn;
       }
+      // a select, not the -inf logit, zeroes the weight past the context (-inf times a zero scale is NaN)
       float p[4];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) p[rr] = fast_exp2(fmaf(sr[rr], a.scale_log2, -m));
+      for (int rr = 0; rr < 4; ++rr) p[rr] = (4 * kg + rr < valid) ? fast_exp2(fmaf(s[rr], a.scale_log2, -m)) : 0.f;
       lsum += (p[0] + p[1]) + (p[2] + p[3]);
 
       // columns 0..G-1 take the weights' bf16 hi parts, G..2G-1 their lo parts

@@ -72,12 +72,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
   // block ids (table entries past the sequence's end may be read, never used)
   // and q.
   const SeqPick seq = pick_sequence<BS>(a, sm_key, sm_pick);
+  if (seq.skip) return;
   WaveIds wids = wave_ids_begin(a, seq, wave, lane);
   uint32_t qw[R][KC][4];  // the q chunks this lane meets in the key pass (bf16 pairs kept packed)
 #pragma unroll
   for (int h = 0; h < R; ++h) {
     const char* qrow =
-        reinterpret_cast<const char*>(a.q) + ((int64_t)seq.b * a.num_heads + blockIdx.y * R + h) * HD * ELT;
+        reinterpret_cast<const char*>(a.q) + ((int64_t)seq.qrow * a.num_heads + blockIdx.y * R + h) * HD * ELT;
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
       const uint4 w = load16(qrow + (grp + GK * i) * 16);
@@ -247,9 +248,14 @@ bool vector_supported(int bf16, int hd, int bs, int g) {
   return (hd == 64 || hd == 128) && (bs == 16 || bs == 32) && (g == 1 || g == 2 || g == 4 || g == 8);
 }
 
+// sequence slots: one per sequence, or one per (sequence, new token) with several
+static unsigned seq_slots(const DecodeArgs& a) {
+  return a.query_start ? (unsigned)a.num_seqs * a.max_query_len : (unsigned)a.num_seqs;
+}
+
 template <bool BF16, int HD, int BS, int HP, int U>
 static hipError_t dispatch_g(const DecodeArgs& a, int g, hipStream_t s) {
-  const dim3 grid(a.num_parts, a.num_kv_heads / HP, a.num_seqs);
+  const dim3 grid(a.num_parts, a.num_kv_heads / HP, seq_slots(a));
   const dim3 block(64 * kWaves);
   switch (g) {
     case 1: hipLaunchKernelGGL((decode_vector_kernel<BF16, HD, BS, 1, HP, U>), grid, block, 0, s, a); break;
@@ -274,7 +280,7 @@ static hipError_t dispatch_shape(const DecodeArgs& a, int hd, int bs, int g, hip
 // match a group of two); grid y runs over kv-head pairs
 template <bool BF16, int U>
 static hipError_t dispatch_pairs(const DecodeArgs& a, int hd, int bs, hipStream_t s) {
-  const dim3 grid(a.num_parts, a.num_kv_heads / 2, a.num_seqs);
+  const dim3 grid(a.num_parts, a.num_kv_heads / 2, seq_slots(a));
   const dim3 block(64 * kWaves);
   if (hd == 64 && bs == 16) hipLaunchKernelGGL((decode_vector_kernel<BF16, 64, 16, 1, 2, U>), grid, block, 0, s, a);
   else if (hd == 64 && bs == 32) hipLaunchKernelGGL((decode_vector_kernel<BF16, 64, 32, 1, 2, U>), grid, block, 0, s, a);

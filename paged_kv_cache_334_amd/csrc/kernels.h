@@ -29,7 +29,8 @@ struct DecodeArgs {
   float scale_log2;         // scale * log2(e): logits are kept in the base-2 domain
   void* out;
   int32_t out_bf16;
-  // Partials when num_parts > 1, each indexed by (b*num_heads + h)*num_parts + part:
+  // Partials when num_parts > 1, each indexed by (row*num_heads + h)*num_parts + part (row = b, or the
+  // new token's query row with several per sequence):
   // ws_m (running max, base 2), ws_l (sum of exp2(s - m)), ws_acc (HD floats each).
   float* ws_m;
   float* ws_l;
@@ -43,6 +44,16 @@ struct DecodeArgs {
   const float* pre_m;
   const float* pre_l;
   const float* pre_acc;
+  // Several new tokens per sequence (NULL: one each, the decode step).  New
+  // token i of sequence b (n_b = query_start[b+1] - query_start[b] of them)
+  // has query/output row query_start[b] + i, sits at position
+  // context_lens[b] - n_b + i and sees the tokens up to and including it.
+  // Partials are then indexed by that row instead of b.
+  const int32_t* query_start;
+  int32_t num_query_tokens;  // rows of q and out
+  int32_t max_query_len;     // host bound of n_b; the grid covers that many tokens per sequence
+  int32_t rows_per_tile;     // (token, head) rows of one kv head a workgroup takes (i-major: row = i*G + h)
+  int32_t row_tiles;         // row tiles per (sequence, kv head)
 };
 
 // Shared-prefix plan words (built on the host by pkv_plan_shared_prefix):
@@ -98,6 +109,15 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, int block_size,
                               hipStream_t stream);
 hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeArgs& a, int head_dim, int block_size, hipStream_t stream);
+
+// Several new tokens per sequence (a.query_start set).  Matrix-core kernel:
+// bf16, head_dim 128, group 1/2/4/8, row tiles of 16 * col_tiles rows
+// (col_tiles 1 or 2).  The vector kernel runs one query token per workgroup
+// through launch_decode_vector.  The merge handles both.
+bool multi_mfma_supported(int dtype_bf16, int head_dim, int block_size, int group);
+hipError_t launch_multi_mfma(const DecodeArgs& a, int block_size, int group, int col_tiles, int inflight,
+                             hipStream_t stream);
+hipError_t launch_multi_reduce(const DecodeArgs& a, int head_dim, int block_size, int group, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, int64_t k_stride, int64_t v_stride,
                                     const int32_t* slots, int32_t num_tokens, void* k_pool, void* v_pool,

@@ -1,0 +1,339 @@
+// Paged attention for several new tokens per sequence, causal among them
+// (bf16, head_dim 128), on matrix cores.
+//
+// A verify step of speculative decoding, or a chunk of a prompt, appends n_b
+// tokens to sequence b and attends from each of them: new token i (position
+// ctx - n_b + i) sees the cached tokens up to and including itself.  The pages
+// name these uses of the paged cache (speculative decoding and forked
+// sequences sharing it: "Master Paged Attention for LLM Inference", "How Paged
+// Attention Works: The Mechanics", item 4; prompt prefill filling it:
+// "PagedAttention Explained", "Enabling Automatic Prefix Caching") without a
+// formula; the mask is the standard causal one of a decoder.
+//
+// All n_b * G query rows of one kv head read the same key/value tiles, so the
+// per-tile work is dense: the rows (new token i, head h of the group), i-major
+// (row = i*G + h), fill the columns of the matrix-core tile.  A workgroup takes
+// 16 * CT rows (CT = 1 or 2 column tiles) of one (sequence, kv head,
+// partition), and walks only the blocks its last row sees.
+//
+// One wave, per 16-token sub-tile (as in the decode kernel, with CT column
+// tiles of 16 rows instead of one tile of 2G hi/lo columns):
+//  * S^T = K . Q^T, v_mfma_f32_16x16x32_bf16, 4 instructions per column tile;
+//    lane (column n, group kg) gets S^T[token 4kg+r][row 16ct + n].
+//  * Causal and context mask per lane: token < the row's limit (positions the
+//    row sees).  Only sub-tiles reaching past the tile's smallest limit are
+//    masked (a wave-uniform branch).
+//  * O^T += V^T . P^T, v_mfma_f32_16x16x16bf16_1k: the bf16 hi and lo parts of
+//    the weights go in as two instructions per column tile.
+// Partition partials are merged by multi_reduce_kernel.
+#include "decode_common.h"
+
+namespace pkv {
+
+template <int BS, int G, int CT, int U>
+__global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
+  constexpr int NW = kWaves;
+  constexpr int HD = 128;
+  constexpr int SUB = BS / 16;  // 16-token sub-tiles per block
+  constexpr int TILE_BYTES = HD * BS * 2;
+  constexpr int R = 16 * CT;    // rows per workgroup
+  static_assert(64 % ((U + SUB - 1) / SUB) == 0, "a round must not straddle two id loads");
+
+  struct Tile {
+    uint4 k[4];  // keys of the sub-tile's 16 tokens, MFMA A-operand order
+    uint2 v[8];  // values, 16 dims x 4 tokens per instruction
+  };
+
+  __shared__ float sm_acc[NW][16][HD];
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+  __shared__ int sm_bad[NW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int kg = lane >> 4;
+
+  // Workgroup -> (unit, row tile), XCD-aware: workgroup i runs on XCD i % 8,
+  // and the row tiles of one unit (partition, kv head, sequence) share an XCD
+  // and are dispatched back to back, so all but the first find the unit's
+  // tiles in that XCD's L2.
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int unit = (slot / a.row_tiles) * kXcds + xcd;
+  const int rt = slot % a.row_tiles;
+  if (unit >= a.num_parts * a.num_kv_heads * a.num_seqs) return;
+  const int part = unit % a.num_parts;
+  const int kvh = (unit / a.num_parts) % a.num_kv_heads;
+  const int b = unit / (a.num_parts * a.num_kv_heads);
+
+  const int qs = a.query_start[b], qe = a.query_start[b + 1];
+  if (qs < 0 || qs > qe || qe > a.num_query_tokens) return;  // its rows are unknown: nothing is written
+  const int qlen = qe - qs;
+  const int nrows = min(qlen, a.max_query_len) * G;  // rows the grid covers
+  const int r0 = rt * R;
+  if (r0 >= nrows) return;
+  const int r_end = min(r0 + R, nrows);
+  const int ctx_raw = a.context_lens[b];
+  const bool ctx_bad = ctx_raw < qlen || ctx_raw > a.max_context || qlen > a.max_query_len;
+  const int base = ctx_raw - qlen + 1;              // tokens new token 0 sees
+  const int lim_min = base + r0 / G;                // tokens the tile's first row sees
+  const int ctx = ctx_bad ? 0 : base + (r_end - 1) / G;  // ... and its last row: the tile's walk
+  const int nblocks = (ctx + BS - 1) / BS;
+  const int nparts = (nblocks + a.blocks_per_part - 1) / a.blocks_per_part;
+  if (part >= nparts) {
+    if (part == 0) {  // a broken length: NaN rows
+      for (int idx = threadIdx.x; idx < (r_end - r0) * HD; idx += blockDim.x) {
+        const int row = r0 + idx / HD;
+        const int64_t o = ((int64_t)(qs + row / G) * a.num_heads + kvh * G + row % G) * HD + idx % HD;
+        if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = 0x7fc0;
+        else reinterpret_cast<float*>(a.out)[o] = NAN;
+      }
+    }
+    return;
+  }
+  const int blk_lo = part * a.blocks_per_part;
+  const int blk_hi = min(nblocks, blk_lo + a.blocks_per_part);
+
+  // Columns: lane column n of column tile ct is row r0 + 16ct + n.
+  int lim[CT];
+  bf16x8 qb[CT][4];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int row = r0 + 16 * ct + n;
+    const bool used = row < r_end;
+    lim[ct] = used ? base + row / G : 0;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
+                           ((int64_t)(qs + (used ? row / G : 0)) * a.num_heads + kvh * G + row % G) * HD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 w = used ? load16(qrow + 32 * i + 8 * kg) : make_uint4(0, 0, 0, 0);
+      qb[ct][i] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  const int nb_part = blk_hi - blk_lo;
+  const int cnt = nb_part > wave ? (nb_part - wave + NW - 1) / NW : 0;  // blocks of this wave
+  WaveIds wids = wave_ids_from(a, b, blk_lo + wave, lane);
+  int bad = wave_ids_check(a, &wids, cnt, lane);
+
+  f32x4 o[CT][8];
+  float m[CT], lsum[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[ct] = -INFINITY;
+    lsum[ct] = 0.f;
+  }
+
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (int64_t)kvh * TILE_BYTES;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)kvh * TILE_BYTES;
+  const int64_t block_bytes = (int64_t)a.num_kv_heads * TILE_BYTES;
+  const int units = cnt * SUB;
+
+  // loads of round rnd: sub-tiles rnd*U .. rnd*U+U-1 of the wave (a missing one
+  // re-reads the wave's last sub-tile, a cache hit, and is not used)
+  auto issue = [&](Tile* T, int rnd) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int x = min(rnd * U + u, units - 1);
+      const int sub = x % SUB;
+      const int64_t off = (int64_t)wave_id_at(a, &wids, x / SUB, cnt, lane, &bad) * block_bytes;
+      const auto kt = tile_rsrc(kbase + off, TILE_BYTES);
+      const auto vt = tile_rsrc(vbase + off, TILE_BYTES);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) T[u].k[i] = bload16(kt, ((4 * i + kg) * BS + 16 * sub + n) * 16);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) T[u].v[nt] = bload8(vt, ((16 * nt + n) * BS + 16 * sub + 4 * kg) * 2);
+    }
+  };
+
+  auto compute = [&](Tile* T, int rnd) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int x = rnd * U + u;
+      if (x >= units) break;
+      const int j = blk_lo + wave + NW * (x / SUB);  // logical block
+      const int tok0 = j * BS + 16 * (x % SUB);      // first token of the sub-tile
+      const int valid = ctx - tok0;
+      if (valid <= 0) continue;  // second half of a block past the walk
+
+      f32x4 s[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        s[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T[u].k[i]), qb[ct][i], s[ct],
+                                                          0, 0, 0);
+      }
+      // rows whose limit falls inside this sub-tile (every row when it is past the smallest limit)
+      const bool masked = tok0 + 16 > lim_min;
+      bool keep[CT][4];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) keep[ct][rr] = !masked || tok0 + 4 * kg + rr < lim[ct];
+
+      // raw logits; the scale (>= 0) is applied to the maximum and inside the exponent
+      float mx[CT];
+      bool grow = false;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        float v4[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) v4[rr] = keep[ct][rr] ? s[ct][rr] : -INFINITY;
+        const float raw = max_xor32(max_xor16(fmaxf(fmaxf(v4[0], v4[1]), fmaxf(v4[2], v4[3]))));
+        mx[ct] = raw == -INFINITY ? -INFINITY : raw * a.scale_log2;  // a column with nothing visible here
+        grow |= mx[ct] > m[ct] + kRescaleSlack;
+      }
+      if (__ballot(grow) != 0) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const float mn = fmaxf(m[ct], mx[ct]);
+          const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[ct] - mn);
+          lsum[ct] *= alpha;
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) o[ct][nt] *= alpha;
+          m[ct] = mn;
+        }
+      }
+      s16x4 pb_hi[CT], pb_lo[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        float p[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) p[rr] = keep[ct][rr] ? fast_exp2(fmaf(s[ct][rr], a.scale_log2, -m[ct])) : 0.f;
+        lsum[ct] += (p[0] + p[1]) + (p[2] + p[3]);
+        uint32_t hi0, lo0, hi1, lo1;
+        split_bf16(p[0], p[1], &hi0, &lo0);
+        split_bf16(p[2], p[3], &hi1, &lo1);
+        pb_hi[ct] = __builtin_bit_cast(s16x4, make_uint2(hi0, hi1));
+        pb_lo[ct] = __builtin_bit_cast(s16x4, make_uint2(lo0, lo1));
+      }
+
+      if (valid < 16) {  // value rows past the walk may hold NaN: zero them, a zero weight is not enough
+        const int first = 4 * kg;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          uint32_t w0 = T[u].v[nt].x, w1 = T[u].v[nt].y;
+          if (first + 0 >= valid) w0 &= 0xffff0000u;
+          if (first + 1 >= valid) w0 &= 0x0000ffffu;
+          if (first + 2 >= valid) w1 &= 0xffff0000u;
+          if (first + 3 >= valid) w1 &= 0x0000ffffu;
+          T[u].v[nt] = make_uint2(w0, w1);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const s16x4 va = __builtin_bit_cast(s16x4, T[u].v[nt]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_hi[ct], o[ct][nt], 0, 0, 0);
+          o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_lo[ct], o[ct][nt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  Tile ta[U], tb[U];
+  pipelined_rounds((units + U - 1) / U, ta, tb, issue, compute);
+
+  // Per column tile: the waves' states through LDS, merged by the workgroup:
+  // M = max_w m_w, l = sum_w 2^(m_w - M) l_w, acc = sum_w 2^(m_w - M) acc_w.
+  if (lane == 0) sm_bad[wave] = bad;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    if (ct) __syncthreads();  // the previous tile's merge has read the buffers
+    const float l = sum_xor32(sum_xor16(lsum[ct]));
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sm_acc[wave][n][16 * nt + 4 * kg + rr] = o[ct][nt][rr];
+    if (kg == 0) {
+      sm_m[wave][n] = m[ct];
+      sm_l[wave][n] = l;
+    }
+    __syncthreads();
+    int any_bad = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any_bad |= sm_bad[w];
+    for (int idx = threadIdx.x; idx < 16 * HD; idx += 64 * NW) {
+      const int c = idx / HD, d = idx % HD;
+      const int row = r0 + 16 * ct + c;
+      if (row >= r_end) continue;
+      float big_m = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][c]);
+      float lt = 0.f, acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = sm_m[w][c] == -INFINITY ? 0.f : fast_exp2(sm_m[w][c] - big_m);
+        lt = fmaf(f, sm_l[w][c], lt);
+        acc = fmaf(f, sm_acc[w][c][d], acc);
+      }
+      if (any_bad) {
+        big_m = NAN;
+        acc = NAN;
+      }
+      const int64_t hrow = (int64_t)(qs + row / G) * a.num_heads + kvh * G + row % G;
+      if (nparts == 1) {
+        const float y = acc / lt;
+        if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[hrow * HD + d] = (uint16_t)f32_to_bf16_rne(y);
+        else reinterpret_cast<float*>(a.out)[hrow * HD + d] = y;
+      } else {
+        const int64_t pi = hrow * a.num_parts + part;
+        a.ws_acc[pi * HD + d] = acc;
+        if (d == 0) {
+          a.ws_m[pi] = big_m;
+          a.ws_l[pi] = lt;
+        }
+      }
+    }
+  }
+}
+
+bool multi_mfma_supported(int bf16, int hd, int bs, int g) {
+  return bf16 && hd == 128 && (bs == 16 || bs == 32) && (g == 1 || g == 2 || g == 4 || g == 8);
+}
+
+template <int CT, int U>
+static hipError_t launch_ct(const DecodeArgs& a, int bs, int g, hipStream_t s) {
+  const int64_t units = (int64_t)a.num_parts * a.num_kv_heads * a.num_seqs;
+  const int64_t wgs = (units + kXcds - 1) / kXcds * kXcds * a.row_tiles;
+  if (wgs <= 0 || wgs > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs);
+  const dim3 block(64 * kWaves);
+#define PKV_MULTI(BS, G) hipLaunchKernelGGL((multi_mfma_kernel<BS, G, CT, U>), grid, block, 0, s, a)
+  if (bs == 16) {
+    switch (g) {
+      case 1: PKV_MULTI(16, 1); break;
+      case 2: PKV_MULTI(16, 2); break;
+      case 4: PKV_MULTI(16, 4); break;
+      case 8: PKV_MULTI(16, 8); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (bs == 32) {
+    switch (g) {
+      case 1: PKV_MULTI(32, 1); break;
+      case 2: PKV_MULTI(32, 2); break;
+      case 4: PKV_MULTI(32, 4); break;
+      case 8: PKV_MULTI(32, 8); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef PKV_MULTI
+  return hipGetLastError();
+}
+
+hipError_t launch_multi_mfma(const DecodeArgs& a, int bs, int g, int col_tiles, int inflight, hipStream_t s) {
+  if (a.rows_per_tile != 16 * col_tiles) return hipErrorInvalidValue;
+  if (col_tiles == 1) return inflight == 2 ? launch_ct<1, 2>(a, bs, g, s) : launch_ct<1, 1>(a, bs, g, s);
+  if (col_tiles == 2 && inflight == 1) return launch_ct<2, 1>(a, bs, g, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

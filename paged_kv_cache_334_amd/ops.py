@@ -55,6 +55,14 @@ lib.pkv_paged_attn_decode.argtypes = [
     _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, ctypes.POINTER(PoolDesc), ctypes.c_float, _i32, _vp, _vp, _sz,
     ctypes.POINTER(DecodeOpts), _vp,
 ]
+lib.pkv_paged_attn_multi_token_workspace_bytes.restype = _sz
+lib.pkv_paged_attn_multi_token_workspace_bytes.argtypes = [ctypes.POINTER(PoolDesc), _i32, _i32, _i32, _i32, _i32,
+                                                           ctypes.POINTER(DecodeOpts)]
+lib.pkv_paged_attn_multi_token.restype = _i32
+lib.pkv_paged_attn_multi_token.argtypes = [
+    _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(PoolDesc), ctypes.c_float, _i32,
+    _vp, _vp, _sz, ctypes.POINTER(DecodeOpts), _vp,
+]
 lib.pkv_reshape_and_cache.restype = _i32
 lib.pkv_reshape_and_cache.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp, ctypes.POINTER(PoolDesc), _vp]
 lib.pkv_copy_blocks.restype = _i32
@@ -226,6 +234,47 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=
                                    nh, max_blocks, int(max_context_len), ctypes.byref(desc), float(scale), odt_code,
                                    _ptr(out), _ptr(workspace), ws_bytes, ctypes.byref(opts), _stream(stream))
     _check(st, "pkv_paged_attn_decode")
+    return out
+
+
+def paged_attn_multi_token(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, max_query_len,
+                           out=None, max_context_len=None, workspace=None, partition_tokens=0, kernel="auto",
+                           out_dtype=None, stream=None, blocks_in_flight=0):
+    """Several new tokens per sequence, causal among them: row
+    ``query_start[b] + i`` of ``q [T, Hq, D]`` (new token i of sequence b, at
+    position ``context_lens[b] - n_b + i``) attends over the sequence's tokens up
+    to and including itself.  ``query_start [B+1]`` int32 on the device;
+    ``max_query_len`` is the host bound of ``n_b``."""
+    desc = pool_desc(k_pool, v_pool)
+    ntok, nh, hd = q.shape
+    nseq = query_start.shape[0] - 1
+    if hd != desc.head_dim or _elem(q) != desc.dtype:
+        raise ValueError("q does not match the pools")
+    for t in (block_tables, context_lens, query_start):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError("block_tables, context_lens and query_start must be contiguous int32")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if block_tables.shape[0] != nseq or context_lens.shape[0] != nseq:
+        raise ValueError("block_tables, context_lens and query_start disagree on the number of sequences")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * desc.block_size
+    if out is None:
+        odt = q.dtype if out_dtype is None else out_dtype
+        out = torch.empty((ntok, nh, hd), dtype=odt, device=q.device)
+    odt_code = PKV_BF16 if out.dtype == torch.bfloat16 else PKV_F32
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, None)
+    need = int(lib.pkv_paged_attn_multi_token_workspace_bytes(ctypes.byref(desc), nseq, nh, ntok, int(max_query_len),
+                                                              int(max_context_len), ctypes.byref(opts)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pkv_paged_attn_multi_token(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
+                                        _ptr(query_start), nseq, nh, ntok, int(max_query_len), max_blocks,
+                                        int(max_context_len), ctypes.byref(desc), float(scale), odt_code, _ptr(out),
+                                        _ptr(workspace), ws_bytes, ctypes.byref(opts), _stream(stream))
+    _check(st, "pkv_paged_attn_multi_token")
     return out
 
 

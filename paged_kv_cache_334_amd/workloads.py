@@ -162,6 +162,13 @@ SPECS = {
 }
 ORDER = ["tiny-f32", "mha-7b", "gqa-70b", "long-32k", "shared-prefix"]
 
+# Several new tokens per sequence: the 70B-shaped GQA batch verifying 4 tokens
+# per sequence (3 drafted + 1), as a speculative-decoding step does.
+MULTI_SPECS = {
+    "verify-gqa-70b": WorkloadSpec("verify-gqa-70b", BF16, 128, 64, 8, 128, 16, (512, 4096), seed=1006,
+                                   query_len=4),
+}
+
 
 @dataclass
 class Workload:

@@ -45,6 +45,7 @@ class GpuWorkload:
         self.new_v = to_device(wl.new_v, s.dtype, device)
         self.new_slots = torch.from_numpy(wl.new_slots).to(device)
         self.cow_pairs = torch.from_numpy(wl.cow_pairs.reshape(-1, 2)).to(device)
+        self.query_start = torch.from_numpy(wl.query_start).to(device)
         if len(wl.init_slots):
             ops.reshape_and_cache(self.init_k, self.init_v, self.init_slots, self.k_pool, self.v_pool)
         self.step_cache_ops()
@@ -59,6 +60,13 @@ class GpuWorkload:
         kw.setdefault("max_context_len", self.wl.max_context)
         return ops.paged_attn_decode(self.q, self.k_pool, self.v_pool, self.block_tables, self.context_lens,
                                      self.wl.scale, **kw)
+
+
+    def multi(self, **kw):
+        kw.setdefault("max_context_len", self.wl.max_context)
+        kw.setdefault("max_query_len", self.wl.max_query_len)
+        return ops.paged_attn_multi_token(self.q, self.k_pool, self.v_pool, self.block_tables, self.context_lens,
+                                          self.query_start, self.wl.scale, **kw)
 
 
 def out_to_f64(out):

@@ -83,6 +83,7 @@ def test_bad_decode_arguments(ops):
     assert _decode(ops, d, ptr=8) == 1                   # misaligned
     assert _decode(ops, d, max_ctx=16 * 16 + 1) == 1     # beyond max_blocks * block_size
     assert _decode(ops, d, scale=float("inf")) == 1
+    assert _decode(ops, d, scale=-0.5) == 1              # the kernels take the max of unscaled logits
     assert _decode(ops, _desc(ops, dtype=ops.PKV_F32), out_dtype=ops.PKV_BF16) == 2
     assert _decode(ops, d, opts=ops.DecodeOpts(0, 9, 0)) == 1
     assert _decode(ops, _desc(ops, num_kv_heads=32), opts=ops.DecodeOpts(0, 2, 0)) == 2  # MFMA needs a group of 4/8
@@ -189,3 +190,50 @@ def test_swap_arguments(ops):
     assert ops.lib.pkv_swap_blocks(p, p, ctypes.byref(d), p, p, ctypes.byref(d), p, -1, None) == 1
     assert ops.lib.pkv_swap_blocks(p, None, ctypes.byref(d), p, p, ctypes.byref(d), p, 2, None) == 1
     assert ops.lib.pkv_swap_blocks(p, p, ctypes.byref(d), p, p, ctypes.byref(d), p, 0, None) == 0
+
+
+def _multi(ops, desc, num_heads=32, max_ctx=256, ptr=16, opts=None, out_dtype=None, ws=0, ws_bytes=0,
+           max_blocks=16, scale=0.1, nseq=4, ntok=12, max_q=4):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    od = desc.dtype if out_dtype is None else out_dtype
+    return ops.lib.pkv_paged_attn_multi_token(p, p, p, p, p, p, nseq, num_heads, ntok, max_q, max_blocks, max_ctx,
+                                              ctypes.byref(desc), scale, od, p, ctypes.c_void_p(ws) if ws else None,
+                                              ws_bytes, ctypes.byref(opts) if opts else None, None)
+
+
+def test_multi_token_arguments(ops):
+    d = _desc(ops)
+    single = ops.DecodeOpts(1 << 30, 0, 0)
+    assert _multi(ops, d, num_heads=12, opts=single) == 1
+    assert _multi(ops, d, ptr=0, opts=single) == 1
+    assert _multi(ops, d, ptr=8, opts=single) == 1
+    assert _multi(ops, d, scale=-1.0, opts=single) == 1
+    assert _multi(ops, d, max_q=-1, opts=single) == 1
+    assert _multi(ops, d, max_q=70000, opts=single) == 2
+    assert _multi(ops, d, max_ctx=16 * 16 + 1, opts=single) == 1
+    # the matrix-core kernel takes bf16 / head_dim 128; f32 runs on the vector kernel
+    assert _multi(ops, _desc(ops, dtype=ops.PKV_F32), opts=ops.DecodeOpts(1 << 30, 2, 0)) == 2
+    assert _multi(ops, _desc(ops, head_dim=64), opts=ops.DecodeOpts(1 << 30, 2, 0)) == 2
+    # no shared-prefix plan, one kv head per workgroup, one block in flight for 32-row tiles
+    plan = (ctypes.c_int32 * 8)()
+    assert _multi(ops, d, opts=ops.DecodeOpts(1 << 30, 0, 0, 0, ctypes.addressof(plan), 16, 8)) == 2
+    assert _multi(ops, d, opts=ops.DecodeOpts(1 << 30, 0, 0, 2)) == 2
+    assert _multi(ops, d, max_q=5, opts=ops.DecodeOpts(1 << 30, 2, 2)) == 2  # 5 tokens x group 4 = 20 rows: 32-row tiles
+    # vector kernel: one workgroup per (sequence, new token) within the grid's z range
+    assert _multi(ops, d, nseq=300, max_q=300, opts=ops.DecodeOpts(1 << 30, 1, 0)) == 2
+    # nothing to do
+    assert _multi(ops, d, ntok=0, opts=single) == 0
+    assert _multi(ops, d, nseq=0, opts=single) == 0
+
+
+def test_multi_token_workspace(ops):
+    d = _desc(ops)  # 8 kv heads, group 4
+    opts = ops.DecodeOpts(64, 0, 0)
+    # 3 new tokens x 4 heads = 12 rows: one 16-row tile; 4 partitions of 64 tokens
+    need = ops.lib.pkv_paged_attn_multi_token_workspace_bytes(ctypes.byref(d), 4, 32, 12, 3, 256, ctypes.byref(opts))
+    assert need == 12 * 32 * 4 * (128 + 2) * 4
+    assert _multi(ops, d, opts=opts, max_q=3) == 3
+    assert _multi(ops, d, opts=opts, max_q=3, ws=16, ws_bytes=need - 4) == 3
+    single = ops.DecodeOpts(1 << 30, 0, 0)
+    assert ops.lib.pkv_paged_attn_multi_token_workspace_bytes(ctypes.byref(d), 4, 32, 12, 3, 256,
+                                                              ctypes.byref(single)) == 0
