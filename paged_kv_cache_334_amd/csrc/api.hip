@@ -458,7 +458,8 @@ pkv_status pkv_paged_attn_multi_token(const void* q, const void* k_pool, const v
   a.max_context = max_context_len;
   a.blocks_per_part = plan.blocks_per_part;
   a.num_parts = plan.num_parts;
-  a.longest_first = 0;
+  // the matrix-core kernel orders sequences longest first (one ranking thread per sequence)
+  a.longest_first = plan.mfma && num_seqs > 1 && num_seqs <= pkv::kMaxRankSeqs && max_context_len < (1 << 23);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = out;
   a.out_bf16 = out_dtype == PKV_BF16;

@@ -29,6 +29,39 @@ __device__ __forceinline__ int covered_start(const DecodeArgs& a, int b) {
   return a.start_blocks ? prefix_covered_blocks(max(a.start_blocks[b], 0), BS) : 0;
 }
 
+// The sequence of rank `slot` when ordered by decreasing context length (ties
+// by index), with its raw context length.  Every thread of the workgroup must
+// call it (two barriers).  key = (length + 1) * 256 + 255 - index: distinct,
+// larger for longer sequences and, among equal lengths, for smaller indices (a
+// broken length counts as -1); rank = how many keys are larger.  The host
+// enables it only for num_seqs <= kMaxRankSeqs and max_context < 2^23, so keys
+// stay below 2^31.
+__device__ __forceinline__ void sequence_of_rank(const DecodeArgs& a, int slot, int* sm_key, int* sm_pick, int* b,
+                                                 int* ctx_raw) {
+  const int t = threadIdx.x;
+  const int nb = a.num_seqs;
+  int raw = 0;
+  uint32_t key = 0;
+  if (t < nb) {
+    raw = a.context_lens[t];
+    const int len = (raw < 0 || raw > a.max_context) ? -1 : raw;
+    key = (uint32_t)(len + 1) * 256u + (uint32_t)(255 - t);
+    sm_key[t] = (int)key;
+  }
+  __syncthreads();
+  if (t < nb) {
+    int rank = 0;
+    for (int o = 0; o < nb; ++o) rank += (uint32_t)sm_key[o] > key;
+    if (rank == slot) {
+      sm_pick[0] = t;
+      sm_pick[1] = raw;
+    }
+  }
+  __syncthreads();
+  *b = sm_pick[0];
+  *ctx_raw = sm_pick[1];
+}
+
 template <int BS>
 __device__ __forceinline__ SeqPick pick_sequence(const DecodeArgs& a, int* sm_key, int* sm_pick) {
   if (a.query_start) {
@@ -58,34 +91,9 @@ __device__ __forceinline__ SeqPick pick_sequence(const DecodeArgs& a, int* sm_ke
     p.skip = false;
     return p;
   }
-  // key = (length + 1) * 256 + 255 - index: distinct, larger for longer
-  // sequences and, among equal lengths, for smaller indices (a broken length
-  // counts as -1); rank = how many keys are larger.  The host enables this
-  // only for max_context < 2^23, so keys stay below 2^31.
-  const int t = threadIdx.x;
-  const int nb = a.num_seqs;
-  int raw = 0;
-  uint32_t key = 0;
-  if (t < nb) {
-    raw = a.context_lens[t];
-    const int len = (raw < 0 || raw > a.max_context) ? -1 : raw;
-    key = (uint32_t)(len + 1) * 256u + (uint32_t)(255 - t);
-    sm_key[t] = (int)key;
-  }
-  __syncthreads();
-  if (t < nb) {
-    int rank = 0;
-    for (int o = 0; o < nb; ++o) rank += (uint32_t)sm_key[o] > key;
-    if (rank == (int)blockIdx.z) {
-      sm_pick[0] = t;
-      sm_pick[1] = raw;
-    }
-  }
-  __syncthreads();
   SeqPick p;
-  p.b = sm_pick[0];
+  sequence_of_rank(a, blockIdx.z, sm_key, sm_pick, &p.b, &p.ctx_raw);
   p.qrow = p.b;
-  p.ctx_raw = sm_pick[1];
   p.start = covered_start<BS>(a, p.b);
   p.skip = false;
   return p;

@@ -16,15 +16,21 @@
 // 16 * CT rows (CT = 1 or 2 column tiles) of one (sequence, kv head,
 // partition), and walks only the blocks its last row sees.
 //
-// One wave, per 16-token sub-tile (as in the decode kernel, with CT column
-// tiles of 16 rows instead of one tile of 2G hi/lo columns):
-//  * S^T = K . Q^T, v_mfma_f32_16x16x32_bf16, 4 instructions per column tile;
-//    lane (column n, group kg) gets S^T[token 4kg+r][row 16ct + n].
+// One wave, per 16-token sub-tile:
+//  * S^T = K . Q^T, v_mfma_f32_16x16x32_bf16, 4 instructions per 16-row column
+//    tile; lane (column n, group kg) gets S^T[token 4kg+r][row 16ct + n].
+//  * One 16-lane row swap per logit (v_permlane16_swap) regroups them so that
+//    lane L holds tokens 8h..8h+7 (h = L / 32) of one column c = L % 32: with
+//    two column tiles, rows 0..31 of the workgroup; with one, row c % 16, the
+//    columns 16..31 repeating 0..15.  That is the B-operand layout of the
+//    32x32x16 matrix instruction, so P.V runs on v_mfma_f32_32x32x16_bf16 (full
+//    rate on gfx950, where the 16x16x16 form runs at half): O^T[32 dims x 32
+//    columns] += V^T[32 dims x 16 tokens] . P^T, 4 instructions per 128 dims.
+//    Weights go in as bf16 hi + lo parts: as two instructions with 32 rows,
+//    as columns 0..15 (hi) and 16..31 (lo) of one with 16.
 //  * Causal and context mask per lane: token < the row's limit (positions the
 //    row sees).  Only sub-tiles reaching past the tile's smallest limit are
 //    masked (a wave-uniform branch).
-//  * O^T += V^T . P^T, v_mfma_f32_16x16x16bf16_1k: the bf16 hi and lo parts of
-//    the weights go in as two instructions per column tile.
 // Partition partials are merged by multi_reduce_kernel.
 #include "decode_common.h"
 
@@ -41,13 +47,15 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
 
   struct Tile {
     uint4 k[4];  // keys of the sub-tile's 16 tokens, MFMA A-operand order
-    uint2 v[8];  // values, 16 dims x 4 tokens per instruction
+    uint4 v[4];  // values: 32 dims x 16 tokens per instruction, 8 tokens of one dim per lane
   };
 
   __shared__ float sm_acc[NW][16][HD];
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
   __shared__ int sm_bad[NW];
+  __shared__ int sm_key[kMaxRankSeqs];
+  __shared__ int sm_pick[2];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -65,7 +73,12 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
   if (unit >= a.num_parts * a.num_kv_heads * a.num_seqs) return;
   const int part = unit % a.num_parts;
   const int kvh = (unit / a.num_parts) % a.num_kv_heads;
-  const int b = unit / (a.num_parts * a.num_kv_heads);
+  // sequence slot -> sequence: longest first when the host asks for it (the
+  // long walks start first, the launch ends on short ones)
+  int b = unit / (a.num_parts * a.num_kv_heads);
+  int ctx_raw;
+  if (a.longest_first) sequence_of_rank(a, b, sm_key, sm_pick, &b, &ctx_raw);
+  else ctx_raw = a.context_lens[b];
 
   const int qs = a.query_start[b], qe = a.query_start[b + 1];
   if (qs < 0 || qs > qe || qe > a.num_query_tokens) return;  // its rows are unknown: nothing is written
@@ -74,7 +87,6 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
   const int r0 = rt * R;
   if (r0 >= nrows) return;
   const int r_end = min(r0 + R, nrows);
-  const int ctx_raw = a.context_lens[b];
   const bool ctx_bad = ctx_raw < qlen || ctx_raw > a.max_context || qlen > a.max_query_len;
   const int base = ctx_raw - qlen + 1;              // tokens new token 0 sees
   const int lim_min = base + r0 / G;                // tokens the tile's first row sees
@@ -95,14 +107,12 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
   const int blk_lo = part * a.blocks_per_part;
   const int blk_hi = min(nblocks, blk_lo + a.blocks_per_part);
 
-  // Columns: lane column n of column tile ct is row r0 + 16ct + n.
-  int lim[CT];
+  // S^T columns: lane column n of column tile ct is row r0 + 16ct + n.
   bf16x8 qb[CT][4];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int row = r0 + 16 * ct + n;
     const bool used = row < r_end;
-    lim[ct] = used ? base + row / G : 0;
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
                            ((int64_t)(qs + (used ? row / G : 0)) * a.num_heads + kvh * G + row % G) * HD;
 #pragma unroll
@@ -111,21 +121,25 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
       qb[ct][i] = __builtin_bit_cast(bf16x8, w);
     }
   }
+  // After the regrouping: lane L has column c = L % 32, tokens 8h..8h+7 (h = L / 32);
+  // its row is r0 + c with two column tiles, r0 + c % 16 with one.
+  const int c = lane & 31;
+  const int h = lane >> 5;
+  const int my_row = r0 + (CT == 2 ? c : (c & 15));
+  const int lim = my_row < r_end ? base + my_row / G : 0;  // tokens the lane's row sees
+  const bool lo_col = CT == 1 && c >= 16;                   // one column tile: columns 16..31 take the lo parts
 
   const int nb_part = blk_hi - blk_lo;
   const int cnt = nb_part > wave ? (nb_part - wave + NW - 1) / NW : 0;  // blocks of this wave
   WaveIds wids = wave_ids_from(a, b, blk_lo + wave, lane);
   int bad = wave_ids_check(a, &wids, cnt, lane);
 
-  f32x4 o[CT][8];
-  float m[CT], lsum[CT];
+  f32x16 o[4];  // O^T, 32 dims per instruction: lane holds column c, dims 32db + 8(i/4) + 4h + i%4
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[ct] = -INFINITY;
-    lsum[ct] = 0.f;
-  }
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
 
   const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (int64_t)kvh * TILE_BYTES;
   const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)kvh * TILE_BYTES;
@@ -144,8 +158,9 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
       const auto vt = tile_rsrc(vbase + off, TILE_BYTES);
 #pragma unroll
       for (int i = 0; i < 4; ++i) T[u].k[i] = bload16(kt, ((4 * i + kg) * BS + 16 * sub + n) * 16);
+      // values: dim 32db + c, tokens 8h..8h+7 of the sub-tile (16 contiguous bytes of the dim-major tile)
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) T[u].v[nt] = bload8(vt, ((16 * nt + n) * BS + 16 * sub + 4 * kg) * 2);
+      for (int db = 0; db < 4; ++db) T[u].v[db] = bload16(vt, ((32 * db + c) * BS + 16 * sub + 8 * h) * 2);
     }
   };
 
@@ -168,70 +183,68 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
           s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T[u].k[i]), qb[ct][i], s[ct],
                                                           0, 0, 0);
       }
-      // rows whose limit falls inside this sub-tile (every row when it is past the smallest limit)
+      // regroup: the swap exchanges odd 16-lane rows of its first operand with
+      // even rows of its second, which leaves tokens 8h + r in the first result
+      // and 8h + 4 + r in the second, for the lane's own column
+      float t8[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(s[0][r]), __float_as_uint(s[CT - 1][r]),
+                                                         false, false);
+        t8[r] = __uint_as_float(sw[0]);
+        t8[4 + r] = __uint_as_float(sw[1]);
+      }
+      // the row's visible tokens (every one when the sub-tile ends before the tile's smallest limit)
       const bool masked = tok0 + 16 > lim_min;
-      bool keep[CT][4];
+      bool keep[8];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) keep[ct][rr] = !masked || tok0 + 4 * kg + rr < lim[ct];
+      for (int e = 0; e < 8; ++e) keep[e] = !masked || tok0 + 8 * h + e < lim;
 
       // raw logits; the scale (>= 0) is applied to the maximum and inside the exponent
-      float mx[CT];
-      bool grow = false;
+      float v8[8];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        float v4[4];
+      for (int e = 0; e < 8; ++e) v8[e] = keep[e] ? t8[e] : -INFINITY;
+      const float raw = max_xor32(fmaxf(fmaxf(fmaxf(v8[0], v8[1]), fmaxf(v8[2], v8[3])),
+                                        fmaxf(fmaxf(v8[4], v8[5]), fmaxf(v8[6], v8[7]))));
+      const float mx = raw == -INFINITY ? -INFINITY : raw * a.scale_log2;  // nothing visible here
+      if (__ballot(mx > m + kRescaleSlack) != 0) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
+        lsum *= alpha;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) v4[rr] = keep[ct][rr] ? s[ct][rr] : -INFINITY;
-        const float raw = max_xor32(max_xor16(fmaxf(fmaxf(v4[0], v4[1]), fmaxf(v4[2], v4[3]))));
-        mx[ct] = raw == -INFINITY ? -INFINITY : raw * a.scale_log2;  // a column with nothing visible here
-        grow |= mx[ct] > m[ct] + kRescaleSlack;
+        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+        m = mn;
       }
-      if (__ballot(grow) != 0) {
+      float p[8];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const float mn = fmaxf(m[ct], mx[ct]);
-          const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[ct] - mn);
-          lsum[ct] *= alpha;
+      for (int e = 0; e < 8; ++e) p[e] = keep[e] ? fast_exp2(fmaf(t8[e], a.scale_log2, -m)) : 0.f;
+      lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      uint32_t hw[4], lw[4];
 #pragma unroll
-          for (int nt = 0; nt < 8; ++nt) o[ct][nt] *= alpha;
-          m[ct] = mn;
-        }
-      }
-      s16x4 pb_hi[CT], pb_lo[CT];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        float p[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) p[rr] = keep[ct][rr] ? fast_exp2(fmaf(s[ct][rr], a.scale_log2, -m[ct])) : 0.f;
-        lsum[ct] += (p[0] + p[1]) + (p[2] + p[3]);
-        uint32_t hi0, lo0, hi1, lo1;
-        split_bf16(p[0], p[1], &hi0, &lo0);
-        split_bf16(p[2], p[3], &hi1, &lo1);
-        pb_hi[ct] = __builtin_bit_cast(s16x4, make_uint2(hi0, hi1));
-        pb_lo[ct] = __builtin_bit_cast(s16x4, make_uint2(lo0, lo1));
-      }
+      for (int e = 0; e < 4; ++e) split_bf16(p[2 * e], p[2 * e + 1], &hw[e], &lw[e]);
+      const bf16x8 pb_hi = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const bf16x8 pb_lo = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
 
       if (valid < 16) {  // value rows past the walk may hold NaN: zero them, a zero weight is not enough
-        const int first = 4 * kg;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          uint32_t w0 = T[u].v[nt].x, w1 = T[u].v[nt].y;
-          if (first + 0 >= valid) w0 &= 0xffff0000u;
-          if (first + 1 >= valid) w0 &= 0x0000ffffu;
-          if (first + 2 >= valid) w1 &= 0xffff0000u;
-          if (first + 3 >= valid) w1 &= 0x0000ffffu;
-          T[u].v[nt] = make_uint2(w0, w1);
+        for (int db = 0; db < 4; ++db) {
+          uint32_t w[4] = {T[u].v[db].x, T[u].v[db].y, T[u].v[db].z, T[u].v[db].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (8 * h + 2 * e >= valid) w[e] &= 0xffff0000u;
+            if (8 * h + 2 * e + 1 >= valid) w[e] &= 0x0000ffffu;
+          }
+          T[u].v[db] = make_uint4(w[0], w[1], w[2], w[3]);
         }
       }
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const s16x4 va = __builtin_bit_cast(s16x4, T[u].v[nt]);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_hi[ct], o[ct][nt], 0, 0, 0);
-          o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_lo[ct], o[ct][nt], 0, 0, 0);
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 va = __builtin_bit_cast(bf16x8, T[u].v[db]);
+        if constexpr (CT == 2) {
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb_hi, o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb_lo, o[db], 0, 0, 0);
+        } else {
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, lo_col ? pb_lo : pb_hi, o[db], 0, 0, 0);
         }
       }
     }
@@ -240,38 +253,49 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
   Tile ta[U], tb[U];
   pipelined_rounds((units + U - 1) / U, ta, tb, issue, compute);
 
-  // Per column tile: the waves' states through LDS, merged by the workgroup:
-  // M = max_w m_w, l = sum_w 2^(m_w - M) l_w, acc = sum_w 2^(m_w - M) acc_w.
+  // wave totals: the weight sum over both token halves; one column tile adds
+  // each row's hi and lo columns (c and c + 16)
+  const float l = sum_xor32(lsum);
+  if constexpr (CT == 1) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] = sum_xor16(o[db][i]);
+  }
+
+  // Per group of 16 columns: the waves' states through LDS, merged by the
+  // workgroup: M = max_w m_w, l = sum_w 2^(m_w - M) l_w, acc = sum_w 2^(m_w - M) acc_w.
   if (lane == 0) sm_bad[wave] = bad;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    if (ct) __syncthreads();  // the previous tile's merge has read the buffers
-    const float l = sum_xor32(sum_xor16(lsum[ct]));
+    if (ct) __syncthreads();  // the previous group's merge has read the buffers
+    if ((c >> 4) == ct) {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) sm_acc[wave][n][16 * nt + 4 * kg + rr] = o[ct][nt][rr];
-    if (kg == 0) {
-      sm_m[wave][n] = m[ct];
-      sm_l[wave][n] = l;
+        for (int i = 0; i < 16; ++i) sm_acc[wave][c & 15][32 * db + 8 * (i / 4) + 4 * h + i % 4] = o[db][i];
+      if (h == 0) {
+        sm_m[wave][c & 15] = m;
+        sm_l[wave][c & 15] = l;
+      }
     }
     __syncthreads();
     int any_bad = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) any_bad |= sm_bad[w];
     for (int idx = threadIdx.x; idx < 16 * HD; idx += 64 * NW) {
-      const int c = idx / HD, d = idx % HD;
-      const int row = r0 + 16 * ct + c;
+      const int col = idx / HD, d = idx % HD;
+      const int row = r0 + 16 * ct + col;
       if (row >= r_end) continue;
       float big_m = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][c]);
+      for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][col]);
       float lt = 0.f, acc = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float f = sm_m[w][c] == -INFINITY ? 0.f : fast_exp2(sm_m[w][c] - big_m);
-        lt = fmaf(f, sm_l[w][c], lt);
-        acc = fmaf(f, sm_acc[w][c][d], acc);
+        const float f = sm_m[w][col] == -INFINITY ? 0.f : fast_exp2(sm_m[w][col] - big_m);
+        lt = fmaf(f, sm_l[w][col], lt);
+        acc = fmaf(f, sm_acc[w][col][d], acc);
       }
       if (any_bad) {
         big_m = NAN;

@@ -237,6 +237,16 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=
     return out
 
 
+def paged_attn_multi_token_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, num_query_tokens, max_query_len,
+                                           max_context_len, partition_tokens=0, kernel="auto",
+                                           blocks_in_flight=0) -> int:
+    desc = pool_desc(k_pool, v_pool)
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, None)
+    return int(lib.pkv_paged_attn_multi_token_workspace_bytes(ctypes.byref(desc), num_seqs, num_heads,
+                                                              num_query_tokens, max_query_len, max_context_len,
+                                                              ctypes.byref(opts)))
+
+
 def paged_attn_multi_token(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, max_query_len,
                            out=None, max_context_len=None, workspace=None, partition_tokens=0, kernel="auto",
                            out_dtype=None, stream=None, blocks_in_flight=0):
