@@ -3,7 +3,7 @@
  *
  * The operations follow the pages' statement of the problem:
  *
- *  - The KV cache is split into fixed-size blocks (16 or 32 tokens) held in one
+ *  - The KV cache is split into fixed-size blocks (8, 16 or 32 tokens) held in one
  *    preallocated pool; each sequence has a block table mapping its logical
  *    blocks to physical ones, which need not be contiguous ("Master Paged
  *    Attention for LLM Inference", section "How Paged Attention Works: The
@@ -68,8 +68,13 @@ typedef enum {
   PKV_EHIP = 4            /* the HIP runtime reported an error at launch */
 } pkv_status;
 
-/* Shapes shared by both pools. Supported: block_size 16 or 32, head_dim 64 or
- * 128, dtype PKV_F32 or PKV_BF16, num_blocks*block_size < 2^31. */
+/* Shapes shared by both pools. Supported: block_size 8, 16 or 32, head_dim 64
+ * or 128, dtype PKV_F32 or PKV_BF16, num_blocks*block_size < 2^31.  Smaller
+ * blocks leave less of a sequence's last block unused but mean more table
+ * entries per token; larger ones the reverse ("PagedAttention Explained",
+ * "Best Practices", "Choose the Right Block Size").  The matrix-core kernels
+ * and the shared-prefix pass take blocks of 16 or 32 tokens; 8-token blocks
+ * run on the vector kernel. */
 typedef struct {
   int32_t num_blocks;
   int32_t num_kv_heads;
@@ -80,9 +85,9 @@ typedef struct {
 
 /* Decode kernel family. */
 typedef enum {
-  PKV_KERNEL_AUTO = 0,   /* MFMA for bf16 with 4 or 8 query heads per kv head, vector otherwise */
+  PKV_KERNEL_AUTO = 0,   /* MFMA for bf16, head_dim 128, blocks of 16/32 and 4 or 8 query heads per kv head; vector otherwise */
   PKV_KERNEL_VECTOR = 1, /* per-lane dot products with cross-lane reductions (any supported group) */
-  PKV_KERNEL_MFMA = 2    /* grouped query tile on matrix cores (bf16, head_dim 128, group 4 or 8) */
+  PKV_KERNEL_MFMA = 2    /* grouped query tile on matrix cores (bf16, head_dim 128, blocks of 16/32, group 4 or 8) */
 } pkv_kernel;
 
 /* Optional decode settings (pass NULL for defaults). */

@@ -33,8 +33,8 @@ pkv_status check_pool(const pkv_pool_desc* pool) {
   if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0 || pool->block_size <= 0 || pool->head_dim <= 0)
     return fail(PKV_EINVAL, "pool sizes must be positive");
   if (pool->dtype != PKV_F32 && pool->dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "dtype must be F32 or BF16");
-  if (pool->block_size != 16 && pool->block_size != 32)
-    return fail(PKV_EUNSUPPORTED, "block_size must be 16 or 32");
+  if (pool->block_size != 8 && pool->block_size != 16 && pool->block_size != 32)
+    return fail(PKV_EUNSUPPORTED, "block_size must be 8, 16 or 32");
   if (pool->head_dim != 64 && pool->head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
   if ((int64_t)pool->num_blocks * pool->block_size >= (int64_t(1) << 31))
     return fail(PKV_EINVAL, "num_blocks * block_size must stay below 2^31");
@@ -94,8 +94,8 @@ pkv_status plan_cascade(const pkv_pool_desc* pool, int32_t num_seqs, int32_t max
     return fail(PKV_EINVAL, "prefix plan: truncated");
   if (!opts->prefix_plan_dev) return fail(PKV_EINVAL, "prefix plan: device copy missing");
   if (groups == 0) return PKV_OK;
-  if (pool->dtype != PKV_BF16 || pool->head_dim != 128)
-    return fail(PKV_EUNSUPPORTED, "cascade decode needs bf16 pools with head_dim 128");
+  if (pool->dtype != PKV_BF16 || pool->head_dim != 128 || pool->block_size < 16)
+    return fail(PKV_EUNSUPPORTED, "cascade decode needs bf16 pools with head_dim 128 and blocks of 16 or 32 tokens");
   // every index the kernels take from the plan is checked here, once, on the host
   const int32_t* start = w + pkv::kPlanHeader;
   const int32_t* gw = start + num_seqs;

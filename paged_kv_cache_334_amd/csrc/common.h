@@ -71,6 +71,7 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each 16
+constexpr int kDppRor8 = 0x128;       // row_ror:8, lane i <-> i^8 within each 16
 
 __device__ __forceinline__ float row_sum16(float v) {
   v += dpp<kDppXor1>(v);
@@ -86,6 +87,15 @@ __device__ __forceinline__ float row_max16(float v) {
   v = fmaxf(v, dpp<kDppMirror>(v));
   return v;
 }
+// sum over each group of 8 lanes
+__device__ __forceinline__ float row_sum8(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  return v;
+}
+// v(lane) + v(lane ^ 8)
+__device__ __forceinline__ float sum_xor8(float v) { return v + dpp<kDppRor8>(v); }
 // v(lane) + v(lane ^ 16)
 __device__ __forceinline__ float sum_xor16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -19,7 +19,7 @@
 // has loads in flight.  Within a round:
 //  * key pass: lane = (token t = lane % BS, lane group grp = lane / BS); the
 //    lane loads 16-byte chunks grp, grp + 64/BS, ... of token t's key row
-//    (the 16 or 32 lanes of one chunk read BS*16 contiguous bytes of the key
+//    (the 8, 16 or 32 lanes of one chunk read BS*16 contiguous bytes of the key
 //    tile), multiplies with q in float32 (bf16 pairs through the dot2
 //    instruction, which returns a float32 sum), and the 64/BS lane groups are
 //    summed with xor shuffles;
@@ -179,11 +179,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
         }
         s += s2;
         // sum the lane groups of one token: lanes t, t+BS, ...
-        if constexpr (BS == 16) s = sum_xor32(sum_xor16(s));
+        if constexpr (BS == 8) s = sum_xor32(sum_xor16(sum_xor8(s)));
+        else if constexpr (BS == 16) s = sum_xor32(sum_xor16(s));
         else s = sum_xor32(s);
         s = (t < valid) ? s * a.scale_log2 : -INFINITY;
 
-        float mx = row_max16(s);
+        float mx = row_max16(s);  // with 8-token blocks lanes 8..15 repeat tokens 0..7
         if constexpr (BS == 32) mx = max_xor16(mx);
         mx = __builtin_amdgcn_readfirstlane(mx);  // the same in every lane
         if (mx > m[h] + kRescaleSlack) {
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
   // holds the same weights), and the RC lanes sharing a dim add their partial sums
 #pragma unroll
   for (int h = 0; h < R; ++h) {
-    float l = row_sum16(lsum[h]);
+    float l = BS == 8 ? row_sum8(lsum[h]) : row_sum16(lsum[h]);
     if constexpr (BS == 32) l = sum_xor16(l);
 #pragma unroll
     for (int c = 0; c < VC; ++c) {
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
 
 bool vector_supported(int bf16, int hd, int bs, int g) {
   (void)bf16;
-  return (hd == 64 || hd == 128) && (bs == 16 || bs == 32) && (g == 1 || g == 2 || g == 4 || g == 8);
+  return (hd == 64 || hd == 128) && (bs == 8 || bs == 16 || bs == 32) && (g == 1 || g == 2 || g == 4 || g == 8);
 }
 
 // sequence slots: one per sequence, or one per (sequence, new token) with several
@@ -269,6 +270,8 @@ static hipError_t dispatch_g(const DecodeArgs& a, int g, hipStream_t s) {
 
 template <bool BF16, int HP, int U>
 static hipError_t dispatch_shape(const DecodeArgs& a, int hd, int bs, int g, hipStream_t s) {
+  if (hd == 64 && bs == 8) return dispatch_g<BF16, 64, 8, HP, U>(a, g, s);
+  if (hd == 128 && bs == 8) return dispatch_g<BF16, 128, 8, HP, U>(a, g, s);
   if (hd == 64 && bs == 16) return dispatch_g<BF16, 64, 16, HP, U>(a, g, s);
   if (hd == 64 && bs == 32) return dispatch_g<BF16, 64, 32, HP, U>(a, g, s);
   if (hd == 128 && bs == 16) return dispatch_g<BF16, 128, 16, HP, U>(a, g, s);
@@ -282,7 +285,9 @@ template <bool BF16, int U>
 static hipError_t dispatch_pairs(const DecodeArgs& a, int hd, int bs, hipStream_t s) {
   const dim3 grid(a.num_parts, a.num_kv_heads / 2, seq_slots(a));
   const dim3 block(64 * kWaves);
-  if (hd == 64 && bs == 16) hipLaunchKernelGGL((decode_vector_kernel<BF16, 64, 16, 1, 2, U>), grid, block, 0, s, a);
+  if (hd == 64 && bs == 8) hipLaunchKernelGGL((decode_vector_kernel<BF16, 64, 8, 1, 2, U>), grid, block, 0, s, a);
+  else if (hd == 128 && bs == 8) hipLaunchKernelGGL((decode_vector_kernel<BF16, 128, 8, 1, 2, U>), grid, block, 0, s, a);
+  else if (hd == 64 && bs == 16) hipLaunchKernelGGL((decode_vector_kernel<BF16, 64, 16, 1, 2, U>), grid, block, 0, s, a);
   else if (hd == 64 && bs == 32) hipLaunchKernelGGL((decode_vector_kernel<BF16, 64, 32, 1, 2, U>), grid, block, 0, s, a);
   else if (hd == 128 && bs == 16) hipLaunchKernelGGL((decode_vector_kernel<BF16, 128, 16, 1, 2, U>), grid, block, 0, s, a);
   else if (hd == 128 && bs == 32) hipLaunchKernelGGL((decode_vector_kernel<BF16, 128, 32, 1, 2, U>), grid, block, 0, s, a);

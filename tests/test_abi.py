@@ -63,7 +63,7 @@ def _decode(ops, desc, num_heads=32, max_ctx=256, ptr=16, opts=None, out_dtype=N
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(block_size=8), 2),
+    (dict(block_size=4), 2),
     (dict(block_size=64), 2),
     (dict(head_dim=96), 2),
     (dict(dtype=7), 2),
@@ -237,3 +237,16 @@ def test_multi_token_workspace(ops):
     single = ops.DecodeOpts(1 << 30, 0, 0)
     assert ops.lib.pkv_paged_attn_multi_token_workspace_bytes(ctypes.byref(d), 4, 32, 12, 3, 256,
                                                               ctypes.byref(single)) == 0
+
+
+def test_block_size_8(ops):
+    """8-token blocks are accepted (vector kernel); the matrix-core kernel and
+    the shared-prefix pass refuse them."""
+    d = _desc(ops, block_size=8)
+    single = ops.DecodeOpts(1 << 30, 0, 0)
+    assert ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(single)) == 0
+    assert _decode(ops, d, opts=ops.DecodeOpts(1 << 30, 2, 0)) == 2
+    plan = (ctypes.c_int32 * 16)(0x504b5650, 4, 8, 1, 16, 2, 16, 16, 0, 0, 16, 0, 2, 0, 0, 1)
+    opts = ops.DecodeOpts(0, 0, 0, 0, ctypes.addressof(plan), 16, 16)
+    assert _decode(ops, d, opts=opts, max_blocks=32) == 2
+    assert "16 or 32" in ops.lib.pkv_last_error().decode()
