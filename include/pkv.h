@@ -65,7 +65,8 @@ typedef enum {
   PKV_EINVAL = 1,         /* bad pointer, size, shape or combination */
   PKV_EUNSUPPORTED = 2,   /* valid but not built: block_size, head_dim, group size, dtype */
   PKV_EWORKSPACE = 3,     /* workspace missing or smaller than required */
-  PKV_EHIP = 4            /* the HIP runtime reported an error at launch */
+  PKV_EHIP = 4,           /* the HIP runtime reported an error at launch */
+  PKV_ENOSPACE = 5        /* block manager: no free block left for the request (nothing changed) */
 } pkv_status;
 
 /* Shapes shared by both pools. Supported: block_size 8, 16 or 32, head_dim 64
@@ -264,6 +265,77 @@ pkv_status pkv_swap_blocks(const void* src_k, const void* src_v, const pkv_pool_
                            void* dst_v, const pkv_pool_desc* dst_pool, const int32_t* src_dst_pairs,
                            int32_t num_pairs, void* stream);
 
+/*
+ * Host-side block manager: the bookkeeping above the kernels.  It keeps the
+ * free list of physical blocks, each sequence's block table and length, and a
+ * reference count per block, and turns appends into slots
+ * (pkv_reshape_and_cache) and copy-on-write pairs (pkv_copy_blocks).
+ *
+ * Rules ("PagedAttention Explained", "Implementing a Simplified Paged KV
+ * Cache"): a sequence takes a new block from the front of the free list when
+ * its length is a multiple of block_size; its next token goes to row
+ * length % block_size of its last block (slot = block * block_size + row);
+ * freeing a sequence drops one reference from each of its blocks and returns
+ * blocks left with none to the back of the free list.  pkv_bm_fork makes a
+ * child that shares all of the parent's blocks; the first write of either into
+ * a shared, partly filled last block first moves the writer to a copy
+ * ("Master Paged Attention for LLM Inference", "How Paged Attention Works: The
+ * Mechanics", item 4), and the (source, destination) pair is queued for
+ * pkv_bm_take_copies.
+ *
+ * Prefix caching ("Paged Attention" glossary, "Why it matters";
+ * "PagedAttention Explained", "Enabling Automatic Prefix Caching"): when token
+ * ids are passed to pkv_bm_append_tokens, every block that fills up is entered
+ * in a cache under a hash of all token ids up to its end (64-bit, chained over
+ * blocks; a hit also compares the block's own ids and its parent's hash).
+ * pkv_bm_add_sequence_cached starts a sequence from a prompt and shares the
+ * longest run of cached full blocks at its start (never the block holding the
+ * prompt's last token).  A cached block whose last reference is dropped stays
+ * in the cache, on the free list, until it is taken for other contents.
+ *
+ * Host memory only, no HIP calls; one manager must not be used from two
+ * threads at once.  Sequence ids are any distinct int64 values.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+/* free_order: NULL (blocks 0..num_blocks-1) or a permutation giving the initial
+ * free-list order.  Returns NULL for bad arguments or no memory. */
+pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
+void pkv_bm_destroy(pkv_block_manager* bm);
+/* Message of the manager's last error ("" before any). */
+const char* pkv_bm_last_error(const pkv_block_manager* bm);
+int32_t pkv_bm_num_free(const pkv_block_manager* bm);
+/* References to a block (0 = free), -1 for an id outside the pool. */
+int32_t pkv_bm_ref_count(const pkv_block_manager* bm, int32_t block);
+/* Full blocks held in the prefix cache. */
+int32_t pkv_bm_num_cached(const pkv_block_manager* bm);
+pkv_status pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq);
+/* New sequence starting with the prompt tokens[0..num_tokens); shares cached
+ * full blocks and writes how many leading tokens they cover to *cached_tokens
+ * (a multiple of block_size, < num_tokens).  The caller appends the rest. */
+pkv_status pkv_bm_add_sequence_cached(pkv_block_manager* bm, int64_t seq, const int32_t* tokens, int32_t num_tokens,
+                                      int32_t* cached_tokens);
+pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
+/* Reserve slots for the next num_tokens tokens of seq: slots[0..num_tokens).
+ * token_ids may be NULL (the sequence's later blocks then enter no cache).
+ * PKV_ENOSPACE when the free list cannot cover the whole request; then nothing
+ * changes. */
+pkv_status pkv_bm_append_tokens(pkv_block_manager* bm, int64_t seq, int32_t num_tokens, const int32_t* token_ids,
+                                int32_t* slots);
+/* Copy-on-write pairs queued since the last call, as pairs[2i] = source,
+ * pairs[2i+1] = destination.  pairs NULL: returns the count and keeps them;
+ * else fills them (max_pairs must cover the count, else -1) and clears the queue. */
+int32_t pkv_bm_take_copies(pkv_block_manager* bm, int32_t* pairs, int32_t max_pairs);
+pkv_status pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq);
+/* Tokens of a sequence, -1 if unknown. */
+int32_t pkv_bm_sequence_length(const pkv_block_manager* bm, int64_t seq);
+/* Its blocks in logical order (table NULL: count only); -1 if unknown or max_blocks too small. */
+int32_t pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq, int32_t* table, int32_t max_blocks);
+/* Block tables [num_seqs][max_blocks_per_seq] (entries past a sequence's
+ * blocks set to pad) and context lengths [num_seqs] of the listed sequences,
+ * in host memory, ready to copy to the device for the attention calls (and to
+ * pass to pkv_plan_shared_prefix). */
+pkv_status pkv_bm_export_batch(pkv_block_manager* bm, const int64_t* seqs, int32_t num_seqs, int32_t max_blocks_per_seq,
+                               int32_t pad, int32_t* block_tables, int32_t* context_lens);
 /* Static text for a status code. */
 const char* pkv_status_string(pkv_status status);
 

@@ -558,6 +558,7 @@ const char* pkv_status_string(pkv_status status) {
     case PKV_EUNSUPPORTED: return "unsupported shape or type";
     case PKV_EWORKSPACE: return "workspace missing or too small";
     case PKV_EHIP: return "HIP runtime error";
+    case PKV_ENOSPACE: return "no free block";
   }
   return "unknown status";
 }

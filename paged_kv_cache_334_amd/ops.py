@@ -22,7 +22,7 @@ lib = ctypes.CDLL(_LIB_PATH)
 
 PKV_F32, PKV_BF16 = 0, 1
 KERNELS = {"auto": 0, "vector": 1, "mfma": 2}
-STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP"}
+STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP", 5: "PKV_ENOSPACE"}
 
 
 class PoolDesc(ctypes.Structure):
@@ -71,6 +71,27 @@ lib.pkv_swap_blocks.restype = _i32
 lib.pkv_swap_blocks.argtypes = [_vp, _vp, ctypes.POINTER(PoolDesc), _vp, _vp, ctypes.POINTER(PoolDesc), _vp, _i32, _vp]
 lib.pkv_plan_shared_prefix.restype = _sz
 lib.pkv_plan_shared_prefix.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz]
+_bm = ctypes.c_void_p
+_i32p = ctypes.POINTER(ctypes.c_int32)
+for _name, _res, _args in [
+    ("pkv_bm_create", _bm, [_i32, _i32, _vp]),
+    ("pkv_bm_destroy", None, [_bm]),
+    ("pkv_bm_last_error", ctypes.c_char_p, [_bm]),
+    ("pkv_bm_num_free", _i32, [_bm]),
+    ("pkv_bm_ref_count", _i32, [_bm, _i32]),
+    ("pkv_bm_num_cached", _i32, [_bm]),
+    ("pkv_bm_add_sequence", _i32, [_bm, _i64]),
+    ("pkv_bm_add_sequence_cached", _i32, [_bm, _i64, _vp, _i32, _i32p]),
+    ("pkv_bm_fork", _i32, [_bm, _i64, _i64]),
+    ("pkv_bm_append_tokens", _i32, [_bm, _i64, _i32, _vp, _vp]),
+    ("pkv_bm_take_copies", _i32, [_bm, _vp, _i32]),
+    ("pkv_bm_free_sequence", _i32, [_bm, _i64]),
+    ("pkv_bm_sequence_length", _i32, [_bm, _i64]),
+    ("pkv_bm_block_table", _i32, [_bm, _i64, _vp, _i32]),
+    ("pkv_bm_export_batch", _i32, [_bm, _vp, _i32, _i32, _i32, _vp, _vp]),
+]:
+    getattr(lib, _name).restype = _res
+    getattr(lib, _name).argtypes = _args
 lib.pkv_status_string.restype = ctypes.c_char_p
 lib.pkv_status_string.argtypes = [_i32]
 lib.pkv_last_error.restype = ctypes.c_char_p
@@ -369,3 +390,135 @@ def probe_copy(src, dst, num_workgroups, stream=None):
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("src and dst sizes differ")
     _probe_check(lib.pkv_probe_copy(_ptr(src), _ptr(dst), nbytes, num_workgroups, _stream(stream)), "pkv_probe_copy")
+
+
+class BlockManagerError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({detail})")
+        self.status = status
+
+
+class BlockManager:
+    """Native host block manager (pkv_bm_* in include/pkv.h): free list,
+    block tables, reference counts, copy-on-write and the prefix cache.  Host
+    memory only; sequence ids are Python ints."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        import numpy as np
+
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+        self._destroy = lib.pkv_bm_destroy  # kept: module globals may be gone when __del__ runs at exit
+        self._h = lib.pkv_bm_create(self.num_blocks, self.block_size, None if order is None else order.ctypes.data)
+        if not self._h:
+            raise ValueError("pkv_bm_create rejected its arguments")
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def _check(self, st, where):
+        if st != 0:
+            raise BlockManagerError(st, where, lib.pkv_bm_last_error(self._h).decode())
+
+    @property
+    def num_free(self) -> int:
+        return int(lib.pkv_bm_num_free(self._h))
+
+    @property
+    def num_cached(self) -> int:
+        return int(lib.pkv_bm_num_cached(self._h))
+
+    def ref_count(self, block: int) -> int:
+        return int(lib.pkv_bm_ref_count(self._h, int(block)))
+
+    def allocate_sequence(self, seq: int) -> None:
+        self._check(lib.pkv_bm_add_sequence(self._h, int(seq)), "pkv_bm_add_sequence")
+
+    def allocate_sequence_cached(self, seq: int, prompt_tokens) -> int:
+        """Start ``seq`` from a prompt, sharing cached full blocks; returns the
+        number of leading prompt tokens they cover."""
+        import numpy as np
+
+        toks = np.ascontiguousarray(np.asarray(prompt_tokens, dtype=np.int32))
+        cached = ctypes.c_int32(0)
+        self._check(lib.pkv_bm_add_sequence_cached(self._h, int(seq), toks.ctypes.data if toks.size else None,
+                                                   toks.size, ctypes.byref(cached)), "pkv_bm_add_sequence_cached")
+        return int(cached.value)
+
+    def fork(self, parent: int, child: int) -> None:
+        self._check(lib.pkv_bm_fork(self._h, int(parent), int(child)), "pkv_bm_fork")
+
+    def append_slots(self, seq: int, num_tokens: int = None, token_ids=None):
+        """Slots of the next tokens of ``seq`` (int32 array)."""
+        import numpy as np
+
+        ids = None
+        if token_ids is not None:
+            ids = np.ascontiguousarray(np.asarray(token_ids, dtype=np.int32))
+            num_tokens = ids.size if num_tokens is None else num_tokens
+            if ids.size != num_tokens:
+                raise ValueError("token_ids length differs from num_tokens")
+        slots = np.empty(int(num_tokens), dtype=np.int32)
+        self._check(lib.pkv_bm_append_tokens(self._h, int(seq), int(num_tokens),
+                                             None if ids is None or ids.size == 0 else ids.ctypes.data,
+                                             slots.ctypes.data if slots.size else None), "pkv_bm_append_tokens")
+        return slots
+
+    def append_slot(self, seq: int) -> int:
+        return int(self.append_slots(seq, 1)[0])
+
+    def take_copies(self):
+        """Queued copy-on-write pairs as an int32 array [P, 2] (clears the queue)."""
+        import numpy as np
+
+        n = int(lib.pkv_bm_take_copies(self._h, None, 0))
+        pairs = np.empty((n, 2), dtype=np.int32)
+        if n:
+            got = int(lib.pkv_bm_take_copies(self._h, pairs.ctypes.data, n))
+            if got != n:
+                raise RuntimeError("copy queue changed during take_copies")
+        else:
+            lib.pkv_bm_take_copies(self._h, pairs.ctypes.data, 0)
+        return pairs
+
+    def free_sequence(self, seq: int) -> None:
+        self._check(lib.pkv_bm_free_sequence(self._h, int(seq)), "pkv_bm_free_sequence")
+
+    def length(self, seq: int) -> int:
+        n = int(lib.pkv_bm_sequence_length(self._h, int(seq)))
+        if n < 0:
+            raise KeyError(seq)
+        return n
+
+    def block_table(self, seq: int):
+        import numpy as np
+
+        n = int(lib.pkv_bm_block_table(self._h, int(seq), None, 0))
+        if n < 0:
+            raise KeyError(seq)
+        out = np.empty(n, dtype=np.int32)
+        if n:
+            lib.pkv_bm_block_table(self._h, int(seq), out.ctypes.data, n)
+        return out
+
+    def export_batch(self, seqs, max_blocks_per_seq: int = None, pad: int = -1):
+        """(block_tables [B, max_blocks], context_lens [B]) int32 host arrays."""
+        import numpy as np
+
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        if max_blocks_per_seq is None:
+            max_blocks_per_seq = max([1] + [len(self.block_table(s)) for s in ids.tolist()])
+        tables = np.empty((ids.size, int(max_blocks_per_seq)), dtype=np.int32)
+        lens = np.empty(ids.size, dtype=np.int32)
+        self._check(lib.pkv_bm_export_batch(self._h, ids.ctypes.data if ids.size else None, ids.size,
+                                            int(max_blocks_per_seq), int(pad),
+                                            tables.ctypes.data if ids.size else None,
+                                            lens.ctypes.data if ids.size else None), "pkv_bm_export_batch")
+        return tables, lens
