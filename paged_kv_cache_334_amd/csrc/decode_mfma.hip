@@ -39,6 +39,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
   constexpr int HD = 128;
   constexpr int SUB = BS / 16;  // 16-token sub-tiles per block
   constexpr int TILE_BYTES = HD * BS * 2;
+  // With 32-token blocks a 128-byte line of the value tile holds 2 dims x 32
+  // tokens, and the block's two 16-token sub-tiles each read half of it: the
+  // second half must still be in cache, so those loads keep the default policy.
+  constexpr int VPOLICY = BS == 16 ? kCacheStream : kCacheDefault;
   static_assert(2 * G <= 16, "group too large for one 16-column tile");
   static_assert(64 % ((U + SUB - 1) / SUB) == 0, "a round must not straddle two id loads");
 
@@ -101,9 +105,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
       const auto kt = tile_rsrc(kbase + off, TILE_BYTES);
       const auto vt = tile_rsrc(vbase + off, TILE_BYTES);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) T[u].k[i] = bload16(kt, ((4 * i + kg) * BS + 16 * sub + n) * 16);
+      for (int i = 0; i < 4; ++i) T[u].k[i] = bload16<kCacheStream>(kt, ((4 * i + kg) * BS + 16 * sub + n) * 16);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) T[u].v[nt] = bload8(vt, ((16 * nt + n) * BS + 16 * sub + 4 * kg) * 2);
+      for (int nt = 0; nt < 8; ++nt) T[u].v[nt] = bload8<VPOLICY>(vt, ((16 * nt + n) * BS + 16 * sub + 4 * kg) * 2);
     }
   };
 

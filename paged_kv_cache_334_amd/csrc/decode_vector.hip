@@ -120,9 +120,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
 #pragma unroll
       for (int hp = 0; hp < HP; ++hp) {
 #pragma unroll
-        for (int c = 0; c < KC; ++c) T[u].k[hp][c] = bload16(kt, hp * TILE_BYTES + ((grp + GK * c) * BS + t) * 16);
+        for (int c = 0; c < KC; ++c) T[u].k[hp][c] = bload16<kCacheStream>(kt, hp * TILE_BYTES + ((grp + GK * c) * BS + t) * 16);
 #pragma unroll
-        for (int c = 0; c < VC; ++c) T[u].v[hp][c] = bload16(vt, hp * TILE_BYTES + (lane + 64 * c) * 16);
+        for (int c = 0; c < VC; ++c) T[u].v[hp][c] = bload16<kCacheStream>(vt, hp * TILE_BYTES + (lane + 64 * c) * 16);
       }
     }
   };

@@ -36,13 +36,18 @@
 
 namespace pkv {
 
-template <int BS, int G, int CT, int U>
+// POLICY: cache policy of the tile loads; streaming with one row tile per unit,
+// default when further row tiles read the same tiles again from L2.
+template <int BS, int G, int CT, int U, int POLICY>
 __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
   constexpr int NW = kWaves;
   constexpr int HD = 128;
   constexpr int SUB = BS / 16;  // 16-token sub-tiles per block
   constexpr int TILE_BYTES = HD * BS * 2;
   constexpr int R = 16 * CT;    // rows per workgroup
+  // the two 16-token sub-tiles of a 32-token block share the value tile's
+  // 128-byte lines: those loads keep the default policy
+  constexpr int VPOLICY = BS == 16 ? POLICY : kCacheDefault;
   static_assert(64 % ((U + SUB - 1) / SUB) == 0, "a round must not straddle two id loads");
 
   struct Tile {
@@ -157,10 +162,10 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
       const auto kt = tile_rsrc(kbase + off, TILE_BYTES);
       const auto vt = tile_rsrc(vbase + off, TILE_BYTES);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) T[u].k[i] = bload16(kt, ((4 * i + kg) * BS + 16 * sub + n) * 16);
+      for (int i = 0; i < 4; ++i) T[u].k[i] = bload16<POLICY>(kt, ((4 * i + kg) * BS + 16 * sub + n) * 16);
       // values: dim 32db + c, tokens 8h..8h+7 of the sub-tile (16 contiguous bytes of the dim-major tile)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) T[u].v[db] = bload16(vt, ((32 * db + c) * BS + 16 * sub + 8 * h) * 2);
+      for (int db = 0; db < 4; ++db) T[u].v[db] = bload16<VPOLICY>(vt, ((32 * db + c) * BS + 16 * sub + 8 * h) * 2);
     }
   };
 
@@ -322,14 +327,14 @@ bool multi_mfma_supported(int bf16, int hd, int bs, int g) {
   return bf16 && hd == 128 && (bs == 16 || bs == 32) && (g == 1 || g == 2 || g == 4 || g == 8);
 }
 
-template <int CT, int U>
+template <int CT, int U, int POLICY>
 static hipError_t launch_ct(const DecodeArgs& a, int bs, int g, hipStream_t s) {
   const int64_t units = (int64_t)a.num_parts * a.num_kv_heads * a.num_seqs;
   const int64_t wgs = (units + kXcds - 1) / kXcds * kXcds * a.row_tiles;
   if (wgs <= 0 || wgs > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs);
   const dim3 block(64 * kWaves);
-#define PKV_MULTI(BS, G) hipLaunchKernelGGL((multi_mfma_kernel<BS, G, CT, U>), grid, block, 0, s, a)
+#define PKV_MULTI(BS, G) hipLaunchKernelGGL((multi_mfma_kernel<BS, G, CT, U, POLICY>), grid, block, 0, s, a)
   if (bs == 16) {
     switch (g) {
       case 1: PKV_MULTI(16, 1); break;
@@ -355,8 +360,13 @@ static hipError_t launch_ct(const DecodeArgs& a, int bs, int g, hipStream_t s) {
 
 hipError_t launch_multi_mfma(const DecodeArgs& a, int bs, int g, int col_tiles, int inflight, hipStream_t s) {
   if (a.rows_per_tile != 16 * col_tiles) return hipErrorInvalidValue;
-  if (col_tiles == 1) return inflight == 2 ? launch_ct<1, 2>(a, bs, g, s) : launch_ct<1, 1>(a, bs, g, s);
-  if (col_tiles == 2 && inflight == 1) return launch_ct<2, 1>(a, bs, g, s);
+  const bool stream = a.row_tiles == 1;
+  if (col_tiles == 1 && inflight == 2)
+    return stream ? launch_ct<1, 2, kCacheStream>(a, bs, g, s) : launch_ct<1, 2, kCacheDefault>(a, bs, g, s);
+  if (col_tiles == 1 && inflight == 1)
+    return stream ? launch_ct<1, 1, kCacheStream>(a, bs, g, s) : launch_ct<1, 1, kCacheDefault>(a, bs, g, s);
+  if (col_tiles == 2 && inflight == 1)
+    return stream ? launch_ct<2, 1, kCacheStream>(a, bs, g, s) : launch_ct<2, 1, kCacheDefault>(a, bs, g, s);
   return hipErrorInvalidValue;
 }
 

