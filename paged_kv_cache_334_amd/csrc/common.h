@@ -56,6 +56,10 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 __device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src, 64); }
+// v of lane `src` (a constant) in every lane, through a scalar register
+__device__ __forceinline__ float readlane_f(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
 
 // Cross-lane reductions without LDS.  Within a row of 16 lanes: DPP quad
 // permutes (xor 1, xor 2), then the half-row and row mirrors, which pair each

@@ -196,9 +196,24 @@ __global__ __launch_bounds__(64 * kWaves) void decode_vector_kernel(DecodeArgs a
         }
         const float p = fast_exp2(s - m[h]);
         lsum[h] += p;
+        // weights of the lane's value tokens tk..tk+X-1; token k's weight sits in lane k
+        // (and k + BS, ...).  With one or two chunks per value row, scalar broadcasts
+        // and a per-lane select replace the LDS permutes.
         float pv[X];
+        if constexpr (RC == 1) {
 #pragma unroll
-        for (int e = 0; e < X; ++e) pv[e] = shfl(p, tk + e);
+          for (int e = 0; e < X; ++e) pv[e] = readlane_f(p, e);
+        } else if constexpr (RC == 2) {
+          const bool second = lane & 1;  // tk == X
+#pragma unroll
+          for (int e = 0; e < X; ++e) {
+            const float lo = readlane_f(p, e), hi = readlane_f(p, X + e);
+            pv[e] = second ? hi : lo;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < X; ++e) pv[e] = shfl(p, tk + e);
+        }
 #pragma unroll
         for (int c = 0; c < VC; ++c) {
           const uint32_t ws[4] = {T[u].v[hp][c].x, T[u].v[hp][c].y, T[u].v[hp][c].z, T[u].v[hp][c].w};
