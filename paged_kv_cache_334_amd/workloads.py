@@ -163,10 +163,14 @@ SPECS = {
 ORDER = ["tiny-f32", "mha-7b", "gqa-70b", "long-32k", "shared-prefix"]
 
 # Several new tokens per sequence: the 70B-shaped GQA batch verifying 4 tokens
-# per sequence (3 drafted + 1), as a speculative-decoding step does.
+# per sequence (3 drafted + 1), as a speculative-decoding step does; and 8
+# sequences each appending a 512-token chunk of their prompt (chunked prefill
+# over the paged cache).
 MULTI_SPECS = {
     "verify-gqa-70b": WorkloadSpec("verify-gqa-70b", BF16, 128, 64, 8, 128, 16, (512, 4096), seed=1006,
                                    query_len=4),
+    "prefill-gqa-70b": WorkloadSpec("prefill-gqa-70b", BF16, 8, 64, 8, 128, 16, (1024, 4096), seed=1007,
+                                    query_len=512),
 }
 
 

@@ -199,8 +199,10 @@ def test_full_multi_sampled(name):
     assert np.isfinite(out).all()
     desc, k_pool, v_pool = oracle_pools(wl)
     rng = np.random.default_rng(0)
-    seqs = sorted({int(np.argmax(wl.context_lens)), int(np.argmin(wl.context_lens))}
-                  | set(rng.integers(0, wl.spec.num_seqs, size=6).tolist()))
+    seqs = {int(np.argmax(wl.context_lens)), int(np.argmin(wl.context_lens))}
+    if wl.max_query_len <= 64:  # long chunks: the two extreme sequences keep the oracle within seconds
+        seqs |= set(rng.integers(0, wl.spec.num_seqs, size=6).tolist())
+    seqs = sorted(seqs)
     rows, q, tables, lens, starts = _sub_batch(wl, seqs)
     _say(f"[multi-full] oracle on {len(seqs)} sequences")
     ref = oracle.paged_attend_causal(q, k_pool, v_pool, desc, tables, lens, starts, wl.scale)
