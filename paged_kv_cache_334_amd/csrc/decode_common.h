@@ -235,7 +235,12 @@ __device__ __forceinline__ void pipelined_rounds(int rounds, Tile* ta, Tile* tb,
 // (logits in base 2).  A sequence inside one partition gets its output row
 // acc / l (rounded to nearest even for bf16); otherwise the partial (M, l, acc)
 // goes to the workspace for the split-K merge.  A bad block id anywhere in the
-// partition turns the row into NaN.
+// partition turns the row into NaN.  After a shared-prefix pass the chunk
+// partials of the prefix are folded in too, kPreBatch at a time: their loads
+// are issued together (one memory round trip per batch, not one per partial)
+// and the running maximum moves once per batch.
+constexpr int kPreBatch = 8;
+
 template <int G, int HD, int NW>
 __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const PartRange& r,
                                                       float (*sm_acc)[G][HD], float (*sm_m)[G], float (*sm_l)[G],
@@ -253,7 +258,6 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
     float big_m = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][h]);
-    for (int c = 0; c < pre; ++c) big_m = fmaxf(big_m, a.pre_m[pre_base + c]);
     float l = 0.f, acc = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -261,10 +265,32 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
       l = fmaf(f, sm_l[w][h], l);
       acc = fmaf(f, sm_acc[w][h][d], acc);
     }
-    for (int c = 0; c < pre; ++c) {
-      const float f = fast_exp2(a.pre_m[pre_base + c] - big_m);
-      l = fmaf(f, a.pre_l[pre_base + c], l);
-      acc = fmaf(f, a.pre_acc[(pre_base + c) * HD + d], acc);
+    for (int c0 = 0; c0 < pre; c0 += kPreBatch) {
+      // slots past the last partial are read in bounds (clamped) and dropped by a select
+      float pm[kPreBatch], pl[kPreBatch], pa[kPreBatch];
+#pragma unroll
+      for (int k = 0; k < kPreBatch; ++k) {
+        const int64_t s = pre_base + min(c0 + k, pre - 1);
+        pm[k] = a.pre_m[s];
+        pl[k] = a.pre_l[s];
+        pa[k] = a.pre_acc[s * HD + d];
+      }
+      float bm = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kPreBatch; ++k) bm = fmaxf(bm, c0 + k < pre ? pm[k] : -INFINITY);
+      if (bm > big_m) {  // move the reference once for the batch
+        const float f = big_m == -INFINITY ? 0.f : fast_exp2(big_m - bm);
+        l *= f;
+        acc *= f;
+        big_m = bm;
+      }
+#pragma unroll
+      for (int k = 0; k < kPreBatch; ++k) {
+        // a NaN partial (bad block id in the prefix) stays NaN through the exponent
+        const float f = c0 + k < pre ? fast_exp2(pm[k] - big_m) : 0.f;
+        l = fmaf(f, c0 + k < pre ? pl[k] : 0.f, l);
+        acc = fmaf(f, c0 + k < pre ? pa[k] : 0.f, acc);
+      }
     }
     if (any_bad) {
       big_m = NAN;
