@@ -201,3 +201,31 @@ def test_errors():
         bm.length(9)
     with pytest.raises(ops.BlockManagerError):
         bm.export_batch([0, 9], max_blocks_per_seq=4)
+
+
+def test_beam_search_batch_gives_one_group_per_request():
+    """Beam search over several requests: each request's beams are forks that
+    share its prompt blocks; after every beam appends its own tokens, the
+    exported batch holds one shared-prefix group per request, each with the
+    prompt's full blocks as its prefix."""
+    bs, beams = 16, 4
+    bm = ops.BlockManager(256, bs)
+    rng = np.random.default_rng(3)
+    prompts = {r: rng.integers(0, 32000, size=int(rng.integers(130, 300))) for r in range(3)}
+    seqs = []
+    for r, prompt in prompts.items():
+        root = 1000 * (r + 1)
+        bm.allocate_sequence(root)
+        bm.append_slots(root, token_ids=prompt)
+        for k in range(beams):
+            bm.fork(root, root + 1 + k)
+            seqs.append(root + 1 + k)
+        bm.free_sequence(root)
+    for s in seqs:
+        bm.append_slots(s, token_ids=rng.integers(0, 32000, size=5))
+    bm.take_copies()
+    tables, lens = bm.export_batch(seqs, pad=-1)
+    plan = ops.plan_shared_prefix(tables, lens, bs, min_group_seqs=beams, min_prefix_blocks=4, device=None)
+    assert plan.groups == len(prompts)
+    expect = [len(prompts[s // 1000 - 1]) // bs for s in seqs]
+    assert plan.prefix_blocks().tolist() == expect
