@@ -73,9 +73,10 @@ typedef enum {
  * or 128, dtype PKV_F32 or PKV_BF16, num_blocks*block_size < 2^31.  Smaller
  * blocks leave less of a sequence's last block unused but mean more table
  * entries per token; larger ones the reverse ("PagedAttention Explained",
- * "Best Practices", "Choose the Right Block Size").  The matrix-core kernels
- * and the shared-prefix pass take blocks of 16 or 32 tokens; 8-token blocks
- * run on the vector kernel. */
+ * "Best Practices", "Choose the Right Block Size").  The shared-prefix pass
+ * and the multi-token matrix-core kernel take blocks of 16 or 32 tokens (with
+ * 8-token blocks multi-token calls run on the vector kernel); the decode
+ * kernels take all three. */
 typedef struct {
   int32_t num_blocks;
   int32_t num_kv_heads;
@@ -86,9 +87,9 @@ typedef struct {
 
 /* Decode kernel family. */
 typedef enum {
-  PKV_KERNEL_AUTO = 0,   /* MFMA for bf16, head_dim 128, blocks of 16/32 and 4 or 8 query heads per kv head; vector otherwise */
+  PKV_KERNEL_AUTO = 0,   /* MFMA for bf16, head_dim 128 and 4 or 8 query heads per kv head; vector otherwise */
   PKV_KERNEL_VECTOR = 1, /* per-lane dot products with cross-lane reductions (any supported group) */
-  PKV_KERNEL_MFMA = 2    /* grouped query tile on matrix cores (bf16, head_dim 128, blocks of 16/32, group 4 or 8) */
+  PKV_KERNEL_MFMA = 2    /* grouped query tile on matrix cores (bf16, head_dim 128, group 4 or 8) */
 } pkv_kernel;
 
 /* Optional decode settings (pass NULL for defaults). */

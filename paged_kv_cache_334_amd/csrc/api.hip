@@ -155,6 +155,7 @@ pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_he
   const bool mfma_ok = pkv::mfma_supported(bf16, pool->head_dim, pool->block_size, g);
   if (kernel == PKV_KERNEL_MFMA && !mfma_ok)
     return fail(PKV_EUNSUPPORTED, "MFMA kernel needs bf16, head_dim 128 and 4 or 8 query heads per kv head");
+  // (blocks of 8, 16 or 32 tokens; 8-token blocks are walked in pairs)
   plan->mfma = (kernel == PKV_KERNEL_MFMA) || (kernel == PKV_KERNEL_AUTO && mfma_ok);
   if (!plan->mfma && !pkv::vector_supported(bf16, pool->head_dim, pool->block_size, g))
     return fail(PKV_EUNSUPPORTED, "query heads per kv head must be 1, 2, 4 or 8");
@@ -172,7 +173,9 @@ pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_he
   // matrix-core kernel: two 4 KiB-tile blocks in flight per wave (its registers
   // leave room), one for larger tiles and for the short suffixes after a shared
   // prefix; vector kernel: one (measured 1-2% faster than two at occupancy 4 vs 2)
-  plan->inflight = inflight ? inflight : ((plan->mfma && tile_bytes <= 4096 && !plan->cascade) ? 2 : 1);
+  // (8-token blocks: one pair in flight, the paired loads take the registers)
+  plan->inflight = inflight ? inflight
+                            : ((plan->mfma && tile_bytes <= 4096 && bs >= 16 && !plan->cascade) ? 2 : 1);
   const int hpw = opts ? opts->heads_per_workgroup : 0;
   if (hpw < 0 || hpw > 2) return fail(PKV_EINVAL, "heads_per_workgroup must be 0, 1 or 2");
   const bool pairs_ok = !plan->mfma && g == 1 && pool->num_kv_heads % 2 == 0;

@@ -160,20 +160,23 @@ __device__ __forceinline__ int wave_block_count(const PartRange& r, int wave) {
 // readlane; no tile load waits on a table lookup.
 struct WaveIds {
   const int32_t* row;  // table entry of the wave's first block
-  int limit;           // entries row[kWaves*i] with kWaves*i < limit lie inside the table row
+  int limit;           // entries row[stride*i] with stride*i < limit lie inside the table row
+  int stride;          // table entries between the wave's consecutive blocks
   int chunk;
   int ids;
 };
 
-// Ids of blocks first, first + kWaves, ... of sequence b's table row.  Entries
+// Ids of blocks first, first + stride, ... of sequence b's table row.  Entries
 // past the sequence's last block may be read (they are inside the row of
 // max_blocks entries) but never used.
-__device__ __forceinline__ WaveIds wave_ids_from(const DecodeArgs& a, int b, int first, int lane) {
+__device__ __forceinline__ WaveIds wave_ids_from(const DecodeArgs& a, int b, int first, int lane,
+                                                 int stride = kWaves) {
   WaveIds w;
   w.row = a.block_tables + (int64_t)b * a.max_blocks + first;
   w.limit = a.max_blocks - first;
+  w.stride = stride;
   w.chunk = 0;
-  w.ids = kWaves * lane < w.limit ? w.row[kWaves * lane] : 0;
+  w.ids = stride * lane < w.limit ? w.row[stride * lane] : 0;
   return w;
 }
 
@@ -198,7 +201,7 @@ __device__ __forceinline__ int wave_id_at(const DecodeArgs& a, WaveIds* w, int i
   const int c = i >> 6;
   if (c != w->chunk) {
     w->chunk = c;
-    const int idx = kWaves * (64 * c + lane);
+    const int idx = w->stride * (64 * c + lane);
     w->ids = idx < w->limit ? w->row[idx] : 0;
     *bad |= wave_ids_check(a, w, cnt, lane);
   }

@@ -28,7 +28,11 @@
 //
 // Memory side as in the vector kernel (block ids per 64 blocks, broadcast with
 // readlane; double-buffered rounds), with the 16-token sub-tile as the unit: a
-// round is U sub-tiles, i.e. U blocks of 16 tokens or U/2 blocks of 32.
+// round is U sub-tiles, i.e. U blocks of 16 tokens, U/2 blocks of 32, or U
+// pairs of consecutive 8-token blocks.  In a pair each lane's tokens lie in one
+// of the two blocks, so every operand load is issued against both tiles with
+// the other half's lanes given an out-of-range offset (the buffer load returns
+// zeros for them) and the two results are OR-ed.
 #include "decode_common.h"
 
 namespace pkv {
@@ -37,12 +41,14 @@ template <int BS, int G, int U>
 __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NW = kWaves;
   constexpr int HD = 128;
-  constexpr int SUB = BS / 16;  // 16-token sub-tiles per block
+  constexpr bool PAIR = BS == 8;           // a 16-token unit spans two blocks
+  constexpr int SUB = PAIR ? 1 : BS / 16;  // 16-token sub-tiles per block
   constexpr int TILE_BYTES = HD * BS * 2;
+  constexpr uint32_t kOutside = 0x40000000u;  // a buffer offset past every tile: the load returns zeros
   // With 32-token blocks a 128-byte line of the value tile holds 2 dims x 32
   // tokens, and the block's two 16-token sub-tiles each read half of it: the
   // second half must still be in cache, so those loads keep the default policy.
-  constexpr int VPOLICY = BS == 16 ? kCacheStream : kCacheDefault;
+  constexpr int VPOLICY = BS <= 16 ? kCacheStream : kCacheDefault;
   static_assert(2 * G <= 16, "group too large for one 16-column tile");
   static_assert(64 % ((U + SUB - 1) / SUB) == 0, "a round must not straddle two id loads");
 
@@ -67,7 +73,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
   const int hslot = n % G;
 
   const SeqPick seq = pick_sequence<BS>(a, sm_key, sm_pick);
-  WaveIds wids = wave_ids_begin(a, seq, wave, lane);
+  // pairs of 8-token blocks: the wave's pairs p = wave, wave + NW, ... hold
+  // blocks 2p and 2p + 1 of the partition, whose ids come from two strided streams
+  WaveIds wids, wids1{};
+  if constexpr (PAIR) {
+    const int first = seq.start + blockIdx.x * a.blocks_per_part + 2 * wave;
+    wids = wave_ids_from(a, seq.b, first, lane, 2 * NW);
+    wids1 = wave_ids_from(a, seq.b, first + 1, lane, 2 * NW);
+  } else {
+    wids = wave_ids_begin(a, seq, wave, lane);
+  }
   bf16x8 qb[4];
   {
     const uint16_t* qrow =
@@ -81,8 +96,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
 
   const PartRange r = part_range<BS>(a, seq);
   if (finish_if_empty<G, HD>(a, r)) return;
-  const int cnt = wave_block_count(r, wave);
+  int cnt, cnt1 = 0;  // the wave's blocks (or pairs), and its pairs whose second block exists
+  if constexpr (PAIR) {
+    const int nb = max(r.blk_hi - r.blk_lo, 0);
+    const int pairs = (nb + 1) / 2, full = nb / 2;
+    cnt = pairs > wave ? (pairs - wave + NW - 1) / NW : 0;
+    cnt1 = full > wave ? (full - wave + NW - 1) / NW : 0;
+  } else {
+    cnt = wave_block_count(r, wave);
+  }
   int bad = wave_ids_check(a, &wids, cnt, lane);
+  if constexpr (PAIR) bad |= wave_ids_check(a, &wids1, cnt1, lane);
 
   f32x4 o[8];
 #pragma unroll
@@ -100,14 +124,42 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int x = min(rnd * U + u, units - 1);
-      const int sub = x % SUB;
-      const int64_t off = (int64_t)wave_id_at(a, &wids, x / SUB, cnt, lane, &bad) * block_bytes;
-      const auto kt = tile_rsrc(kbase + off, TILE_BYTES);
-      const auto vt = tile_rsrc(vbase + off, TILE_BYTES);
+      if constexpr (PAIR) {
+        // a pair without a second block (the partition's last, odd one) reads the
+        // first block twice; those tokens lie past the partition and are masked
+        const int id0 = wave_id_at(a, &wids, x, cnt, lane, &bad);
+        const int id1 = x < cnt1 ? wave_id_at(a, &wids1, x, cnt1, lane, &bad) : id0;
+        const auto kt0 = tile_rsrc(kbase + (int64_t)id0 * block_bytes, TILE_BYTES);
+        const auto kt1 = tile_rsrc(kbase + (int64_t)id1 * block_bytes, TILE_BYTES);
+        const auto vt0 = tile_rsrc(vbase + (int64_t)id0 * block_bytes, TILE_BYTES);
+        const auto vt1 = tile_rsrc(vbase + (int64_t)id1 * block_bytes, TILE_BYTES);
+        // keys: token n of the unit is row n % 8 of block n / 8
 #pragma unroll
-      for (int i = 0; i < 4; ++i) T[u].k[i] = bload16<kCacheStream>(kt, ((4 * i + kg) * BS + 16 * sub + n) * 16);
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t off = ((4 * i + kg) * BS + (n & 7)) * 16;
+          const uint4 k0 = bload16<kCacheStream>(kt0, n < 8 ? off : kOutside);
+          const uint4 k1 = bload16<kCacheStream>(kt1, n < 8 ? kOutside : off);
+          T[u].k[i] = make_uint4(k0.x | k1.x, k0.y | k1.y, k0.z | k1.z, k0.w | k1.w);
+        }
+        // values: tokens 4kg..4kg+3 of the unit are rows 4(kg % 2).. of block kg / 2
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) T[u].v[nt] = bload8<VPOLICY>(vt, ((16 * nt + n) * BS + 16 * sub + 4 * kg) * 2);
+        for (int nt = 0; nt < 8; ++nt) {
+          const uint32_t off = ((16 * nt + n) * BS + 4 * (kg & 1)) * 2;
+          const uint2 v0 = bload8<VPOLICY>(vt0, kg < 2 ? off : kOutside);
+          const uint2 v1 = bload8<VPOLICY>(vt1, kg < 2 ? kOutside : off);
+          T[u].v[nt] = make_uint2(v0.x | v1.x, v0.y | v1.y);
+        }
+      } else {
+        const int sub = x % SUB;
+        const int64_t off = (int64_t)wave_id_at(a, &wids, x / SUB, cnt, lane, &bad) * block_bytes;
+        const auto kt = tile_rsrc(kbase + off, TILE_BYTES);
+        const auto vt = tile_rsrc(vbase + off, TILE_BYTES);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) T[u].k[i] = bload16<kCacheStream>(kt, ((4 * i + kg) * BS + 16 * sub + n) * 16);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+          T[u].v[nt] = bload8<VPOLICY>(vt, ((16 * nt + n) * BS + 16 * sub + 4 * kg) * 2);
+      }
     }
   };
 
@@ -116,8 +168,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
     for (int u = 0; u < U; ++u) {
       const int x = rnd * U + u;
       if (x >= units) break;
-      const int j = r.blk_lo + wave + NW * (x / SUB);  // logical block
-      const int valid = r.ctx - j * BS - 16 * (x % SUB);
+      // first token of the unit, and its rows inside the context and the partition
+      const int tok0 = PAIR ? (r.blk_lo + 2 * (wave + NW * x)) * BS
+                            : (r.blk_lo + wave + NW * (x / SUB)) * BS + 16 * (x % SUB);
+      const int valid = min(r.ctx, r.blk_hi * BS) - tok0;
       if (valid <= 0) continue;  // second half of a block past the context
 
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -196,14 +250,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
 }
 
 bool mfma_supported(int bf16, int hd, int bs, int g) {
-  return bf16 && hd == 128 && (bs == 16 || bs == 32) && (g == 4 || g == 8);
+  return bf16 && hd == 128 && (bs == 8 || bs == 16 || bs == 32) && (g == 4 || g == 8);
 }
 
 template <int U>
 static hipError_t launch_u(const DecodeArgs& a, int bs, int g, hipStream_t s) {
   const dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
   const dim3 block(64 * kWaves);
-  if (bs == 16 && g == 4) hipLaunchKernelGGL((decode_mfma_kernel<16, 4, U>), grid, block, 0, s, a);
+  if (bs == 8 && g == 4) hipLaunchKernelGGL((decode_mfma_kernel<8, 4, U>), grid, block, 0, s, a);
+  else if (bs == 8 && g == 8) hipLaunchKernelGGL((decode_mfma_kernel<8, 8, U>), grid, block, 0, s, a);
+  else if (bs == 16 && g == 4) hipLaunchKernelGGL((decode_mfma_kernel<16, 4, U>), grid, block, 0, s, a);
   else if (bs == 16 && g == 8) hipLaunchKernelGGL((decode_mfma_kernel<16, 8, U>), grid, block, 0, s, a);
   else if (bs == 32 && g == 4) hipLaunchKernelGGL((decode_mfma_kernel<32, 4, U>), grid, block, 0, s, a);
   else if (bs == 32 && g == 8) hipLaunchKernelGGL((decode_mfma_kernel<32, 8, U>), grid, block, 0, s, a);

@@ -49,6 +49,9 @@ SMALL = {
     # 8-token blocks: bf16 MHA, bf16 group 8, float32 head_dim 64 group 2
     "mha-bs8": lambda: generate("mha-7b", num_seqs=5, ctx=(1, 300), num_heads=4, num_kv_heads=4, block_size=8),
     "g8-bs8": lambda: generate("gqa-70b", num_seqs=4, ctx=(1, 400), num_heads=16, num_kv_heads=2, block_size=8),
+    # 8-token blocks, group 4, odd block counts split over partitions (pairs cut by a partition end)
+    "g4-bs8": lambda: generate("long-32k", num_seqs=3, ctx=(200, 700), num_heads=8, num_kv_heads=2, block_size=8,
+                               outlier_fraction=0.01),
     "f32-g2-bs8": lambda: generate(WorkloadSpec("f32-g2", "f32", 3, 4, 2, 64, 8, (1, 120), seed=8)),
 }
 
@@ -58,6 +61,7 @@ VARIANTS = [  # (kernel, partition tokens)
     ("vector", 64),
     ("mfma", 1 << 30),
     ("mfma", 96),
+    ("mfma", 40),  # odd partitions at 8-token blocks: a pair cut by the partition end
     ("auto", 32),
 ]
 
@@ -85,9 +89,8 @@ def test_small_cache_ops_bit_exact(small_case):
 def test_small_decode(small_case, kernel, ptoks, out_dtype):
     name, wl, gw, _, ref = small_case
     g = wl.spec.group
-    if kernel == "mfma" and not (wl.dtype == "bf16" and wl.spec.head_dim == 128 and g in (4, 8)
-                                 and wl.spec.block_size >= 16):
-        pytest.skip("MFMA kernel needs bf16, head_dim 128, blocks of 16/32, group 4 or 8")
+    if kernel == "mfma" and not (wl.dtype == "bf16" and wl.spec.head_dim == 128 and g in (4, 8)):
+        pytest.skip("MFMA kernel needs bf16, head_dim 128, group 4 or 8")
     if out_dtype == "f32" and wl.dtype == "f32":
         pytest.skip("same as 'same'")
     _say(f"[small] decode {name} kernel={kernel} partition={ptoks} out={out_dtype}")
