@@ -167,15 +167,14 @@ pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_he
     st = plan_cascade(pool, num_seqs, max_blocks_per_seq, g, opts, plan);
     if (st != PKV_OK) return st;
   }
-  const int tile_bytes = bs * pool->head_dim * elt_bytes(pool->dtype);
   const int inflight = opts ? opts->blocks_in_flight : 0;
   if (inflight < 0 || inflight > 2) return fail(PKV_EINVAL, "blocks_in_flight must be 0, 1 or 2");
-  // matrix-core kernel: two 4 KiB-tile blocks in flight per wave (its registers
-  // leave room), one for larger tiles and for the short suffixes after a shared
-  // prefix; vector kernel: one (measured 1-2% faster than two at occupancy 4 vs 2)
-  // (8-token blocks: one pair in flight, the paired loads take the registers)
-  plan->inflight = inflight ? inflight
-                            : ((plan->mfma && tile_bytes <= 4096 && bs >= 16 && !plan->cascade) ? 2 : 1);
+  // matrix-core kernel: two 16-token sub-tiles in flight per wave (its registers
+  // leave room; measured +3.5% on the 70B-shaped batch at 32-token blocks, equal
+  // on 8 x 32k), one for the short suffixes after a shared prefix and for pairs
+  // of 8-token blocks (their paired loads take the registers: -8% with two);
+  // vector kernel: one (measured 1-2% faster than two at occupancy 4 vs 2)
+  plan->inflight = inflight ? inflight : ((plan->mfma && bs >= 16 && !plan->cascade) ? 2 : 1);
   const int hpw = opts ? opts->heads_per_workgroup : 0;
   if (hpw < 0 || hpw > 2) return fail(PKV_EINVAL, "heads_per_workgroup must be 0, 1 or 2");
   const bool pairs_ok = !plan->mfma && g == 1 && pool->num_kv_heads % 2 == 0;
