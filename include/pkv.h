@@ -74,9 +74,8 @@ typedef enum {
  * blocks leave less of a sequence's last block unused but mean more table
  * entries per token; larger ones the reverse ("PagedAttention Explained",
  * "Best Practices", "Choose the Right Block Size").  The shared-prefix pass
- * and the multi-token matrix-core kernel take blocks of 16 or 32 tokens (with
- * 8-token blocks multi-token calls run on the vector kernel); the decode
- * kernels take all three. */
+ * takes blocks of 16 or 32 tokens; every other kernel takes all three (the
+ * matrix-core ones walk 8-token blocks in pairs). */
 typedef struct {
   int32_t num_blocks;
   int32_t num_kv_heads;

@@ -255,7 +255,9 @@ pkv_status make_multi_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t 
     plan->row_tiles = (int)((rows + plan->rows_per_tile - 1) / plan->rows_per_tile);
     if (plan->col_tiles == 2 && inflight == 2)
       return fail(PKV_EUNSUPPORTED, "row tiles of 32 take one block in flight");
-    plan->inflight = inflight ? inflight : (plan->col_tiles == 1 && tile_bytes <= 4096 ? 2 : 1);
+    // two blocks in flight for 16-row tiles of 16-token blocks; one otherwise (the
+    // 32-row accumulators, or the 8-token block pairs, take the registers)
+    plan->inflight = inflight ? inflight : (plan->col_tiles == 1 && pool->block_size == 16 && tile_bytes <= 4096 ? 2 : 1);
   } else {
     plan->rows_per_tile = g;
     plan->row_tiles = qmax;

@@ -148,6 +148,16 @@ __device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return make_uint2(v[0], v[1]);
 }
 
+// Loads through a per-lane address with the streaming (non-temporal) hint.
+__device__ __forceinline__ uint4 gload16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 gload8_stream(const void* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v[0], v[1]);
+}
+
 // Load 16 bytes (one layout chunk).
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 // Load 8 bytes.

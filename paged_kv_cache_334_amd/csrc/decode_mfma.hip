@@ -30,9 +30,8 @@
 // readlane; double-buffered rounds), with the 16-token sub-tile as the unit: a
 // round is U sub-tiles, i.e. U blocks of 16 tokens, U/2 blocks of 32, or U
 // pairs of consecutive 8-token blocks.  In a pair each lane's tokens lie in one
-// of the two blocks, so every operand load is issued against both tiles with
-// the other half's lanes given an out-of-range offset (the buffer load returns
-// zeros for them) and the two results are OR-ed.
+// of the two blocks: the lane picks its block's tile base and loads through a
+// per-lane address (one streaming global load per operand).
 #include "decode_common.h"
 
 namespace pkv {
@@ -44,7 +43,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
   constexpr bool PAIR = BS == 8;           // a 16-token unit spans two blocks
   constexpr int SUB = PAIR ? 1 : BS / 16;  // 16-token sub-tiles per block
   constexpr int TILE_BYTES = HD * BS * 2;
-  constexpr uint32_t kOutside = 0x40000000u;  // a buffer offset past every tile: the load returns zeros
   // With 32-token blocks a 128-byte line of the value tile holds 2 dims x 32
   // tokens, and the block's two 16-token sub-tiles each read half of it: the
   // second half must still be in cache, so those loads keep the default policy.
@@ -127,28 +125,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
       if constexpr (PAIR) {
         // a pair without a second block (the partition's last, odd one) reads the
         // first block twice; those tokens lie past the partition and are masked
+        // (ids are checked against the pool, so every address below lies inside it)
         const int id0 = wave_id_at(a, &wids, x, cnt, lane, &bad);
         const int id1 = x < cnt1 ? wave_id_at(a, &wids1, x, cnt1, lane, &bad) : id0;
-        const auto kt0 = tile_rsrc(kbase + (int64_t)id0 * block_bytes, TILE_BYTES);
-        const auto kt1 = tile_rsrc(kbase + (int64_t)id1 * block_bytes, TILE_BYTES);
-        const auto vt0 = tile_rsrc(vbase + (int64_t)id0 * block_bytes, TILE_BYTES);
-        const auto vt1 = tile_rsrc(vbase + (int64_t)id1 * block_bytes, TILE_BYTES);
         // keys: token n of the unit is row n % 8 of block n / 8
+        const char* kt = kbase + (int64_t)(n < 8 ? id0 : id1) * block_bytes;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t off = ((4 * i + kg) * BS + (n & 7)) * 16;
-          const uint4 k0 = bload16<kCacheStream>(kt0, n < 8 ? off : kOutside);
-          const uint4 k1 = bload16<kCacheStream>(kt1, n < 8 ? kOutside : off);
-          T[u].k[i] = make_uint4(k0.x | k1.x, k0.y | k1.y, k0.z | k1.z, k0.w | k1.w);
-        }
+        for (int i = 0; i < 4; ++i)
+          T[u].k[i] = gload16_stream(kt + ((4 * i + kg) * BS + (n & 7)) * 16);
         // values: tokens 4kg..4kg+3 of the unit are rows 4(kg % 2).. of block kg / 2
+        const char* vt = vbase + (int64_t)(kg < 2 ? id0 : id1) * block_bytes;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const uint32_t off = ((16 * nt + n) * BS + 4 * (kg & 1)) * 2;
-          const uint2 v0 = bload8<VPOLICY>(vt0, kg < 2 ? off : kOutside);
-          const uint2 v1 = bload8<VPOLICY>(vt1, kg < 2 ? kOutside : off);
-          T[u].v[nt] = make_uint2(v0.x | v1.x, v0.y | v1.y);
-        }
+        for (int nt = 0; nt < 8; ++nt) T[u].v[nt] = gload8_stream(vt + ((16 * nt + n) * BS + 4 * (kg & 1)) * 2);
       } else {
         const int sub = x % SUB;
         const int64_t off = (int64_t)wave_id_at(a, &wids, x / SUB, cnt, lane, &bad) * block_bytes;

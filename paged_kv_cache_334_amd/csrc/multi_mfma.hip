@@ -42,12 +42,13 @@ template <int BS, int G, int CT, int U, int POLICY>
 __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
   constexpr int NW = kWaves;
   constexpr int HD = 128;
-  constexpr int SUB = BS / 16;  // 16-token sub-tiles per block
+  constexpr bool PAIR = BS == 8;           // a 16-token unit spans two blocks, each lane loading from its own
+  constexpr int SUB = PAIR ? 1 : BS / 16;  // 16-token sub-tiles per block
   constexpr int TILE_BYTES = HD * BS * 2;
   constexpr int R = 16 * CT;    // rows per workgroup
   // the two 16-token sub-tiles of a 32-token block share the value tile's
   // 128-byte lines: those loads keep the default policy
-  constexpr int VPOLICY = BS == 16 ? POLICY : kCacheDefault;
+  constexpr int VPOLICY = BS <= 16 ? POLICY : kCacheDefault;
   static_assert(64 % ((U + SUB - 1) / SUB) == 0, "a round must not straddle two id loads");
 
   struct Tile {
@@ -134,10 +135,18 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
   const int lim = my_row < r_end ? base + my_row / G : 0;  // tokens the lane's row sees
   const bool lo_col = CT == 1 && c >= 16;                   // one column tile: columns 16..31 take the lo parts
 
+  // the wave's blocks w, w + NW, ...; with 8-token blocks its pairs p = w, w + NW, ...
+  // (blocks 2p and 2p + 1, ids from two strided streams; cnt1 = pairs with a second block)
   const int nb_part = blk_hi - blk_lo;
-  const int cnt = nb_part > wave ? (nb_part - wave + NW - 1) / NW : 0;  // blocks of this wave
-  WaveIds wids = wave_ids_from(a, b, blk_lo + wave, lane);
+  const int nunits = PAIR ? (nb_part + 1) / 2 : nb_part;
+  const int nfull = nb_part / 2;
+  const int cnt = nunits > wave ? (nunits - wave + NW - 1) / NW : 0;
+  const int cnt1 = PAIR && nfull > wave ? (nfull - wave + NW - 1) / NW : 0;
+  WaveIds wids = wave_ids_from(a, b, blk_lo + (PAIR ? 2 : 1) * wave, lane, (PAIR ? 2 : 1) * NW);
+  WaveIds wids1{};
+  if constexpr (PAIR) wids1 = wave_ids_from(a, b, blk_lo + 2 * wave + 1, lane, 2 * NW);
   int bad = wave_ids_check(a, &wids, cnt, lane);
+  if constexpr (PAIR) bad |= wave_ids_check(a, &wids1, cnt1, lane);
 
   f32x16 o[4];  // O^T, 32 dims per instruction: lane holds column c, dims 32db + 8(i/4) + 4h + i%4
 #pragma unroll
@@ -157,15 +166,35 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int x = min(rnd * U + u, units - 1);
-      const int sub = x % SUB;
-      const int64_t off = (int64_t)wave_id_at(a, &wids, x / SUB, cnt, lane, &bad) * block_bytes;
-      const auto kt = tile_rsrc(kbase + off, TILE_BYTES);
-      const auto vt = tile_rsrc(vbase + off, TILE_BYTES);
+      if constexpr (PAIR) {
+        // a pair without a second block reads the first twice (those tokens lie past
+        // the partition and are masked); ids are checked, so every address is in the pool
+        const int id0 = wave_id_at(a, &wids, x, cnt, lane, &bad);
+        const int id1 = x < cnt1 ? wave_id_at(a, &wids1, x, cnt1, lane, &bad) : id0;
+        const char* kt = kbase + (int64_t)(n < 8 ? id0 : id1) * block_bytes;  // token n: row n % 8 of block n / 8
+        const char* vt = vbase + (int64_t)(h == 0 ? id0 : id1) * block_bytes;  // tokens 8h..8h+7: all of block h
 #pragma unroll
-      for (int i = 0; i < 4; ++i) T[u].k[i] = bload16<POLICY>(kt, ((4 * i + kg) * BS + 16 * sub + n) * 16);
-      // values: dim 32db + c, tokens 8h..8h+7 of the sub-tile (16 contiguous bytes of the dim-major tile)
+        for (int i = 0; i < 4; ++i) {
+          const char* p = kt + ((4 * i + kg) * BS + (n & 7)) * 16;
+          T[u].k[i] = POLICY == kCacheStream ? gload16_stream(p) : load16(p);
+        }
 #pragma unroll
-      for (int db = 0; db < 4; ++db) T[u].v[db] = bload16<VPOLICY>(vt, ((32 * db + c) * BS + 16 * sub + 8 * h) * 2);
+        for (int db = 0; db < 4; ++db) {
+          const char* p = vt + (32 * db + c) * BS * 2;
+          T[u].v[db] = POLICY == kCacheStream ? gload16_stream(p) : load16(p);
+        }
+      } else {
+        const int sub = x % SUB;
+        const int64_t off = (int64_t)wave_id_at(a, &wids, x / SUB, cnt, lane, &bad) * block_bytes;
+        const auto kt = tile_rsrc(kbase + off, TILE_BYTES);
+        const auto vt = tile_rsrc(vbase + off, TILE_BYTES);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) T[u].k[i] = bload16<POLICY>(kt, ((4 * i + kg) * BS + 16 * sub + n) * 16);
+        // values: dim 32db + c, tokens 8h..8h+7 of the sub-tile (16 contiguous bytes of the dim-major tile)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          T[u].v[db] = bload16<VPOLICY>(vt, ((32 * db + c) * BS + 16 * sub + 8 * h) * 2);
+      }
     }
   };
 
@@ -174,9 +203,9 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
     for (int u = 0; u < U; ++u) {
       const int x = rnd * U + u;
       if (x >= units) break;
-      const int j = blk_lo + wave + NW * (x / SUB);  // logical block
-      const int tok0 = j * BS + 16 * (x % SUB);      // first token of the sub-tile
-      const int valid = ctx - tok0;
+      // first token of the unit, and its rows inside the walk and the partition
+      const int tok0 = PAIR ? (blk_lo + 2 * (wave + NW * x)) * BS : (blk_lo + wave + NW * (x / SUB)) * BS + 16 * (x % SUB);
+      const int valid = min(ctx, blk_hi * BS) - tok0;
       if (valid <= 0) continue;  // second half of a block past the walk
 
       f32x4 s[CT];
@@ -324,7 +353,7 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
 }
 
 bool multi_mfma_supported(int bf16, int hd, int bs, int g) {
-  return bf16 && hd == 128 && (bs == 16 || bs == 32) && (g == 1 || g == 2 || g == 4 || g == 8);
+  return bf16 && hd == 128 && (bs == 8 || bs == 16 || bs == 32) && (g == 1 || g == 2 || g == 4 || g == 8);
 }
 
 template <int CT, int U, int POLICY>
@@ -335,7 +364,15 @@ static hipError_t launch_ct(const DecodeArgs& a, int bs, int g, hipStream_t s) {
   const dim3 grid((unsigned)wgs);
   const dim3 block(64 * kWaves);
 #define PKV_MULTI(BS, G) hipLaunchKernelGGL((multi_mfma_kernel<BS, G, CT, U, POLICY>), grid, block, 0, s, a)
-  if (bs == 16) {
+  if (bs == 8) {
+    switch (g) {
+      case 1: PKV_MULTI(8, 1); break;
+      case 2: PKV_MULTI(8, 2); break;
+      case 4: PKV_MULTI(8, 4); break;
+      case 8: PKV_MULTI(8, 8); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (bs == 16) {
     switch (g) {
       case 1: PKV_MULTI(16, 1); break;
       case 2: PKV_MULTI(16, 2); break;

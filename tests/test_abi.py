@@ -240,15 +240,16 @@ def test_multi_token_workspace(ops):
 
 
 def test_block_size_8(ops):
-    """8-token blocks are accepted by the decode kernels (the matrix-core one
-    walks them in pairs); the multi-token matrix-core kernel and the
-    shared-prefix pass refuse them."""
+    """8-token blocks are accepted by the decode and multi-token kernels (the
+    matrix-core ones walk them in pairs); the shared-prefix pass refuses them."""
     d = _desc(ops, block_size=8)
     single = ops.DecodeOpts(1 << 30, 0, 0)
     assert ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(single)) == 0
     # an explicit matrix-core request plans (a split makes the workspace nonzero)
     assert ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(ops.DecodeOpts(64, 2, 0))) > 0
-    assert _multi(ops, d, max_ctx=128, opts=ops.DecodeOpts(1 << 30, 2, 0)) == 2
+    need = ops.lib.pkv_paged_attn_multi_token_workspace_bytes(ctypes.byref(d), 4, 32, 12, 3, 256,
+                                                              ctypes.byref(ops.DecodeOpts(64, 2, 0)))
+    assert need > 0
     plan = (ctypes.c_int32 * 16)(0x504b5650, 4, 8, 1, 16, 2, 16, 16, 0, 0, 16, 0, 2, 0, 0, 1)
     opts = ops.DecodeOpts(0, 0, 0, 0, ctypes.addressof(plan), 16, 16)
     assert _decode(ops, d, opts=opts, max_blocks=32) == 2

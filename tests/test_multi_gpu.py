@@ -37,9 +37,12 @@ SMALL = {
                                                  query_len=(1, 5))),
     # whole prompts as one chunk: up to 130 tokens x group 4 = 520 rows, 17 row tiles
     "prompt": lambda: generate("gqa-70b", num_seqs=2, ctx=(40, 130), num_heads=8, num_kv_heads=2, query_len=512),
-    # 8-token blocks (vector kernel), group 4, up to 6 new tokens
+    # 8-token blocks (block pairs on the matrix-core kernel), group 4, up to 6 new tokens
     "g4-bs8": lambda: generate("gqa-70b", num_seqs=3, ctx=(1, 250), num_heads=8, num_kv_heads=2, block_size=8,
                                query_len=(1, 6)),
+    # 8-token blocks, group 8, up to 5 new tokens: 32-row tiles over block pairs
+    "g8-bs8": lambda: generate("gqa-70b", num_seqs=4, ctx=(1, 300), num_heads=16, num_kv_heads=2, block_size=8,
+                               query_len=(1, 5)),
     # shared prefix with copy-on-write at the first new token
     "prefix-cow": lambda: generate("shared-prefix", num_seqs=8, shared_prefix=256, ctx=(16, 100), num_heads=8,
                                    num_kv_heads=2, cow_fraction=0.25, query_len=(1, 4)),
@@ -56,7 +59,7 @@ VARIANTS = [  # (kernel, partition tokens, blocks in flight)
 
 
 def _mfma_ok(wl):
-    return wl.dtype == "bf16" and wl.spec.head_dim == 128 and wl.spec.block_size >= 16
+    return wl.dtype == "bf16" and wl.spec.head_dim == 128
 
 
 @pytest.fixture(scope="module", params=sorted(SMALL))
