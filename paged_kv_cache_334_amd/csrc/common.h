@@ -119,6 +119,20 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// NaN-propagating maximum (v_maximum3_f32 on gfx950).  fmaxf must quiet a
+// signalling NaN input first, which costs one extra instruction per operand
+// that the compiler cannot prove canonical (every matrix-core result); where
+// no input may be NaN except through the data itself, this form is cheaper.
+__device__ __forceinline__ float maxp(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float maxp_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return maxp(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float maxp_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return maxp(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Buffer resource over one tile whose base is wave-uniform (kept in scalar
 // registers): the per-lane offsets stay the same 32-bit values for every tile,
 // and a load past `bytes` returns zeros instead of leaving the tile.

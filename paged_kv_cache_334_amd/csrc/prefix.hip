@@ -15,19 +15,24 @@
 // Workgroup = 4 waves x 32 query rows (two 16-column MFMA tiles per wave).
 // Per iteration 64 prefix tokens: the next iteration's key and value tiles
 // travel from memory straight into the other LDS buffer (global_load_lds)
-// while the current one is computed (two buffers, one barrier per iteration).  The LDS copy keeps the pool's
-// tile layout (keys chunk-major, values dim-major) except that a 32-token
-// value tile is split into two 16-token halves and value rows are swizzled
-// (value_offset), so the matrix-core operand reads below are conflict-free
-// for both block sizes:
-//  * S^T = K . Q^T, v_mfma_f32_16x16x32_bf16: A = keys (lane: token n, lane
-//    group kg -> 16-byte chunk 4i+kg), B = queries (lane: column n, dims
-//    32i+8kg..+7); lane gets S^T[token 4kg+r][column n].
-//  * O^T += V^T . P^T over 32 tokens (two sub-tiles), v_mfma_f32_16x16x32_bf16:
-//    the contraction index k = 8kg + j stands for token 4kg + j of the first
-//    sub-tile (j < 4) or of the second, so B = the lane's own 8 weights and
-//    A = values of dim 16nt+n at those tokens (two 8-byte reads).  Weights go
-//    in as bf16 hi + lo parts (two instructions), keeping ~16 significant bits.
+// while the current one is computed (two buffers, one barrier per iteration).
+// An iteration is two runs of 32 tokens (two 16-token blocks or one 32-token
+// block).  Each run's logits come from two S tiles whose 16 rows interleave:
+// tile X holds tokens 8j + 4X + r (j, r < 4), so after the product the lane of
+// group kg owns tokens 8kg..8kg+7 of the run across the two tiles, exactly the
+// 8 contraction indices it supplies to P.V, and the value operand is one
+// 16-byte piece of a dim's row.
+//  * S^T = K . Q^T, v_mfma_f32_16x16x32_bf16: A = keys (lane: the tile's row
+//    n, lane group kg -> 16-byte chunk 4i+kg), B = queries (lane: column n,
+//    dims 32i+8kg..+7); lane gets S^T[row 4kg+r][column n].
+//  * O^T += V^T . P^T over the run, v_mfma_f32_16x16x32_bf16: k = 8kg + j is
+//    token 8kg + j, B = the lane's own 8 weights, A = values of dim 16nt+n at
+//    those tokens.  Weights go in as bf16 hi + lo parts (two instructions),
+//    keeping ~16 significant bits.
+// The LDS copy permutes 16-byte pieces so that both operand reads are free of
+// bank conflicts (measured with the hardware counter): within a key chunk row
+// the tokens of one S tile sit in 16 consecutive slots (key_slot_token), and a
+// 32-token value row has its four pieces rotated by bits 1-2 of the dim.
 #include "decode_common.h"
 
 namespace pkv {
@@ -60,17 +65,24 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds, const void* gbase, uint3
 }
 __device__ __forceinline__ void lds_dma_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Byte offset, inside a 16-token value tile in LDS, of dim d's 8-byte piece kg
-// (tokens 4kg..4kg+3).  Rows are 32 bytes; dims with bit 3 set have their two
-// 16-byte halves swapped, so the 32 lanes of one half-wave (16 dims, two
-// pieces each) hit all 64 banks once instead of dims d and d+8 sharing banks.
-__device__ __forceinline__ int value_offset(int d, int kg) { return d * 32 + ((kg ^ (((d >> 3) & 1) << 1)) * 8); }
+// Token (inside its block) whose key piece sits in slot s of an LDS key chunk
+// row.  32-token blocks: slots 0-15 hold S tile 0's rows in order, 16-31 tile
+// 1's.  16-token blocks (b = the block's place in its run): the first block
+// keeps tile 0's tokens in slots 0-7 and tile 1's in 8-15, the second block the
+// other way round, so one tile's read covers both halves of the row's banks.
+template <int BS>
+__device__ __forceinline__ int key_slot_token(int s, int b) {
+  if constexpr (BS == 32) return 8 * ((s >> 2) & 3) + 4 * (s >> 4) + (s & 3);
+  else return 8 * ((s >> 2) & 1) + 4 * (((s >> 3) & 1) ^ b) + (s & 3);
+}
+// Piece of a 32-token value row stored at slot s of dim d (and the inverse).
+__device__ __forceinline__ int value_rot(int d) { return (d >> 1) & 3; }
 
 template <int BS, int G>
 __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   constexpr int NB = TOK / BS;          // blocks per iteration
   constexpr int TILE = BS * HD * 2;     // bytes of one (block, kv head) tile
-  constexpr int SUBB = BS / 16;         // 16-token sub-tiles per block
+  constexpr int RUN_BYTES = 32 * HD * 2; // one 32-token run of keys (or values)
   static_assert(NB * TILE == STAGE_HALF, "stage size");
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][STAGE_HALF];  // [buffer][K=0/V=1]
@@ -166,15 +178,14 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       const int kb = piece * 1024 / TILE;
       const int in_tile = piece * 1024 % TILE;
       const int64_t base = (int64_t)__builtin_amdgcn_readlane(ids, first + kb - id_base) * block_bytes;
-      // keys: the LDS copy keeps the tile's byte order
-      lds_dma16(lds_addr(&lds[buf][0][piece * 1024]), kpool + base, in_tile + lane * 16);
-      // values: LDS position in_tile + 16*lane of a [half][D][16] tile with
-      // swizzled rows -> dim d, 8-token slot q8 of the pool's [D][BS] tile
-      const int half = in_tile / (HD * 32);
-      const int pos = in_tile % (HD * 32) + lane * 16;
-      const int d = pos / 32;
-      const int q8 = 2 * half + (((pos / 16) % 2) ^ ((d >> 3) & 1));
-      lds_dma16(lds_addr(&lds[buf][1][piece * 1024]), vpool + base, d * (BS * 2) + q8 * 16);
+      const int q = in_tile / 16 + lane;  // 16-byte piece of the tile that this lane's LDS spot holds
+      // keys: chunk q / BS, slot q % BS <- that chunk's key_slot_token
+      lds_dma16(lds_addr(&lds[buf][0][piece * 1024]), kpool + base,
+                ((q / BS) * BS + key_slot_token<BS>(q % BS, kb & 1)) * 16);
+      // values: 16-token rows keep the pool's order; 32-token rows are rotated
+      const int d = q / (BS / 8);
+      const int vpiece = BS == 32 ? ((q & 3) ^ value_rot(d)) : (q & 1);
+      lds_dma16(lds_addr(&lds[buf][1][piece * 1024]), vpool + base, d * (BS * 2) + vpiece * 16);
     }
   };
 
@@ -191,14 +202,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // P.V (matrix cores).  The second pair's S^T runs while the first pair's
   // weights are computed, and the first pair's P.V while the second's are.
   auto compute = [&](int buf) {
-    f32x4 s[4][2];  // [sub-tile][column tile]
+    f32x4 s[4][2];  // [run * 2 + S tile][column tile]
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      const unsigned char* kt = &lds[buf][0][(sub / SUBB) * TILE];
-      const int ts = (sub % SUBB) * 16;
+      const unsigned char* kt = &lds[buf][0][(sub >> 1) * RUN_BYTES];
+      const int x = sub & 1;
+      // the lane's row n of tile x: 32-token blocks slot 16x + n; 16-token blocks
+      // block n / 8 of the run, slot n % 8 + 8 (x ^ block)
+      const int koff = BS == 32 ? 16 * x + n : (n >> 3) * (TILE / 16) + (n & 7) + 8 * (x ^ (n >> 3));
       bf16x8 ka[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kt + ((4 * i + kg) * BS + ts + n) * 16);
+      for (int i = 0; i < 4; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kt + ((4 * i + kg) * BS + koff) * 16);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -215,14 +229,14 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       float mx[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const float a = fmaxf(fmaxf(fmaxf(s0[ct][0], s0[ct][1]), fmaxf(s0[ct][2], s0[ct][3])),
-                              fmaxf(fmaxf(s1[ct][0], s1[ct][1]), fmaxf(s1[ct][2], s1[ct][3])));
-        mx[ct] = max_xor32(max_xor16(a)) * p.scale_log2;
+        const float a = maxp(maxp(maxp(s0[ct][0], s0[ct][1]), maxp(s0[ct][2], s0[ct][3])),
+                             maxp(maxp(s1[ct][0], s1[ct][1]), maxp(s1[ct][2], s1[ct][3])));
+        mx[ct] = maxp_xor32(maxp_xor16(a)) * p.scale_log2;
       }
       if (__ballot(mx[0] > m[0] + kRescaleSlack || mx[1] > m[1] + kRescaleSlack) != 0) {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const float mn = fmaxf(m[ct], mx[ct]);
+          const float mn = maxp(m[ct], mx[ct]);
           const float alpha = fast_exp2(m[ct] - mn);
           lsum[ct] *= alpha;
 #pragma unroll
@@ -230,9 +244,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
           m[ct] = mn;
         }
       }
-      // weights as bf16 hi/lo operands; the P.V contraction takes them in the
-      // order k = 8kg + j <-> token 4kg + j of the pair's first sub-tile (j < 4)
-      // or of its second
+      // weights as bf16 hi/lo operands: pr[j] is token 8kg + j of the run
+      // (tile 0's rows for j < 4, tile 1's for j >= 4)
       bf16x8 pb_hi[2], pb_lo[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
@@ -250,15 +263,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
         pb_hi[ct] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
         pb_lo[ct] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
-      const int sub0 = 2 * pair, sub1 = 2 * pair + 1;
-      const unsigned char* v0 = &lds[buf][1][(sub0 / SUBB) * TILE + (sub0 % SUBB) * (HD * 32)];
-      const unsigned char* v1 = &lds[buf][1][(sub1 / SUBB) * TILE + (sub1 % SUBB) * (HD * 32)];
+      const unsigned char* vr = &lds[buf][1][pair * RUN_BYTES];
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const int off = value_offset(16 * nt + n, kg);
-        const uint2 a0 = *reinterpret_cast<const uint2*>(v0 + off);
-        const uint2 a1 = *reinterpret_cast<const uint2*>(v1 + off);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
+        // dim 16nt + n, tokens 8kg..8kg+7 of the run
+        const int d = 16 * nt + n;
+        const int off = BS == 32 ? d * 64 + 16 * (kg ^ value_rot(d)) : (kg >> 1) * TILE + d * 32 + 16 * (kg & 1);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vr + off);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb_hi[ct], o[ct][nt], 0, 0, 0);
