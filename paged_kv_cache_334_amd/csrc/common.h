@@ -121,8 +121,9 @@ __device__ __forceinline__ float max_xor32(float v) {
 
 // NaN-propagating maximum (v_maximum3_f32 on gfx950).  fmaxf must quiet a
 // signalling NaN input first, which costs one extra instruction per operand
-// that the compiler cannot prove canonical (every matrix-core result); where
-// no input may be NaN except through the data itself, this form is cheaper.
+// that the compiler cannot prove canonical (every matrix-core result).  Used
+// where masked logits are already -inf, so a NaN can only come from the data
+// itself, and then the output row is NaN either way.
 __device__ __forceinline__ float maxp(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float maxp_xor16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);

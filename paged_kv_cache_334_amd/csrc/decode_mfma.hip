@@ -171,10 +171,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeArgs a) 
       float sr[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) sr[rr] = (4 * kg + rr < valid) ? s[rr] : -INFINITY;
-      float mx = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
-      mx = max_xor32(max_xor16(mx)) * a.scale_log2;  // per column (head slot)
+      float mx = maxp(maxp(sr[0], sr[1]), maxp(sr[2], sr[3]));
+      mx = maxp_xor32(maxp_xor16(mx)) * a.scale_log2;  // per column (head slot)
       if (__ballot(mx > m + kRescaleSlack) != 0) {
-        const float mn = fmaxf(m, mx);
+        const float mn = maxp(m, mx);
         const float alpha = fast_exp2(m - mn);
         lsum *= alpha;
 #pragma unroll

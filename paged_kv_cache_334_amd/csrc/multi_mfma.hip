@@ -238,11 +238,11 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
       float v8[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v8[e] = keep[e] ? t8[e] : -INFINITY;
-      const float raw = max_xor32(fmaxf(fmaxf(fmaxf(v8[0], v8[1]), fmaxf(v8[2], v8[3])),
-                                        fmaxf(fmaxf(v8[4], v8[5]), fmaxf(v8[6], v8[7]))));
+      const float raw = maxp_xor32(maxp(maxp(maxp(v8[0], v8[1]), maxp(v8[2], v8[3])),
+                                        maxp(maxp(v8[4], v8[5]), maxp(v8[6], v8[7]))));
       const float mx = raw == -INFINITY ? -INFINITY : raw * a.scale_log2;  // nothing visible here
       if (__ballot(mx > m + kRescaleSlack) != 0) {
-        const float mn = fmaxf(m, mx);
+        const float mn = maxp(m, mx);
         const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
         lsum *= alpha;
 #pragma unroll
