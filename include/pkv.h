@@ -129,7 +129,13 @@ typedef struct {
  * block ids agree; the group's prefix is the longest run of identical block ids
  * at the start of every member's table, counting only blocks fully inside every
  * member's context.  Groups with fewer than min_group_seqs members (at least 2)
- * or a prefix shorter than min_prefix_blocks are dropped.
+ * or a prefix shorter than min_prefix_blocks are dropped.  Groups nest, as the
+ * forks of a beam search leave them under a shared system prompt: members of
+ * a group that agree on the block id right after its prefix form a child group
+ * by the same rule, kept when it extends the blocks the parent's pass covers
+ * (whole 64-token iterations) by at least min_prefix_blocks blocks and one
+ * iteration; the child's pass starts where the parent's ends.  At most 4
+ * levels.  Each sequence's prefix is that of its deepest group.
  *
  *  block_tables  HOST [num_seqs][max_blocks_per_seq] int32
  *  context_lens  HOST [num_seqs] int32

@@ -2,6 +2,7 @@
 // split-K planning and launches.  Host code only; no host synchronization.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -74,6 +75,7 @@ struct Plan {
   int prefix_tiles = 0;         // 128-row tiles over all groups
   int prefix_chunk_blocks = 0;  // prefix blocks per workgroup
   int prefix_chunks = 0;        // chunk slots per (sequence, query head)
+  int prefix_grid_chunks = 0;   // chunks of the longest group
 };
 
 // Prefix-pass workgroups to aim for (two per CU).
@@ -90,49 +92,72 @@ pkv_status plan_cascade(const pkv_pool_desc* pool, int32_t num_seqs, int32_t max
   if (w[pkv::kPlanBlockSize] != pool->block_size) return fail(PKV_EINVAL, "prefix plan: made for another block size");
   const int64_t groups = w[pkv::kPlanGroups], members = w[pkv::kPlanMembers];
   if (groups < 0 || members < 0 ||
-      nw < (size_t)(pkv::kPlanHeader + num_seqs + pkv::kGroupWords * groups + members))
+      nw < (size_t)(pkv::kPlanHeader + 2 * (int64_t)num_seqs + pkv::kGroupWords * groups + members))
     return fail(PKV_EINVAL, "prefix plan: truncated");
   if (!opts->prefix_plan_dev) return fail(PKV_EINVAL, "prefix plan: device copy missing");
   if (groups == 0) return PKV_OK;
   if (pool->dtype != PKV_BF16 || pool->head_dim != 128 || pool->block_size < 16)
     return fail(PKV_EUNSUPPORTED, "cascade decode needs bf16 pools with head_dim 128 and blocks of 16 or 32 tokens");
   // every index the kernels take from the plan is checked here, once, on the host
+  const int bs = pool->block_size;
   const int32_t* start = w + pkv::kPlanHeader;
-  const int32_t* gw = start + num_seqs;
+  const int32_t* group_of = pkv::plan_group_of(w);
+  const int32_t* gw = pkv::plan_groups(w);
   const int32_t* mw = gw + pkv::kGroupWords * groups;
-  int64_t tiles = 0, max_prefix = 0;
+  int64_t tiles = 0, longest = 0;
   for (int64_t gi = 0; gi < groups; ++gi) {
-    const int32_t prefix = gw[pkv::kGroupWords * gi], begin = gw[pkv::kGroupWords * gi + 1];
-    const int32_t count = gw[pkv::kGroupWords * gi + 2], leader = gw[pkv::kGroupWords * gi + 3];
+    const int32_t* gr = gw + pkv::kGroupWords * gi;
+    const int32_t prefix = gr[pkv::kGroupPrefix], begin = gr[pkv::kGroupBegin];
+    const int32_t count = gr[pkv::kGroupCount], leader = gr[pkv::kGroupLeader];
+    const int32_t gstart = gr[pkv::kGroupStart], parent = gr[pkv::kGroupParent];
     if (prefix <= 0 || count <= 0 || begin < 0 || (int64_t)begin + count > members)
       return fail(PKV_EINVAL, "prefix plan: bad group");
     if (prefix > max_blocks_per_seq || leader < 0 || leader >= num_seqs)
       return fail(PKV_EINVAL, "prefix plan: group does not fit the block tables");
+    // a child starts where its parent's pass ends; parents come first, depth is bounded
+    if (parent < -1 || parent >= gi) return fail(PKV_EINVAL, "prefix plan: bad parent group");
+    const int32_t want_start =
+        parent < 0 ? 0 : pkv::prefix_covered_blocks(gw[pkv::kGroupWords * parent + pkv::kGroupPrefix], bs);
+    if (gstart != want_start || (parent >= 0 && prefix <= gw[pkv::kGroupWords * parent + pkv::kGroupPrefix]))
+      return fail(PKV_EINVAL, "prefix plan: group does not extend its parent");
+    int depth = 0;
+    for (int32_t a = parent; a >= 0; a = gw[pkv::kGroupWords * a + pkv::kGroupParent]) ++depth;
+    if (depth >= pkv::kMaxPrefixLevels) return fail(PKV_EINVAL, "prefix plan: groups nested too deep");
     for (int32_t k = 0; k < count; ++k) {
       const int32_t b = mw[begin + k];
-      if (b < 0 || b >= num_seqs || start[b] != prefix)
-        return fail(PKV_EINVAL, "prefix plan: member outside the batch or with another prefix");
+      if (b < 0 || b >= num_seqs || group_of[b] < 0 || group_of[b] >= groups)
+        return fail(PKV_EINVAL, "prefix plan: member outside the batch or without a group");
+      // gi must lie on the member's path from its deepest group to the root
+      int32_t a = group_of[b];
+      while (a > gi) a = gw[pkv::kGroupWords * a + pkv::kGroupParent];
+      if (a != gi) return fail(PKV_EINVAL, "prefix plan: member not under its group");
     }
     tiles += ((int64_t)count * g + 127) / 128;
-    const int64_t covered = pkv::prefix_covered_blocks(prefix, pool->block_size);
-    max_prefix = covered > max_prefix ? covered : max_prefix;
+    longest = std::max<int64_t>(longest, pkv::prefix_covered_blocks(prefix, bs) - gstart);
   }
-  if (max_prefix == 0) return PKV_OK;  // every prefix shorter than one pass iteration: plain decode
-  for (int32_t b = 0; b < num_seqs; ++b)
-    if (start[b] < 0 || pkv::prefix_covered_blocks(start[b], pool->block_size) > max_prefix)
+  if (longest <= 0) return PKV_OK;  // every prefix shorter than one pass iteration: plain decode
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t gi = group_of[b];
+    if (gi < -1 || gi >= groups || start[b] != (gi < 0 ? 0 : gw[pkv::kGroupWords * gi + pkv::kGroupPrefix]))
       return fail(PKV_EINVAL, "prefix plan: bad per-sequence prefix");
+  }
   if (tiles > 0x7fffffff) return fail(PKV_EUNSUPPORTED, "prefix plan: too many rows");
-  const int64_t per_iter = 64 / pool->block_size;  // blocks the prefix kernel moves per iteration
+  const int64_t per_iter = 64 / bs;  // blocks the prefix kernel moves per iteration
   // as many chunks as keep every workgroup of the pass resident at once (a
   // second, partial round of workgroups would double the pass's time)
   const int64_t units = tiles * pool->num_kv_heads;
   const int64_t want = units >= kPrefixTargetWorkgroups ? 1 : kPrefixTargetWorkgroups / units;
-  int64_t cb = (max_prefix + want - 1) / want;
+  int64_t cb = (longest + want - 1) / want;
   cb = (cb + per_iter - 1) / per_iter * per_iter;
+  // chunk slots of the deepest path (each sequence's partials run from the root down)
+  int64_t slots = 0;
+  for (int32_t b = 0; b < num_seqs; ++b)
+    slots = std::max<int64_t>(slots, pkv::path_slots(gw, group_of[b], bs, (int)cb));
   plan->cascade = true;
   plan->prefix_tiles = (int)tiles;
   plan->prefix_chunk_blocks = (int)cb;
-  plan->prefix_chunks = (int)((max_prefix + cb - 1) / cb);
+  plan->prefix_grid_chunks = (int)((longest + cb - 1) / cb);
+  plan->prefix_chunks = (int)slots;
   if (plan->prefix_chunks > 65535) return fail(PKV_EUNSUPPORTED, "prefix plan: too many chunks");
   return PKV_OK;
 }
@@ -385,7 +410,8 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
     p.max_blocks = max_blocks_per_seq;
     p.num_blocks = pool->num_blocks;
     p.chunk_blocks = plan.prefix_chunk_blocks;
-    p.num_chunks = plan.prefix_chunks;
+    p.num_chunks = plan.prefix_grid_chunks;
+    p.num_slots = plan.prefix_chunks;
     p.num_tiles = plan.prefix_tiles;
     p.scale_log2 = a.scale_log2;
     p.ws_m = pre;
@@ -394,6 +420,7 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
     hipError_t pe = pkv::launch_prefix(p, pool->block_size, plan.group, s);
     if (pe != hipSuccess) return fail(PKV_EHIP, std::string("prefix launch: ") + hipGetErrorString(pe));
     a.start_blocks = opts->prefix_plan_dev + pkv::kPlanHeader;
+    a.plan = opts->prefix_plan_dev;
     a.prefix_chunks = plan.prefix_chunks;
     a.prefix_chunk_blocks = plan.prefix_chunk_blocks;
     a.pre_m = p.ws_m;

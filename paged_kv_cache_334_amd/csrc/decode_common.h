@@ -256,7 +256,9 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
     const int h = idx / HD, d = idx % HD;
     const int hq = h0 + h;
     // partials of the shared-prefix pass, merged here when this pass is the only suffix partition
-    const int pre = (r.start > 0 && r.nparts == 1) ? (r.start + a.prefix_chunk_blocks - 1) / a.prefix_chunk_blocks : 0;
+    const int pre = (r.start > 0 && r.nparts == 1)
+                        ? path_slots(plan_groups(a.plan), plan_group_of(a.plan)[r.b], a.plan[kPlanBlockSize], a.prefix_chunk_blocks)
+                        : 0;
     const int64_t pre_base = ((int64_t)r.b * a.num_heads + hq) * a.prefix_chunks;
     float big_m = -INFINITY;
 #pragma unroll

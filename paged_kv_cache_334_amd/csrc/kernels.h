@@ -35,10 +35,13 @@ struct DecodeArgs {
   float* ws_m;
   float* ws_l;
   float* ws_acc;
-  // Cascade (shared-prefix) mode: start_blocks[b] = blocks of sequence b already
-  // covered by the prefix pass (NULL: none).  Its partials for chunk c < ceil(start /
-  // prefix_chunk_blocks) sit at (b*num_heads + h)*prefix_chunks + c of pre_*.
+  // Cascade (shared-prefix) mode: start_blocks[b] = raw prefix blocks of sequence
+  // b's deepest group (NULL: none); the prefix pass covered
+  // prefix_covered_blocks() of them.  Its partials, path_slots() of them for
+  // the group plan_group_of(plan)[b], sit at (b*num_heads + h)*prefix_chunks + c
+  // of pre_*.
   const int32_t* start_blocks;
+  const int32_t* plan;
   int32_t prefix_chunks;
   int32_t prefix_chunk_blocks;
   const float* pre_m;
@@ -58,9 +61,13 @@ struct DecodeArgs {
 
 // Shared-prefix plan words (built on the host by pkv_plan_shared_prefix):
 //   [0] magic  [1] num_seqs  [2] block_size  [3] num_groups  [4] max prefix blocks
-//   [5] total members, then prefix_blocks[num_seqs], then per group
-//   {prefix_blocks, member_begin, member_count, leader}, then the member lists.
-constexpr int32_t kPlanMagic = 0x504b5650;  // "PKVP"
+//   [5] total members, then prefix_blocks[num_seqs] (prefix of the sequence's
+//   deepest group, 0 = none), then group_of[num_seqs] (that group, -1 = none),
+//   then per group {prefix_blocks, member_begin, member_count, leader,
+//   start_blocks, parent}, then the member lists.  Groups nest (a beam tree):
+//   a child group's members are members of its parent, it starts where the
+//   parent's pass coverage ends and extends the shared run; parents come first.
+constexpr int32_t kPlanMagic = 0x32564b50;  // "PKV2"
 
 // The shared-prefix pass moves 64 tokens per iteration and handles whole
 // iterations only: it covers the largest multiple of 64/block_size blocks of
@@ -76,7 +83,34 @@ constexpr int kPlanGroups = 3;
 constexpr int kPlanMaxPrefix = 4;
 constexpr int kPlanMembers = 5;
 constexpr int kPlanHeader = 6;
-constexpr int kGroupWords = 4;
+constexpr int kGroupWords = 6;
+constexpr int kGroupPrefix = 0, kGroupBegin = 1, kGroupCount = 2, kGroupLeader = 3, kGroupStart = 4, kGroupParent = 5;
+constexpr int kMaxPrefixLevels = 4;  // nesting depth of shared-prefix groups
+
+// Plan sections.
+__host__ __device__ inline const int32_t* plan_group_of(const int32_t* plan) {
+  return plan + kPlanHeader + plan[kPlanSeqs];
+}
+__host__ __device__ inline const int32_t* plan_groups(const int32_t* plan) {
+  return plan + kPlanHeader + 2 * plan[kPlanSeqs];
+}
+// Prefix chunks of one group (chunk_blocks blocks each, the last one shorter).
+__host__ __device__ inline int group_chunks(const int32_t* gr, int block_size, int chunk_blocks) {
+  const int n = prefix_covered_blocks(gr[kGroupPrefix], block_size) - gr[kGroupStart];
+  return n > 0 ? (n + chunk_blocks - 1) / chunk_blocks : 0;
+}
+// Chunk partial slots of a sequence run through its groups from the root:
+// group g's chunks sit after those of its ancestors.  Returns the slots of
+// the groups from `gi` up to the root.
+__host__ __device__ inline int path_slots(const int32_t* groups, int gi, int block_size, int chunk_blocks) {
+  int n = 0;
+  for (int depth = 0; gi >= 0 && depth < kMaxPrefixLevels; ++depth) {
+    const int32_t* gr = groups + kGroupWords * gi;
+    n += group_chunks(gr, block_size, chunk_blocks);
+    gi = gr[kGroupParent];
+  }
+  return n;
+}
 
 // Everything the shared-prefix kernel reads.
 struct PrefixArgs {
@@ -90,7 +124,8 @@ struct PrefixArgs {
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t chunk_blocks;  // prefix blocks per workgroup
-  int32_t num_chunks;    // chunk slots per (sequence, query head)
+  int32_t num_chunks;    // chunks of the longest group (grid)
+  int32_t num_slots;     // chunk slots per (sequence, query head)
   int32_t num_tiles;     // 128-row tiles over all groups
   float scale_log2;
   float* ws_m;

@@ -104,26 +104,31 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // which group and 128-row tile: groups hold their tiles in order
   const int32_t* plan = p.plan;
   const int num_groups = plan[kPlanGroups];
-  const int32_t* groups = plan + kPlanHeader + plan[kPlanSeqs];
+  const int32_t* groups = plan_groups(plan);
   int tile = slot % p.num_tiles, gi = 0;
-  int gprefix = 0, gbegin = 0, gcount = 0, leader = 0;
+  int gend = 0, gstart = 0, gbegin = 0, gcount = 0, leader = 0, parent = -1;
   for (; gi < num_groups; ++gi) {
     const int32_t* gr = groups + kGroupWords * gi;
-    const int tiles = (gr[2] * G + 127) / 128;
+    const int tiles = (gr[kGroupCount] * G + 127) / 128;
     if (tile < tiles) {
-      gprefix = prefix_covered_blocks(gr[0], BS);
-      gbegin = gr[1];
-      gcount = gr[2];
-      leader = gr[3];
+      gend = prefix_covered_blocks(gr[kGroupPrefix], BS);
+      gstart = gr[kGroupStart];
+      gbegin = gr[kGroupBegin];
+      gcount = gr[kGroupCount];
+      leader = gr[kGroupLeader];
+      parent = gr[kGroupParent];
       break;
     }
     tile -= tiles;
   }
   if (gi == num_groups) return;
   const int32_t* members = groups + kGroupWords * num_groups + gbegin;
-  const int blk_lo = chunk * p.chunk_blocks;
-  const int blk_hi = min(gprefix, blk_lo + p.chunk_blocks);
-  if (blk_lo >= blk_hi) return;  // the merge counts only the chunks the group's prefix reaches
+  // chunk `chunk` of the group's blocks [gstart, gend); a nested group's slots
+  // follow those of its ancestors
+  const int blk_lo = gstart + chunk * p.chunk_blocks;
+  const int blk_hi = min(gend, blk_lo + p.chunk_blocks);
+  if (blk_lo >= blk_hi) return;  // the merge counts only the chunks the group's blocks reach
+  const int slot0 = path_slots(groups, parent, BS, p.chunk_blocks) + chunk;
   const int rows = gcount * G;
   const int row0 = tile * 128 + ROWS_PER_WAVE * wave;  // this wave's first row
   const bool wave_active = row0 < rows;
@@ -300,7 +305,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     if (row >= rows) continue;
     const int b = members[row / G];
     const int h = kvh * G + row % G;
-    const int64_t pi = ((int64_t)b * p.num_heads + h) * p.num_chunks + chunk;
+    const int64_t pi = ((int64_t)b * p.num_heads + h) * p.num_slots + slot0;
     float* acc = p.ws_acc + pi * HD;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {

@@ -177,9 +177,15 @@ class PrefixPlan:
         return int(self.host[3])
 
     def prefix_blocks(self):
-        """Blocks of each sequence covered by a shared prefix (0 = none)."""
+        """Blocks of each sequence covered by a shared prefix (its deepest
+        group's, 0 = none)."""
         n = int(self.host[1])
         return self.host[6:6 + n]
+
+    def group_of(self):
+        """Deepest shared-prefix group of each sequence (-1 = none)."""
+        n = int(self.host[1])
+        return self.host[6 + n:6 + 2 * n]
 
 
 def plan_shared_prefix(block_tables, context_lens, block_size, min_group_seqs=4, min_prefix_blocks=8,

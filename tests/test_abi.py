@@ -169,12 +169,22 @@ def test_prefix_plan_is_checked_before_launch(ops):
     bad = words.copy()
     bad[1] = 5
     assert call(bad) == 1                                   # other batch size
+    g0 = 6 + 2 * 4  # words of group 0 (after prefix_of[4] and group_of[4])
     bad = words.copy()
-    bad[6 + 4 + 3] = 9
+    bad[g0 + 3] = 9
     assert call(bad) == 1                                   # leader outside the batch
     bad = words.copy()
     bad[6 + 2] = 3
     assert call(bad) == 1                                   # member with another prefix
+    bad = words.copy()
+    bad[6 + 4 + 2] = -1
+    assert call(bad) == 1                                   # member without a group
+    bad = words.copy()
+    bad[g0 + 5] = 0
+    assert call(bad) == 1                                   # group as its own parent
+    bad = words.copy()
+    bad[g0 + 4] = 4
+    assert call(bad) == 1                                   # root not starting at block 0
     assert call(words, desc=_desc(ops, dtype=ops.PKV_F32)) == 2  # cascade needs bf16
     opts = ops.DecodeOpts(0, 0, 0, 0, words.ctypes.data, 16, words.size)
     ws = ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(opts))
@@ -250,7 +260,7 @@ def test_block_size_8(ops):
     need = ops.lib.pkv_paged_attn_multi_token_workspace_bytes(ctypes.byref(d), 4, 32, 12, 3, 256,
                                                               ctypes.byref(ops.DecodeOpts(64, 2, 0)))
     assert need > 0
-    plan = (ctypes.c_int32 * 16)(0x504b5650, 4, 8, 1, 16, 2, 16, 16, 0, 0, 16, 0, 2, 0, 0, 1)
-    opts = ops.DecodeOpts(0, 0, 0, 0, ctypes.addressof(plan), 16, 16)
+    plan = (ctypes.c_int32 * 22)(0x32564b50, 4, 8, 1, 16, 2, 16, 16, 0, 0, 0, 0, -1, -1, 16, 0, 2, 0, 0, -1, 0, 1)
+    opts = ops.DecodeOpts(0, 0, 0, 0, ctypes.addressof(plan), 16, 22)
     assert _decode(ops, d, opts=opts, max_blocks=32) == 2
     assert "16 or 32" in ops.lib.pkv_last_error().decode()

@@ -170,3 +170,45 @@ def test_full_shared_prefix_workload_sampled():
     ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale, pairs=pairs)
     got = np.stack([out[b, h] for b, h in pairs])
     check_attention(got, ref, "bf16", "bf16", "cascade/full")
+
+
+def _nested(name):
+    """Workloads whose shared prefixes nest (beam trees), from flat ones with
+    table entries repointed (tests/beam_tree.py); returns (wl, groups expected)."""
+    from beam_tree import three_levels, two_levels
+
+    if name == "nested-2-levels":
+        # three groups of 20 shared blocks, all of them sharing their first 12
+        wl = generate("shared-prefix", num_seqs=23, shared_prefix=320, ctx=(1, 70), num_heads=16, num_kv_heads=2,
+                      prefix_groups=3, unshared_seqs=5)
+        groups = [[b for b in range(23) if prefix_group_of(wl.spec, b) == k] for k in range(3)]
+        wl.block_tables = two_levels(wl.block_tables, groups, 12)
+        return wl, 4
+    # twelve sequences sharing 32 blocks rewired into a three-level tree
+    wl = generate("shared-prefix", num_seqs=12, shared_prefix=512, ctx=(16, 100), num_heads=8, num_kv_heads=2,
+                  cow_fraction=0.25)
+    wl.block_tables = three_levels(wl.block_tables, list(range(12)), 32)
+    return wl, 5
+
+
+@pytest.mark.parametrize("name", ["nested-2-levels", "nested-3-levels"])
+def test_nested_cascade_matches_oracle(name):
+    """Nested groups: each level's pass covers its own block range for its own
+    members, every sequence's partials run from the root group down, and the
+    suffix pass merges them all."""
+    _say(f"[cascade] {name}")
+    wl, ngroups = _nested(name)
+    gw = GpuWorkload(wl)
+    desc, kp, vp = oracle_pools(wl)
+    ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale)
+    plan = ops.plan_shared_prefix(wl.block_tables, wl.context_lens, wl.spec.block_size, min_group_seqs=2,
+                                  min_prefix_blocks=1)
+    assert plan.groups == ngroups
+    for out_dtype in ("bf16", "f32"):
+        odt = torch.float32 if out_dtype == "f32" else None
+        out = gw.decode(prefix_plan=plan, out_dtype=odt)
+        torch.cuda.synchronize()
+        check_attention(out_to_f64(out), ref, "bf16", out_dtype, f"cascade/{name}")
+    a = out_to_f64(gw.decode(prefix_plan=plan, out_dtype=torch.float32))
+    b = out_to_f64(gw.decode(out_dtype=torch.float32))
+    assert np.abs(a - b).max() <= 2e-3
