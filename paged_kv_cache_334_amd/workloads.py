@@ -129,6 +129,7 @@ class WorkloadSpec:
     ctx: Union[Tuple[int, int], Tuple[int, ...]]  # (lo, hi) inclusive uniform, or explicit lengths
     ctx_is_list: bool = False
     shared_prefix: int = 0  # tokens every sequence of a prefix group shares (block aligned)
+    tree_prefix: int = 0  # of those, tokens every prefix group shares with the others (block aligned)
     prefix_groups: int = 1  # sequence b < num_seqs - unshared_seqs joins group b % prefix_groups
     unshared_seqs: int = 0  # trailing sequences with no shared prefix
     cow_fraction: float = 0.0  # fraction of sequences whose last block was just forked
@@ -160,6 +161,14 @@ SPECS = {
     "shared-prefix": WorkloadSpec("shared-prefix", BF16, 200, 32, 8, 128, 16, (16, 512),
                                   shared_prefix=30000, cow_fraction=0.10, seed=1005),
 }
+# Nested sharing, as beam search leaves it: 8 requests x 16 beams under one
+# 4096-token system prompt, each request's 2048-token prompt shared by its
+# beams, U[16, 256] tokens of each beam's own, 10% of the beams just forked.
+TREE_SPECS = {
+    "beam-tree": WorkloadSpec("beam-tree", BF16, 128, 32, 8, 128, 16, (16, 256), shared_prefix=6144,
+                              tree_prefix=4096, prefix_groups=8, cow_fraction=0.10, seed=1008),
+}
+SPECS.update(TREE_SPECS)
 ORDER = ["tiny-f32", "mha-7b", "gqa-70b", "long-32k", "shared-prefix"]
 
 # Several new tokens per sequence: the 70B-shaped GQA batch verifying 4 tokens
@@ -291,8 +300,10 @@ def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overri
         spec = replace(spec, **overrides)
     bs = spec.block_size
     nseq = spec.num_seqs
-    if spec.shared_prefix % bs:
-        raise ValueError("the shared prefix must be a whole number of blocks")
+    if spec.shared_prefix % bs or spec.tree_prefix % bs:
+        raise ValueError("the shared prefixes must be whole numbers of blocks")
+    if spec.tree_prefix > spec.shared_prefix:
+        raise ValueError("the prefix common to all groups cannot exceed a group's")
 
     rng = lambda purpose: np.random.default_rng([spec.seed, purpose])  # noqa: E731
     ctx = context_lengths(spec)
@@ -314,21 +325,33 @@ def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overri
     prefix_blocks = spec.shared_prefix // bs
     groups = spec.prefix_groups if spec.shared_prefix else 0
     own = [int(n) - (spec.shared_prefix if prefix_group_of(spec, b) >= 0 else 0) for b, n in enumerate(ctx)]
-    needed = prefix_blocks * groups + int(sum(-(-o // bs) for o in own)) + len(cow_seqs)
+    tree_blocks = spec.tree_prefix // bs if groups else 0
+    needed = tree_blocks + (prefix_blocks - tree_blocks) * groups + int(sum(-(-o // bs) for o in own)) + len(cow_seqs)
     num_blocks = spec.num_blocks if spec.num_blocks is not None else int(np.ceil(spec.pool_factor * needed))
     if num_blocks < needed + 1:
         raise ValueError("pool too small")
     free_order = rng(_PERM).permutation(num_blocks)
     mgr = BlockManager(num_blocks, bs, free_order)
 
-    # token order: the shared prefixes first, then each sequence's own tokens
+    # token order: the prefix common to all groups, the rest of each group's
+    # prefix (forked from it), then each sequence's own tokens
     init_slots = []
-    init_owner = []  # (seq, or -1 - group for a prefix token, position)
+    init_owner = []  # (seq, or -1 - group for a prefix token, -1 - groups for a common one, position)
+    if tree_blocks:
+        mgr.allocate_sequence(("tree",))
+        for pos in range(spec.tree_prefix):
+            init_slots.append(mgr.append_slot(("tree",)))
+            init_owner.append((-1 - groups, pos))
     for gi in range(groups):
-        mgr.allocate_sequence(("prefix", gi))
-        for pos in range(spec.shared_prefix):
+        if tree_blocks:
+            mgr.fork(("tree",), ("prefix", gi))
+        else:
+            mgr.allocate_sequence(("prefix", gi))
+        for pos in range(spec.tree_prefix if tree_blocks else 0, spec.shared_prefix):
             init_slots.append(mgr.append_slot(("prefix", gi)))
             init_owner.append((-1 - gi, pos))
+    if tree_blocks:
+        mgr.free_sequence(("tree",))
     for b in range(nseq):
         gi = prefix_group_of(spec, b)
         if gi >= 0:

@@ -212,3 +212,41 @@ def test_nested_cascade_matches_oracle(name):
     a = out_to_f64(gw.decode(prefix_plan=plan, out_dtype=torch.float32))
     b = out_to_f64(gw.decode(out_dtype=torch.float32))
     assert np.abs(a - b).max() <= 2e-3
+
+
+def test_beam_tree_workload():
+    """The beam-tree generator at a small size (four requests x eight beams under
+    a common prompt, copy-on-write of just-forked beams): nested cascade
+    against the oracle."""
+    wl = generate("beam-tree", num_seqs=32, shared_prefix=640, tree_prefix=384, ctx=(1, 60), prefix_groups=4,
+                  num_heads=16, num_kv_heads=2)
+    _say("[cascade] beam-tree small")
+    gw = GpuWorkload(wl)
+    desc, kp, vp = oracle_pools(wl)
+    ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale)
+    plan = ops.plan_shared_prefix(wl.block_tables, wl.context_lens, 16)
+    assert plan.groups == 5
+    for out_dtype in ("bf16", "f32"):
+        out = gw.decode(prefix_plan=plan, out_dtype=torch.float32 if out_dtype == "f32" else None)
+        check_attention(out_to_f64(out), ref, "bf16", out_dtype, "cascade/beam-tree-small")
+
+
+def test_full_beam_tree_workload_sampled():
+    """The full beam-tree workload in the benchmark's launch configuration
+    (default plan thresholds), sampled rows against the oracle."""
+    _say("[cascade] full beam-tree build")
+    wl = generate("beam-tree")
+    gw = GpuWorkload(wl)
+    plan = ops.plan_shared_prefix(wl.block_tables, wl.context_lens, 16)
+    assert plan.groups == 9
+    out = out_to_f64(gw.decode(prefix_plan=plan))
+    assert np.isfinite(out).all()
+    desc, kp, vp = oracle_pools(wl)
+    rng = np.random.default_rng(6)
+    seqs = sorted({int(np.argmax(wl.context_lens)), int(np.argmin(wl.context_lens)),
+                   *rng.integers(0, 128, size=6).tolist()})
+    pairs = [(b, h) for b in seqs for h in rng.choice(32, size=4, replace=False).tolist()]
+    _say(f"[cascade] full beam-tree oracle on {len(pairs)} rows")
+    ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale, pairs=pairs)
+    got = np.stack([out[b, h] for b, h in pairs])
+    check_attention(got, ref, "bf16", "bf16", "cascade/full-beam-tree")

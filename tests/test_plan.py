@@ -178,3 +178,15 @@ def test_child_must_add_a_pass_iteration():
     _, group_of, groups = parse(plan_words(tables, ctx, 16))
     assert [(p, m, s) for p, m, s, _ in groups] == [(4, [0, 1, 2, 3], 0), (10, [0, 1], 4)]
     assert group_of.tolist() == [1, 1, 0, 0]
+
+
+def test_beam_tree_workload_nests_one_level():
+    """The beam-tree generator (a prompt common to every request, each request's
+    own prompt shared by its beams, forks through the block manager) gives a
+    root group over all beams and one child per request."""
+    wl = generate("beam-tree", num_seqs=32, shared_prefix=384, tree_prefix=256, ctx=(1, 40), prefix_groups=4)
+    prefix_of, group_of, groups = parse(plan_words(wl.block_tables, wl.context_lens, 16))
+    assert groups == rule(wl.block_tables, wl.context_lens, 16)
+    assert groups[0] == (16, list(range(32)), 0, -1)
+    assert sorted(groups[1:]) == sorted((24, [b for b in range(32) if b % 4 == k], 16, 0) for k in range(4))
+    assert (prefix_of == 24).all() and sorted(set(group_of.tolist())) == [1, 2, 3, 4]
