@@ -127,9 +127,15 @@ pkv_status plan_cascade(const pkv_pool_desc* pool, int32_t num_seqs, int32_t max
       const int32_t b = mw[begin + k];
       if (b < 0 || b >= num_seqs || group_of[b] < 0 || group_of[b] >= groups)
         return fail(PKV_EINVAL, "prefix plan: member outside the batch or without a group");
-      // gi must lie on the member's path from its deepest group to the root
+      // gi must lie on the member's path from its deepest group to the root;
+      // the walk reaches groups whose own words are checked later, so every
+      // step must go to a smaller index
       int32_t a = group_of[b];
-      while (a > gi) a = gw[pkv::kGroupWords * a + pkv::kGroupParent];
+      while (a > gi) {
+        const int32_t up = gw[pkv::kGroupWords * a + pkv::kGroupParent];
+        if (up < -1 || up >= a) return fail(PKV_EINVAL, "prefix plan: bad parent group");
+        a = up;
+      }
       if (a != gi) return fail(PKV_EINVAL, "prefix plan: member not under its group");
     }
     tiles += ((int64_t)count * g + 127) / 128;

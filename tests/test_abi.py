@@ -185,6 +185,20 @@ def test_prefix_plan_is_checked_before_launch(ops):
     bad = words.copy()
     bad[g0 + 4] = 4
     assert call(bad) == 1                                   # root not starting at block 0
+    # a nested plan (root over all four, children over the first and last two) whose
+    # child names itself as parent: rejected, no endless walk up the tree
+    t2 = tables.copy()
+    t2[2:, 8:] += 100
+    nested = ops.plan_shared_prefix(t2, ctx, 16, 2, 1, device=None).host
+    assert int(nested[3]) == 3
+    nopts = ops.DecodeOpts(0, 0, 0, 0, nested.ctypes.data, 16, nested.size)
+    assert _decode(ops, d, opts=nopts, ws=16, ws_bytes=16) == 3  # plan accepted, stops at the workspace check
+    bad = nested.copy()
+    bad[g0 + 6 + 5] = 1
+    assert call(bad) == 1                                   # child as its own parent
+    bad = nested.copy()
+    bad[g0 + 6 + 5] = 7
+    assert call(bad) == 1                                   # parent outside the plan
     assert call(words, desc=_desc(ops, dtype=ops.PKV_F32)) == 2  # cascade needs bf16
     opts = ops.DecodeOpts(0, 0, 0, 0, words.ctypes.data, 16, words.size)
     ws = ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(opts))
