@@ -7,6 +7,8 @@
 #include <cstdint>
 #include <cstdio>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "../../include/pkv.h"
 #include "kernels.h"
@@ -105,6 +107,8 @@ pkv_status plan_cascade(const pkv_pool_desc* pool, int32_t num_seqs, int32_t max
   const int32_t* gw = pkv::plan_groups(w);
   const int32_t* mw = gw + pkv::kGroupWords * groups;
   int64_t tiles = 0, longest = 0;
+  std::vector<std::pair<int64_t, int64_t>> work;  // (row tiles, blocks the pass covers) per group
+  work.reserve(groups);
   for (int64_t gi = 0; gi < groups; ++gi) {
     const int32_t* gr = gw + pkv::kGroupWords * gi;
     const int32_t prefix = gr[pkv::kGroupPrefix], begin = gr[pkv::kGroupBegin];
@@ -138,8 +142,11 @@ pkv_status plan_cascade(const pkv_pool_desc* pool, int32_t num_seqs, int32_t max
       }
       if (a != gi) return fail(PKV_EINVAL, "prefix plan: member not under its group");
     }
-    tiles += ((int64_t)count * g + 127) / 128;
-    longest = std::max<int64_t>(longest, pkv::prefix_covered_blocks(prefix, bs) - gstart);
+    const int64_t t = ((int64_t)count * g + 127) / 128;
+    const int64_t n = std::max<int64_t>(pkv::prefix_covered_blocks(prefix, bs) - gstart, 0);
+    tiles += t;
+    longest = std::max<int64_t>(longest, n);
+    work.emplace_back(t, n);
   }
   if (longest <= 0) return PKV_OK;  // every prefix shorter than one pass iteration: plain decode
   for (int32_t b = 0; b < num_seqs; ++b) {
@@ -149,12 +156,23 @@ pkv_status plan_cascade(const pkv_pool_desc* pool, int32_t num_seqs, int32_t max
   }
   if (tiles > 0x7fffffff) return fail(PKV_EUNSUPPORTED, "prefix plan: too many rows");
   const int64_t per_iter = 64 / bs;  // blocks the prefix kernel moves per iteration
-  // as many chunks as keep every workgroup of the pass resident at once (a
-  // second, partial round of workgroups would double the pass's time)
-  const int64_t units = tiles * pool->num_kv_heads;
-  const int64_t want = units >= kPrefixTargetWorkgroups ? 1 : kPrefixTargetWorkgroups / units;
-  int64_t cb = (longest + want - 1) / want;
-  cb = (cb + per_iter - 1) / per_iter * per_iter;
+  // The shortest chunk (whole iterations) whose workgroups all fit at once: a
+  // second, partial round of workgroups would double the pass's time.  Only
+  // workgroups whose chunk lies inside their group's blocks count: a nested
+  // group covers fewer blocks than the longest, and the rest of its grid
+  // slots exit at once.
+  auto workgroups = [&](int64_t cb) {
+    int64_t n = 0;
+    for (const auto& w : work) n += w.first * ((w.second + cb - 1) / cb);
+    return n * pool->num_kv_heads;
+  };
+  int64_t lo = 1, hi = (longest + per_iter - 1) / per_iter;  // chunk length in iterations
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) / 2;
+    if (workgroups(mid * per_iter) <= kPrefixTargetWorkgroups) hi = mid;
+    else lo = mid + 1;
+  }
+  const int64_t cb = lo * per_iter;
   // chunk slots of the deepest path (each sequence's partials run from the root down)
   int64_t slots = 0;
   for (int32_t b = 0; b < num_seqs; ++b)
