@@ -109,6 +109,7 @@ pkv_status plan_cascade(const pkv_pool_desc* pool, int32_t num_seqs, int32_t max
   int64_t tiles = 0, longest = 0;
   std::vector<std::pair<int64_t, int64_t>> work;  // (row tiles, blocks the pass covers) per group
   work.reserve(groups);
+  std::vector<int32_t> listed(num_seqs, 0);  // groups whose member list holds the sequence
   for (int64_t gi = 0; gi < groups; ++gi) {
     const int32_t* gr = gw + pkv::kGroupWords * gi;
     const int32_t prefix = gr[pkv::kGroupPrefix], begin = gr[pkv::kGroupBegin];
@@ -131,6 +132,8 @@ pkv_status plan_cascade(const pkv_pool_desc* pool, int32_t num_seqs, int32_t max
       const int32_t b = mw[begin + k];
       if (b < 0 || b >= num_seqs || group_of[b] < 0 || group_of[b] >= groups)
         return fail(PKV_EINVAL, "prefix plan: member outside the batch or without a group");
+      if (k > 0 && b <= mw[begin + k - 1]) return fail(PKV_EINVAL, "prefix plan: member list not increasing");
+      ++listed[b];
       // gi must lie on the member's path from its deepest group to the root;
       // the walk reaches groups whose own words are checked later, so every
       // step must go to a smaller index
@@ -153,6 +156,11 @@ pkv_status plan_cascade(const pkv_pool_desc* pool, int32_t num_seqs, int32_t max
     const int32_t gi = group_of[b];
     if (gi < -1 || gi >= groups || start[b] != (gi < 0 ? 0 : gw[pkv::kGroupWords * gi + pkv::kGroupPrefix]))
       return fail(PKV_EINVAL, "prefix plan: bad per-sequence prefix");
+    // every group on the path from the deepest one to the root lists b (each
+    // listing group was checked to be on the path): its chunk slots are written
+    int32_t path = 0;
+    for (int32_t a = gi; a >= 0; a = gw[pkv::kGroupWords * a + pkv::kGroupParent]) ++path;
+    if (listed[b] != path) return fail(PKV_EINVAL, "prefix plan: sequence missing from a group on its path");
   }
   if (tiles > 0x7fffffff) return fail(PKV_EUNSUPPORTED, "prefix plan: too many rows");
   const int64_t per_iter = 64 / bs;  // blocks the prefix kernel moves per iteration

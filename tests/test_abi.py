@@ -199,6 +199,15 @@ def test_prefix_plan_is_checked_before_launch(ops):
     bad = nested.copy()
     bad[g0 + 6 + 5] = 7
     assert call(bad) == 1                                   # parent outside the plan
+    mem = g0 + 3 * 6  # member lists: root [0 1 2 3], then [0 1], then [2 3]
+    assert nested[mem:].tolist() == [0, 1, 2, 3, 0, 1, 2, 3]
+    bad = nested.copy()
+    bad[mem + 4:mem + 6] = [1, 0]
+    assert call(bad) == 1                                   # member list not increasing
+    bad = nested.copy()
+    bad[g0 + 1:g0 + 3] = [1, 3]                             # root lists [1 2 3]: sequence 0 missing
+    assert call(bad) == 1
+    assert "missing from a group on its path" in ops.lib.pkv_last_error().decode()
     assert call(words, desc=_desc(ops, dtype=ops.PKV_F32)) == 2  # cascade needs bf16
     opts = ops.DecodeOpts(0, 0, 0, 0, words.ctypes.data, 16, words.size)
     ws = ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(opts))
