@@ -34,3 +34,20 @@ def three_levels(tables, seqs, prefix):
     for b in seqs[3:6]:
         t[b, 20:prefix] = rev_lo
     return t
+
+
+def random_tree(tables, seqs, prefix, rng, lo=0, depth=0, max_depth=3):
+    """Split `seqs` (sharing tables[s, :prefix]) into a random nested tree, in
+    place: at a random block k past `lo`, a random tail of the list takes the
+    blocks k..prefix-1 of its first member's row in reverse order (a different
+    id at k, still full blocks of the prefix), and both parts split again."""
+    if depth >= max_depth or len(seqs) < 4 or prefix - lo < 12:
+        return
+    k = int(rng.integers(lo + 1, prefix - 8))
+    cut = int(rng.integers(2, len(seqs) - 1))
+    head, tail = seqs[:cut], seqs[cut:]
+    row = tables[tail[0], k:prefix][::-1].copy()
+    for b in tail:
+        tables[b, k:prefix] = row
+    random_tree(tables, head, prefix, rng, k, depth + 1, max_depth)
+    random_tree(tables, tail, prefix, rng, k, depth + 1, max_depth)

@@ -250,3 +250,24 @@ def test_full_beam_tree_workload_sampled():
     ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale, pairs=pairs)
     got = np.stack([out[b, h] for b, h in pairs])
     check_attention(got, ref, "bf16", "bf16", "cascade/full-beam-tree")
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_beam_trees_match_oracle(seed):
+    """Random nested trees (tests/beam_tree.py random_tree) over a flat shared
+    prefix of 64 blocks: cascade against the oracle."""
+    from beam_tree import random_tree
+
+    rng = np.random.default_rng(200 + seed)
+    bs = (16, 32, 16)[seed]
+    wl = generate("shared-prefix", num_seqs=24, shared_prefix=64 * bs, ctx=(1, 40), num_heads=8, num_kv_heads=2,
+                  block_size=bs, seed=seed, cow_fraction=0.2)
+    random_tree(wl.block_tables, list(rng.permutation(24)), 64, rng)
+    plan = ops.plan_shared_prefix(wl.block_tables, wl.context_lens, bs, min_group_seqs=2, min_prefix_blocks=1)
+    _say(f"[cascade] random tree seed {seed}: {plan.groups} groups")
+    assert plan.groups >= 2
+    gw = GpuWorkload(wl)
+    desc, kp, vp = oracle_pools(wl)
+    ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale)
+    out = gw.decode(prefix_plan=plan, out_dtype=torch.float32)
+    check_attention(out_to_f64(out), ref, "bf16", "f32", f"cascade/random-tree-{seed}")

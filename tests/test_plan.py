@@ -190,3 +190,24 @@ def test_beam_tree_workload_nests_one_level():
     assert groups[0] == (16, list(range(32)), 0, -1)
     assert sorted(groups[1:]) == sorted((24, [b for b in range(32) if b % 4 == k], 16, 0) for k in range(4))
     assert (prefix_of == 24).all() and sorted(set(group_of.tolist())) == [1, 2, 3, 4]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_beam_trees(seed):
+    """Random nested trees over a flat shared prefix: the plan equals the rule,
+    children start where their parents' passes end, and parents come first."""
+    from beam_tree import random_tree
+
+    rng = np.random.default_rng(100 + seed)
+    bs = int(rng.choice([16, 32]))
+    wl = generate("shared-prefix", num_seqs=24, shared_prefix=64 * bs, ctx=(1, 40), num_heads=8, num_kv_heads=2,
+                  block_size=bs, seed=seed)
+    tables = wl.block_tables.copy()
+    random_tree(tables, list(rng.permutation(24)), 64, rng)
+    _, group_of, groups = parse(plan_words(tables, wl.context_lens, bs))
+    assert groups == rule(tables, wl.context_lens, bs)
+    per = 64 // bs
+    for p, members, start, parent in groups:
+        if parent >= 0:
+            assert parent < groups.index((p, members, start, parent))
+            assert start == groups[parent][0] // per * per and set(members) < set(groups[parent][1])
