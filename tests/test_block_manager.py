@@ -229,3 +229,39 @@ def test_beam_search_batch_gives_one_group_per_request():
     assert plan.groups == len(prompts)
     expect = [len(prompts[s // 1000 - 1]) // bs for s in seqs]
     assert plan.prefix_blocks().tolist() == expect
+
+
+def test_beam_search_under_a_cached_system_prompt_nests():
+    """Several requests share a system prompt through the prefix cache, and
+    each request is forked into beams: the exported batch plans as one root
+    group over every beam (the system prompt's blocks) with one child group per
+    request (its own prompt's full blocks) -- a beam tree built by the native
+    manager alone."""
+    bs, beams = 16, 4
+    bm = ops.BlockManager(512, bs)
+    rng = np.random.default_rng(7)
+    system = rng.integers(0, 32000, size=320)  # 20 full blocks
+    prompts = {r: np.concatenate([system, rng.integers(0, 32000, size=200)]) for r in range(3)}
+    seqs = []
+    for r, prompt in prompts.items():
+        root = 1000 * (r + 1)
+        reused = bm.allocate_sequence_cached(root, prompt)
+        assert reused == (0 if r == 0 else 320)
+        bm.append_slots(root, token_ids=prompt[reused:])
+        for k in range(beams):
+            bm.fork(root, root + 1 + k)
+            seqs.append(root + 1 + k)
+        bm.free_sequence(root)
+    for s in seqs:
+        bm.append_slots(s, token_ids=rng.integers(0, 32000, size=5))
+    bm.take_copies()
+    tables, lens = bm.export_batch(seqs, pad=-1)
+    plan = ops.plan_shared_prefix(tables, lens, bs, min_group_seqs=beams, min_prefix_blocks=4, device=None)
+    assert plan.groups == 1 + len(prompts)
+    n = len(seqs)
+    gw = plan.host[6 + 2 * n:6 + 2 * n + 6 * plan.groups].reshape(-1, 6)
+    assert gw[0].tolist()[:3] == [20, 0, n] and gw[0][4] == 0 and gw[0][5] == -1
+    for child in gw[1:]:
+        prefix, _, count, _, start, parent = child.tolist()
+        assert (prefix, count, start, parent) == (520 // bs, beams, 20, 0)
+    assert plan.prefix_blocks().tolist() == [520 // bs] * n
