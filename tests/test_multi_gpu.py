@@ -210,3 +210,18 @@ def test_full_multi_sampled(name):
     _say(f"[multi-full] oracle on {len(seqs)} sequences")
     ref = oracle.paged_attend_causal(q, k_pool, v_pool, desc, tables, lens, starts, wl.scale)
     check_attention(out[rows], ref, wl.dtype, "bf16", f"{name}/full")
+
+
+def test_more_sequences_than_the_ranking_takes():
+    """300 sequences of 1-4 new tokens: the matrix-core kernel's natural-order
+    walk (longest-first ranking covers at most 256 sequences)."""
+    wl = generate("gqa-70b", num_seqs=300, ctx=(1, 60), num_heads=16, num_kv_heads=2, query_len=(1, 4))
+    gw = GpuWorkload(wl)
+    desc, k_pool, v_pool = oracle_pools(wl)
+    ref = oracle.paged_attend_causal(wl.q, k_pool, v_pool, desc, wl.block_tables, wl.context_lens, wl.query_start,
+                                     wl.scale)
+    for ptoks in (1 << 30, 32):
+        _say(f"[multi] 300 sequences, partition {ptoks}")
+        out = out_to_f64(gw.multi(kernel="mfma", partition_tokens=ptoks, blocks_in_flight=1, out_dtype=torch.float32))
+        torch.cuda.synchronize()
+        check_attention(out, ref, wl.dtype, "f32", f"300-seqs/multi/{ptoks}")

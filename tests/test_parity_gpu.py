@@ -274,3 +274,20 @@ def test_swap_blocks_gpu():
     oracle.swap_blocks(dev_k, dev_v, desc_dev, rk, rv, oracle.PoolDesc(4, s.num_kv_heads, s.block_size,
                                                                           s.head_dim, s.dtype), pairs[:1])
     assert np.array_equal(to_bits(k2), rk) and np.array_equal(to_bits(v2), rv)
+
+
+def test_more_sequences_than_the_ranking_takes():
+    """300 sequences: more than the decode kernels rank longest-first (one per
+    thread of a workgroup), so they walk in natural order; vector and
+    matrix-core kernels, single pass and partitioned."""
+    cases = (("mha", "vector", generate("mha-7b", num_seqs=300, ctx=(1, 60), num_heads=2, num_kv_heads=2)),
+             ("gqa", "mfma", generate("gqa-70b", num_seqs=300, ctx=(1, 60), num_heads=16, num_kv_heads=2)))
+    for name, kernel, wl in cases:
+        _say(f"[300 seqs] {name} {kernel}")
+        gw = GpuWorkload(wl)
+        desc, k_pool, v_pool = oracle_pools(wl)
+        ref = oracle.paged_decode(wl.q, k_pool, v_pool, desc, wl.block_tables, wl.context_lens, wl.scale)
+        for ptoks in (0, 32):
+            out = gw.decode(kernel=kernel, partition_tokens=ptoks, out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            check_attention(out_to_f64(out), ref, "bf16", "f32", f"300-seqs/{name}/{kernel}/{ptoks}")
