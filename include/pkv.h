@@ -129,13 +129,16 @@ typedef struct {
  * block ids agree; the group's prefix is the longest run of identical block ids
  * at the start of every member's table, counting only blocks fully inside every
  * member's context.  Groups with fewer than min_group_seqs members (at least 2)
- * or a prefix shorter than min_prefix_blocks are dropped.  Groups nest, as the
- * forks of a beam search leave them under a shared system prompt: members of
- * a group that agree on the block id right after its prefix form a child group
- * by the same rule, kept when it extends the blocks the parent's pass covers
- * (whole 64-token iterations) by at least min_prefix_blocks blocks and one
- * iteration; the child's pass starts where the parent's ends.  At most 4
- * levels.  Each sequence's prefix is that of its deepest group.
+ * or a prefix shorter than min_prefix_blocks are dropped; the members of a
+ * group dropped for a short run are searched again past it, so smaller sets
+ * that share a long run behind a short common start still form groups.
+ * Groups nest, as the forks of a beam search leave them under a shared system
+ * prompt: members of a group that agree on the block id right after its prefix
+ * form a child group by the same rule, kept when it extends the blocks the
+ * parent's pass covers (whole 64-token iterations) by at least
+ * min_prefix_blocks blocks and one iteration; the child's pass starts where the
+ * parent's ends.  At most 4 levels.  Each sequence's prefix is that of its
+ * deepest group.
  *
  *  block_tables  HOST [num_seqs][max_blocks_per_seq] int32
  *  context_lens  HOST [num_seqs] int32
@@ -168,7 +171,8 @@ size_t pkv_paged_attn_workspace_bytes(const pkv_pool_desc* pool, int32_t num_seq
  *  q             [num_seqs][num_heads][head_dim], pool->dtype
  *  k_pool/v_pool pools in the layout above
  *  block_tables  [num_seqs][max_blocks_per_seq] int32; entries past a
- *                sequence's last block are never read
+ *                sequence's last block may be read (they lie inside the row)
+ *                but are never used as block ids, so they may hold anything
  *  context_lens  [num_seqs] int32, each in [0, max_context_len]
  *  max_context_len  host-side upper bound of context_lens (<= max_blocks_per_seq*block_size)
  *  out_dtype     PKV_BF16 or PKV_F32 for bf16 inputs; PKV_F32 for f32 inputs

@@ -228,11 +228,14 @@ __global__ __launch_bounds__(64 * kWaves) void multi_mfma_kernel(DecodeArgs a) {
         t8[r] = __uint_as_float(sw[0]);
         t8[4 + r] = __uint_as_float(sw[1]);
       }
-      // the row's visible tokens (every one when the sub-tile ends before the tile's smallest limit)
-      const bool masked = tok0 + 16 > lim_min;
+      // the row's visible tokens (every one when the sub-tile ends before the tile's
+      // smallest limit and inside the partition).  A pair cut by the partition end
+      // (valid == 8) holds a repeat of its first block in tokens 8..15: those lie
+      // below the causal limit, so the partition bound must mask their logits too.
+      const bool masked = tok0 + 16 > lim_min || valid < 16;
       bool keep[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) keep[e] = !masked || tok0 + 8 * h + e < lim;
+      for (int e = 0; e < 8; ++e) keep[e] = !masked || (8 * h + e < valid && tok0 + 8 * h + e < lim);
 
       // raw logits; the scale (>= 0) is applied to the maximum and inside the exponent
       float v8[8];

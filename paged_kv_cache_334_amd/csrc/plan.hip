@@ -39,7 +39,8 @@ struct Planner {
   // Groups among `cands` (sorted) that share block ids beyond the parent's run
   // of `shared` blocks: candidates agreeing on the id at position `shared` form
   // a group when there are enough of them and their common run reaches far
-  // enough; each group then looks for its own children.
+  // enough; each group then looks for its own children, and a candidate whose
+  // run falls short is searched again from the end of that run.
   void split(const std::vector<int32_t>& cands, int32_t shared, int32_t parent, int level) {
     std::vector<int32_t> order;
     for (int32_t b : cands)
@@ -77,6 +78,13 @@ struct Planner {
           const std::vector<int32_t> members = g.members;
           groups.push_back(std::move(g));
           if (level + 1 < pkv::kMaxPrefixLevels) split(members, p, gi, level + 1);
+        } else {
+          // too short a common run: its members may still share long runs in
+          // smaller sets past it (a short common start, then diverging
+          // prompts); look for those at the same level, under the same parent.
+          // Every member agrees on ids [0, p], so the position grows and the
+          // search ends.
+          split(g.members, p, parent, level);
         }
       }
       i = j;

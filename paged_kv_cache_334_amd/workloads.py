@@ -8,26 +8,16 @@ reference counts, the slot of each appended token, and copy-on-write when a
 sequence appends into a block it shares.  Both the HIP path and the CPU oracle
 are fed from what it returns.
 
-Bookkeeping rules ("PagedAttention Explained", agentechip.com, section
-"Implementing a Simplified Paged KV Cache"):
-
-* a new block is taken from the front of the free list when a sequence's
-  length is a multiple of ``block_size``; an empty free list raises
-  an error (CacheExhausted);
-* the token goes to row ``length % block_size`` of the last block of the
-  sequence's table; here that becomes its slot ``block * block_size + row``;
-* freeing a sequence decrements each block's reference count and returns the
-  block to the free list at zero;
-* sequences that fork share blocks (reference count > 1); appending into a
-  shared last block first copies it to a fresh block ("Master Paged Attention
-  for LLM Inference", "How Paged Attention Works: The Mechanics", item 4).
+The bookkeeping lives in ``BlockPool`` (its docstring gives the rules and
+the passages they come from): whole runs of tokens are placed at once, so a
+workload of hundreds of thousands of cached tokens is laid out in a few
+array operations per sequence.
 
 Random inputs: NumPy PCG64 with one independent stream per purpose,
 ``default_rng([seed, purpose])``; values are float32 N(0, 1), rounded to
 bfloat16 by round-to-nearest-even on the bits.
 """
 
-from collections import deque
 from dataclasses import dataclass, field, replace
 from typing import List, Optional, Sequence, Tuple, Union
 
@@ -46,63 +36,110 @@ class CacheExhausted(RuntimeError):
     pass
 
 
-class BlockManager:
-    """Free list, block tables, reference counts and slots of a paged KV cache."""
+class BlockPool:
+    """Physical block ids of one paged cache and who holds them.
+
+    State: a FIFO of free ids (a ring over an int32 array: ids are taken from
+    its front and returned to its back), a holder count per id, and per
+    sequence its held ids in logical order plus its token count.  Requests are
+    served whole: ``extend`` reserves every slot of a run of tokens at once, or
+    raises ``CacheExhausted`` and changes nothing.
+
+    Rules (the slot rule is what ``reshape_and_cache`` consumes): the run's
+    tokens take rows ``position % block_size`` of the sequence's blocks, a new
+    block is taken each time a position is a multiple of ``block_size``
+    ("PagedAttention Explained", "Implementing a Simplified Paged KV Cache");
+    a run that starts inside a last block held by others first moves the
+    sequence to a private copy, queued as a (source, destination) pair
+    (copy-on-write: "Master Paged Attention for LLM Inference", "How Paged
+    Attention Works: The Mechanics", item 4); releasing a sequence drops its
+    hold on each block, and ids left with no holder go to the back of the FIFO
+    in the sequence's logical order.
+    """
 
     def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
-        self.num_blocks = num_blocks
-        self.block_size = block_size
-        order = range(num_blocks) if free_order is None else free_order
-        self.free = deque(int(b) for b in order)
-        self.ref = [0] * num_blocks
-        self.tables = {}
-        self.lengths = {}
-        self.pending_copies: List[Tuple[int, int]] = []
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        ring = np.arange(self.num_blocks, dtype=np.int32) if free_order is None else np.asarray(free_order, np.int32)
+        if ring.shape != (self.num_blocks,):
+            raise ValueError("free_order must list every block once")
+        self._ring = ring.copy()
+        self._head = 0
+        self._nfree = self.num_blocks
+        self.holders = np.zeros(self.num_blocks, dtype=np.int32)
+        self._held = {}  # sequence -> list of block ids, logical order
+        self._tokens = {}  # sequence -> token count
+        self._copies: List[Tuple[int, int]] = []
 
-    def _take(self) -> int:
-        if not self.free:
-            raise CacheExhausted("block pool is empty: cannot give the sequence a new block")
-        blk = self.free.popleft()
-        self.ref[blk] += 1
-        return blk
+    # -- the free FIFO ----------------------------------------------------------
+    @property
+    def free_count(self) -> int:
+        return self._nfree
 
-    def allocate_sequence(self, seq_id) -> None:
-        self.tables[seq_id] = []
-        self.lengths[seq_id] = 0
+    def free_ids(self) -> np.ndarray:
+        """Free ids, front of the FIFO first."""
+        return self._ring[(self._head + np.arange(self._nfree)) % self.num_blocks]
 
-    def fork(self, parent, child) -> None:
-        """``child`` starts with ``parent``'s tokens, sharing its blocks."""
-        self.tables[child] = list(self.tables[parent])
-        self.lengths[child] = self.lengths[parent]
-        for blk in self.tables[child]:
-            self.ref[blk] += 1
+    def _pop_front(self, k: int) -> np.ndarray:
+        ids = self._ring[(self._head + np.arange(k)) % self.num_blocks]
+        self._head = (self._head + k) % self.num_blocks
+        self._nfree -= k
+        self.holders[ids] += 1
+        return ids
 
-    def append_slot(self, seq_id) -> int:
-        """Reserve the slot of the sequence's next token and return it."""
-        length = self.lengths[seq_id]
-        row = length % self.block_size
-        table = self.tables[seq_id]
-        if row == 0:
-            table.append(self._take())
-        elif self.ref[table[-1]] > 1:
-            src = table[-1]
-            dst = self._take()
-            self.ref[src] -= 1
-            table[-1] = dst
-            self.pending_copies.append((src, dst))
-        self.lengths[seq_id] = length + 1
-        return table[-1] * self.block_size + row
+    def _push_back(self, ids: np.ndarray) -> None:
+        pos = (self._head + self._nfree + np.arange(len(ids))) % self.num_blocks
+        self._ring[pos] = ids
+        self._nfree += len(ids)
 
-    def free_sequence(self, seq_id) -> None:
-        for blk in self.tables[seq_id]:
-            self.ref[blk] -= 1
-            if self.ref[blk] == 0:
-                self.free.append(blk)
-        del self.tables[seq_id]
-        del self.lengths[seq_id]
+    # -- sequences --------------------------------------------------------------
+    def new_sequence(self, seq) -> None:
+        self._held[seq] = []
+        self._tokens[seq] = 0
 
-    def take_copies(self) -> List[Tuple[int, int]]:
-        pairs, self.pending_copies = self.pending_copies, []
+    def share_sequence(self, parent, child) -> None:
+        """``child`` holds every block of ``parent`` (its tokens so far)."""
+        held = list(self._held[parent])
+        self._held[child] = held
+        self._tokens[child] = self._tokens[parent]
+        self.holders[np.asarray(held, dtype=np.int64)] += 1
+
+    def extend(self, seq, n: int) -> np.ndarray:
+        """Slots (``block * block_size + row``) of the sequence's next ``n`` tokens."""
+        bs = self.block_size
+        held = self._held[seq]
+        first = self._tokens[seq]
+        grow = -(-(first + n) // bs) - len(held)  # blocks the run adds past the held ones
+        private = first % bs != 0 and n > 0 and self.holders[held[-1]] > 1
+        if grow + int(private) > self._nfree:
+            raise CacheExhausted(f"block pool is empty: {grow + int(private)} blocks wanted, {self._nfree} free")
+        if private:
+            src = held[-1]
+            dst = int(self._pop_front(1)[0])
+            self.holders[src] -= 1
+            held[-1] = dst
+            self._copies.append((int(src), dst))
+        if grow > 0:
+            held.extend(self._pop_front(grow).tolist())
+        self._tokens[seq] = first + n
+        pos = np.arange(first, first + n, dtype=np.int64)
+        return (np.asarray(held, dtype=np.int64)[pos // bs] * bs + pos % bs).astype(np.int32)
+
+    def release(self, seq) -> None:
+        ids = np.asarray(self._held.pop(seq), dtype=np.int64)
+        del self._tokens[seq]
+        self.holders[ids] -= 1
+        self._push_back(ids[self.holders[ids] == 0].astype(np.int32))
+
+    def table(self, seq) -> List[int]:
+        return list(self._held[seq])
+
+    def tokens(self, seq) -> int:
+        return self._tokens[seq]
+
+    def drain_copies(self) -> List[Tuple[int, int]]:
+        """Copy-on-write pairs queued since the last call, oldest first."""
+        pairs, self._copies = self._copies, []
         return pairs
 
 
@@ -135,6 +172,8 @@ class WorkloadSpec:
     cow_fraction: float = 0.0  # fraction of sequences whose last block was just forked
     outlier_fraction: float = 0.0  # key rows scaled by ``outlier_scale``
     outlier_scale: float = 8.0
+    # token positions [lo, hi) the outliers are drawn from (None: the sequence's own tokens)
+    outlier_window: Optional[Tuple[int, int]] = None
     pool_factor: float = 1.5
     num_blocks: Optional[int] = None  # fixed pool size instead of pool_factor
     scale: Optional[float] = None  # default 1/sqrt(head_dim)
@@ -331,56 +370,59 @@ def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overri
     if num_blocks < needed + 1:
         raise ValueError("pool too small")
     free_order = rng(_PERM).permutation(num_blocks)
-    mgr = BlockManager(num_blocks, bs, free_order)
+    pool = BlockPool(num_blocks, bs, free_order)
 
     # token order: the prefix common to all groups, the rest of each group's
-    # prefix (forked from it), then each sequence's own tokens
-    init_slots = []
-    init_owner = []  # (seq, or -1 - group for a prefix token, -1 - groups for a common one, position)
+    # prefix (its holder shares the common part), then each sequence's own
+    # tokens; each sequence's run of own tokens is one contiguous range of it
+    runs = []  # slot arrays, in token order
+    own_start = np.zeros(nseq, dtype=np.int64)  # token index of sequence b's first own token
+    count = 0
     if tree_blocks:
-        mgr.allocate_sequence(("tree",))
-        for pos in range(spec.tree_prefix):
-            init_slots.append(mgr.append_slot(("tree",)))
-            init_owner.append((-1 - groups, pos))
+        pool.new_sequence(("tree",))
+        runs.append(pool.extend(("tree",), spec.tree_prefix))
+        count += spec.tree_prefix
     for gi in range(groups):
         if tree_blocks:
-            mgr.fork(("tree",), ("prefix", gi))
+            pool.share_sequence(("tree",), ("prefix", gi))
         else:
-            mgr.allocate_sequence(("prefix", gi))
-        for pos in range(spec.tree_prefix if tree_blocks else 0, spec.shared_prefix):
-            init_slots.append(mgr.append_slot(("prefix", gi)))
-            init_owner.append((-1 - gi, pos))
+            pool.new_sequence(("prefix", gi))
+        n = spec.shared_prefix - (spec.tree_prefix if tree_blocks else 0)
+        runs.append(pool.extend(("prefix", gi), n))
+        count += n
     if tree_blocks:
-        mgr.free_sequence(("tree",))
+        pool.release(("tree",))
     for b in range(nseq):
         gi = prefix_group_of(spec, b)
         if gi >= 0:
-            mgr.fork(("prefix", gi), b)
+            pool.share_sequence(("prefix", gi), b)
         else:
-            mgr.allocate_sequence(b)
-        first = spec.shared_prefix if gi >= 0 else 0
-        for pos in range(first, int(ctx[b] - qlen[b])):
-            init_slots.append(mgr.append_slot(b))
-            init_owner.append((b, pos))
+            pool.new_sequence(b)
+        n = int(ctx[b] - qlen[b]) - (spec.shared_prefix if gi >= 0 else 0)
+        own_start[b] = count
+        runs.append(pool.extend(b, n))
+        count += n
     for gi in range(groups):
-        mgr.free_sequence(("prefix", gi))
-    for b in cow_seqs:  # an implicit sibling keeps referencing every block of b
-        mgr.fork(b, ("sibling", b))
+        pool.release(("prefix", gi))
+    for b in cow_seqs:  # an implicit sibling keeps holding every block of b
+        pool.share_sequence(b, ("sibling", b))
+    init_slots = np.concatenate(runs).astype(np.int32) if runs else np.zeros(0, np.int32)
     # the step: each sequence's new tokens (copy-on-write happens at the first)
-    new_slots = [mgr.append_slot(b) for b in range(nseq) for _ in range(int(qlen[b]))]
-    cow_pairs = np.asarray(mgr.take_copies(), dtype=np.int32).reshape(-1, 2)
+    new_slots = np.concatenate([pool.extend(b, int(qlen[b])) for b in range(nseq)]).astype(np.int32)
+    cow_pairs = np.asarray(pool.drain_copies(), dtype=np.int32).reshape(-1, 2)
 
     # block tables as the decode sees them
-    max_blocks = max(len(mgr.tables[b]) for b in range(nseq))
+    max_blocks = max(len(pool.table(b)) for b in range(nseq))
     if table_pad == "unused":
-        pad = int(mgr.free[0])
+        pad = int(pool.free_ids()[0])
     elif table_pad == "minus1":
         pad = -1
     else:
         raise ValueError(table_pad)
     tables = np.full((nseq, max_blocks), pad, dtype=np.int32)
     for b in range(nseq):
-        tables[b, : len(mgr.tables[b])] = mgr.tables[b]
+        held = pool.table(b)
+        tables[b, : len(held)] = held
 
     # token values, in the token order above, the new tokens last
     hkv, hd = spec.num_kv_heads, spec.head_dim
@@ -390,19 +432,22 @@ def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overri
     if spec.outlier_fraction > 0:
         key_scale = np.ones(total, dtype=np.float32)
         orng = rng(_OUTLIER)
-        index_of = {}
-        for i, (b, pos) in enumerate(init_owner):
-            index_of[(b, pos)] = i
-        for b in range(nseq):
-            for i in range(int(qlen[b])):
-                index_of[(b, int(ctx[b] - qlen[b]) + i)] = len(init_slots) + int(query_start[b]) + i
         for b in range(nseq):
             first = spec.shared_prefix if prefix_group_of(spec, b) >= 0 else 0
             n_out = int(np.floor(spec.outlier_fraction * (int(ctx[b]) - first)))
-            pos = np.sort(orng.choice(np.arange(first, int(ctx[b])), size=n_out, replace=False))
+            lo, hi = first, int(ctx[b])
+            if spec.outlier_window is not None:
+                lo, hi = max(lo, spec.outlier_window[0]), min(hi, spec.outlier_window[1])
+                if n_out > hi - lo:
+                    raise ValueError("outlier window holds fewer tokens than outliers")
+            pos = np.sort(orng.choice(np.arange(lo, hi), size=n_out, replace=False))
             outliers[b] = pos
-            for p in pos.tolist():
-                key_scale[index_of[(b, p)]] = spec.outlier_scale
+            # a cached own token's index follows its sequence's run; a new token's
+            # follows every cached one, in query-row order
+            cached = int(ctx[b] - qlen[b])
+            idx = np.where(pos < cached, own_start[b] + (pos - first),
+                           len(init_slots) + int(query_start[b]) + (pos - cached))
+            key_scale[idx] = spec.outlier_scale
     keys = _normal_bits(rng(_K), (total, hkv, hd), spec.dtype, scale_rows=key_scale)
     values = _normal_bits(rng(_V), (total, hkv, hd), spec.dtype)
     q = _normal_bits(rng(_Q), (len(new_slots), spec.num_heads, hd), spec.dtype)
@@ -417,10 +462,10 @@ def generate(spec: Union[str, WorkloadSpec], table_pad: str = "unused", **overri
         q=q,
         init_k=keys[:t0],
         init_v=values[:t0],
-        init_slots=np.asarray(init_slots, dtype=np.int32),
+        init_slots=init_slots,
         new_k=keys[t0:],
         new_v=values[t0:],
-        new_slots=np.asarray(new_slots, dtype=np.int32),
+        new_slots=new_slots,
         cow_pairs=cow_pairs,
         outlier_positions=outliers,
         query_start=query_start,

@@ -35,7 +35,7 @@ from logical_model import (
     slot_map,
     to_f64,
 )
-from paged_kv_cache_334_amd.workloads import BlockManager, Workload
+from paged_kv_cache_334_amd.workloads import BlockPool, Workload
 
 
 def pin_single_token(wl):
@@ -148,18 +148,18 @@ def private_copy(wl):
     values = np.concatenate([wl.init_v, wl.new_v])
     nseq = wl.spec.num_seqs
     total_blocks = int(sum(-(-int(n) // bs) for n in wl.context_lens)) + 1
-    mgr = BlockManager(total_blocks, bs)
+    pool = BlockPool(total_blocks, bs)
     rows, slots = [], []
     for b in range(nseq):
-        mgr.allocate_sequence(b)
+        pool.new_sequence(b)
         for p in range(int(wl.context_lens[b])):
             rows.append(smap[int(wl.block_tables[b, p // bs]) * bs + p % bs])
-            slots.append(mgr.append_slot(b))
-    max_blocks = max(len(mgr.tables[b]) for b in range(nseq))
-    pad = int(mgr.free[0])
+        slots.extend(pool.extend(b, int(wl.context_lens[b])).tolist())
+    max_blocks = max(len(pool.table(b)) for b in range(nseq))
+    pad = int(pool.free_ids()[0])
     tables = np.full((nseq, max_blocks), pad, dtype=np.int32)
     for b in range(nseq):
-        tables[b, : len(mgr.tables[b])] = mgr.tables[b]
+        tables[b, : len(pool.table(b))] = pool.table(b)
     rows = np.asarray(rows, dtype=np.int64)
     empty = keys[:0]
     return Workload(**{**wl.__dict__, "num_blocks": total_blocks, "block_tables": tables, "table_pad": pad,

@@ -151,25 +151,27 @@ def test_bad_prefix_block_gives_nan_rows_of_the_group_only():
     assert np.array_equal(out[others], good[others])
 
 
-def test_full_shared_prefix_workload_sampled():
+def test_full_shared_prefix_workload():
     """The full shared-prefix workload (200 sequences, 30000 shared tokens) in the
-    benchmark's launch configuration: cascade with the default plan thresholds."""
+    benchmark's launch configuration (cascade, default plan thresholds): every
+    sequence, one whole kv-head group each (the kv head rotating with the
+    sequence, so all of them are covered), in both output forms."""
     _say("[cascade] full shared-prefix build")
     wl = generate("shared-prefix")
     gw = GpuWorkload(wl)
     plan = ops.plan_shared_prefix(wl.block_tables, wl.context_lens, 16)
     assert plan.groups == 1
-    out = out_to_f64(gw.decode(prefix_plan=plan))
-    assert np.isfinite(out).all()
     desc, kp, vp = oracle_pools(wl)
-    rng = np.random.default_rng(5)
-    seqs = sorted({int(np.argmax(wl.context_lens)), int(np.argmin(wl.context_lens)),
-                   *rng.integers(0, 200, size=6).tolist()})
-    pairs = [(b, h) for b in seqs for h in rng.choice(32, size=4, replace=False).tolist()]
+    s = wl.spec
+    pairs = [(b, (b % s.num_kv_heads) * s.group + i) for b in range(s.num_seqs) for i in range(s.group)]
     _say(f"[cascade] full oracle on {len(pairs)} rows")
     ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale, pairs=pairs)
-    got = np.stack([out[b, h] for b, h in pairs])
-    check_attention(got, ref, "bf16", "bf16", "cascade/full")
+    for out_dtype in ("f32", "bf16"):
+        _say(f"[cascade] full shared-prefix out={out_dtype}")
+        out = out_to_f64(gw.decode(prefix_plan=plan, out_dtype=torch.float32 if out_dtype == "f32" else None))
+        assert np.isfinite(out).all()
+        got = np.stack([out[b, h] for b, h in pairs])
+        check_attention(got, ref, "bf16", out_dtype, f"cascade/full/{out_dtype}")
 
 
 def _nested(name):
@@ -231,25 +233,22 @@ def test_beam_tree_workload():
         check_attention(out_to_f64(out), ref, "bf16", out_dtype, "cascade/beam-tree-small")
 
 
-def test_full_beam_tree_workload_sampled():
+def test_full_beam_tree_workload():
     """The full beam-tree workload in the benchmark's launch configuration
-    (default plan thresholds), sampled rows against the oracle."""
+    (default plan thresholds): every row against the oracle, both output forms."""
     _say("[cascade] full beam-tree build")
     wl = generate("beam-tree")
     gw = GpuWorkload(wl)
     plan = ops.plan_shared_prefix(wl.block_tables, wl.context_lens, 16)
     assert plan.groups == 9
-    out = out_to_f64(gw.decode(prefix_plan=plan))
-    assert np.isfinite(out).all()
     desc, kp, vp = oracle_pools(wl)
-    rng = np.random.default_rng(6)
-    seqs = sorted({int(np.argmax(wl.context_lens)), int(np.argmin(wl.context_lens)),
-                   *rng.integers(0, 128, size=6).tolist()})
-    pairs = [(b, h) for b in seqs for h in rng.choice(32, size=4, replace=False).tolist()]
-    _say(f"[cascade] full beam-tree oracle on {len(pairs)} rows")
-    ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale, pairs=pairs)
-    got = np.stack([out[b, h] for b, h in pairs])
-    check_attention(got, ref, "bf16", "bf16", "cascade/full-beam-tree")
+    _say("[cascade] full beam-tree oracle, all rows")
+    ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale)
+    for out_dtype in ("f32", "bf16"):
+        _say(f"[cascade] full beam-tree out={out_dtype}")
+        out = out_to_f64(gw.decode(prefix_plan=plan, out_dtype=torch.float32 if out_dtype == "f32" else None))
+        assert np.isfinite(out).all()
+        check_attention(out, ref, "bf16", out_dtype, f"cascade/full-beam-tree/{out_dtype}")
 
 
 @pytest.mark.parametrize("seed", range(3))

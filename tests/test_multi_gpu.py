@@ -1,7 +1,7 @@
 """Several new tokens per sequence, causal among them (pkv_paged_attn_multi_token),
 on the GPU against the oracle's paged_attend_causal: small ragged cases on
-every kernel and partitioning, the broken-length paths, and the verify
-workload at full size on sampled rows."""
+every kernel and partitioning, the broken-length paths, and the verify and
+prompt-chunk workloads at full size."""
 
 import numpy as np
 import pytest
@@ -53,6 +53,11 @@ VARIANTS = [  # (kernel, partition tokens, blocks in flight)
     ("mfma", 1 << 30, 1),
     ("mfma", 32, 0),
     ("mfma", 96, 1),
+    # odd block counts per partition at 8-token blocks: the last pair of a
+    # partition has no second block, and its repeated first block must stay out
+    # of the softmax sum
+    ("mfma", 24, 1),
+    ("mfma", 40, 0),
     ("vector", 1 << 30, 0),
     ("vector", 48, 0),
 ]
@@ -193,23 +198,28 @@ def _sub_batch(wl, seqs):
     return rows, wl.q[rows], wl.block_tables[seqs], wl.context_lens[seqs], starts
 
 
+@pytest.mark.parametrize("out_dtype", ["same", "f32"])
 @pytest.mark.parametrize("name", sorted(MULTI_SPECS))
-def test_full_multi_sampled(name):
+def test_full_multi(name, out_dtype):
+    """Full-size workloads in the benchmark's launch configuration (automatic
+    plan).  The verify workload is compared on every row; the prompt chunks
+    (512 new tokens per sequence, one oracle attention per token) on their
+    longest and shortest sequences, which keeps the oracle within seconds."""
     _say(f"[multi-full] building {name}")
     wl = generate(MULTI_SPECS[name])
     gw = GpuWorkload(wl)
-    out = out_to_f64(gw.multi())  # the benchmark's launch configuration (automatic plan)
+    odt = torch.float32 if out_dtype == "f32" else None
+    out = out_to_f64(gw.multi(out_dtype=odt))
     assert np.isfinite(out).all()
     desc, k_pool, v_pool = oracle_pools(wl)
-    rng = np.random.default_rng(0)
-    seqs = {int(np.argmax(wl.context_lens)), int(np.argmin(wl.context_lens))}
-    if wl.max_query_len <= 64:  # long chunks: the two extreme sequences keep the oracle within seconds
-        seqs |= set(rng.integers(0, wl.spec.num_seqs, size=6).tolist())
-    seqs = sorted(seqs)
+    if wl.max_query_len <= 64:
+        seqs = list(range(wl.spec.num_seqs))
+    else:
+        seqs = sorted({int(np.argmax(wl.context_lens)), int(np.argmin(wl.context_lens))})
     rows, q, tables, lens, starts = _sub_batch(wl, seqs)
-    _say(f"[multi-full] oracle on {len(seqs)} sequences")
+    _say(f"[multi-full] oracle on {len(seqs)} sequences, {len(rows)} query rows")
     ref = oracle.paged_attend_causal(q, k_pool, v_pool, desc, tables, lens, starts, wl.scale)
-    check_attention(out[rows], ref, wl.dtype, "bf16", f"{name}/full")
+    check_attention(out[rows], ref, wl.dtype, "f32" if odt is not None else "bf16", f"{name}/full/{out_dtype}")
 
 
 def test_more_sequences_than_the_ranking_takes():

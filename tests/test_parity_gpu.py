@@ -4,8 +4,9 @@
   tokens), both pools must equal the oracle's pools bit for bit, every element
   (NaN-poisoned tails and unused blocks included).
 * Attention: every output of small cases that still span several blocks,
-  partitions and a ragged tail; sampled outputs at the full workload sizes in
-  the launch configuration the benchmark uses.  Tolerances in
+  partitions and a ragged tail; outputs at the full workload sizes in
+  the launch configuration the benchmark uses (every row; one whole kv-head
+  group per sequence on the shared-prefix workload).  Tolerances in
   gpu_harness.check_attention.
 """
 
@@ -186,6 +187,18 @@ def test_bad_block_id_gives_nan_not_a_fault():
 
 # ---- full sizes ---------------------------------------------------------------------
 
+def _full_pairs(wl):
+    """(sequence, query head) rows compared at full size: every row, except on
+    the shared-prefix workload, where each sequence gets one whole kv-head group
+    (the group's kv head rotating with the sequence, so every kv head is
+    covered): the oracle resolves 30000+ tokens per (sequence, kv head)."""
+    s = wl.spec
+    if not s.shared_prefix:
+        return None
+    g = s.group
+    return [(b, ((b % s.num_kv_heads) * g) + i) for b in range(s.num_seqs) for i in range(g)]
+
+
 @pytest.fixture(scope="module", params=ORDER)
 def full_case(request):
     name = request.param
@@ -194,45 +207,63 @@ def full_case(request):
     gw = GpuWorkload(wl)
     _say(f"[full] oracle pools {name}")
     pools = oracle_pools(wl)
-    return name, wl, gw, pools
-
-
-def _sample_pairs(wl, n=48, seed=0):
-    rng = np.random.default_rng(seed)
-    ctx = wl.context_lens
-    seqs = {int(np.argmax(ctx)), int(np.argmin(ctx))}
-    seqs |= set(rng.integers(0, wl.spec.num_seqs, size=n // 4).tolist())
-    pairs = set()
-    for b in seqs:
-        for h in rng.choice(wl.spec.num_heads, size=min(4, wl.spec.num_heads), replace=False).tolist():
-            pairs.add((b, int(h)))
-    first = int(np.argmax(ctx))
-    for h in range(wl.spec.num_heads):  # every head of the longest sequence
-        pairs.add((first, h))
-    return sorted(pairs)
+    desc, k_pool, v_pool = pools
+    pairs = _full_pairs(wl)
+    _say(f"[full] oracle attention {name} ({'all rows' if pairs is None else f'{len(pairs)} rows'})")
+    ref = oracle.paged_decode(wl.q, k_pool, v_pool, desc, wl.block_tables, wl.context_lens, wl.scale, pairs=pairs)
+    return name, wl, gw, pools, pairs, ref
 
 
 def test_full_cache_ops_bit_exact(full_case):
-    name, wl, gw, (desc, k_ref, v_ref) = full_case
+    name, wl, gw, (desc, k_ref, v_ref), _, _ = full_case
     _say(f"[full] cache ops {name}")
     assert np.array_equal(to_bits(gw.k_pool), k_ref), "key pool differs"
     assert np.array_equal(to_bits(gw.v_pool), v_ref), "value pool differs"
 
 
 @pytest.mark.parametrize("out_dtype", ["same", "f32"])
-def test_full_decode_sampled(full_case, out_dtype):
-    name, wl, gw, (desc, k_pool, v_pool) = full_case
+def test_full_decode(full_case, out_dtype):
+    """The benchmark's launch configuration (automatic plan) against the oracle
+    on every compared row."""
+    name, wl, gw, _, pairs, ref = full_case
     if out_dtype == "f32" and wl.dtype == "f32":
         pytest.skip("same")
     _say(f"[full] decode {name} out={out_dtype}")
     odt = torch.float32 if out_dtype == "f32" else None
-    out = out_to_f64(gw.decode(out_dtype=odt))  # the benchmark's launch configuration (automatic plan)
+    out = out_to_f64(gw.decode(out_dtype=odt))
     assert np.isfinite(out).all()
-    pairs = _sample_pairs(wl)
-    ref = oracle.paged_decode(wl.q, k_pool, v_pool, desc, wl.block_tables, wl.context_lens, wl.scale, pairs=pairs)
-    got = np.stack([out[b, h] for b, h in pairs])
+    got = out if pairs is None else np.stack([out[b, h] for b, h in pairs])
     check_attention(got, ref, wl.dtype, "f32" if (odt is not None or wl.dtype == "f32") else "bf16",
-                    f"{name}/full")
+                    f"{name}/full/{out_dtype}")
+
+
+# The long-context workload stresses the running maximum: its outlier keys (x8)
+# give logits far above the others.  Here every outlier of a sequence sits in
+# one window: the last split-K partition of the automatic plan (the reference
+# moves once, late, and every earlier partial is rescaled in the merge), or the
+# first (later partitions never reach its maximum).  Checked with the automatic
+# partition plan and with explicit partition lengths that cut the window into
+# several partitions.
+OUTLIER_WINDOWS = {"last-partition": (24576, 32768), "first-partition": (0, 8192)}
+
+
+@pytest.mark.parametrize("where", sorted(OUTLIER_WINDOWS))
+def test_long_context_outliers_in_one_partition(where):
+    _say(f"[outliers] building long-32k, outliers in the {where}")
+    wl = generate("long-32k", outlier_window=OUTLIER_WINDOWS[where])
+    lo, hi = OUTLIER_WINDOWS[where]
+    assert all(((p >= lo) & (p < hi)).all() and len(p) == 327 for p in wl.outlier_positions.values())
+    gw = GpuWorkload(wl)
+    desc, k_pool, v_pool = oracle_pools(wl)
+    _say(f"[outliers] oracle {where}")
+    ref = oracle.paged_decode(wl.q, k_pool, v_pool, desc, wl.block_tables, wl.context_lens, wl.scale)
+    for ptoks in (0, 2048, 1 << 30):
+        for out_dtype in ("f32", "same"):
+            _say(f"[outliers] {where} partition={ptoks} out={out_dtype}")
+            odt = torch.float32 if out_dtype == "f32" else None
+            out = out_to_f64(gw.decode(partition_tokens=ptoks, out_dtype=odt))
+            check_attention(out, ref, wl.dtype, "f32" if odt is not None else "bf16",
+                            f"outliers/{where}/{ptoks}/{out_dtype}")
 
 
 def test_swap_blocks_gpu():

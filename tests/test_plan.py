@@ -5,7 +5,8 @@ agree (each with at least min_prefix_blocks blocks fully inside its context);
 the group's prefix is the longest run of identical block ids at the start of
 every member's table, counting only blocks fully inside every member's
 context; groups below min_group_seqs members or min_prefix_blocks blocks are
-dropped.  Checked against a direct restatement of that rule and against the
+dropped, and the members of a group dropped for a short run are searched again
+from the end of that run.  Checked against a direct restatement of that rule and against the
 prefixes the seeded workloads build on purpose.
 """
 
@@ -47,6 +48,8 @@ def rule(tables, ctx, bs, min_group=2, min_prefix=1):
                 groups.append((p, members, start, parent))
                 if level + 1 < 4:
                     split(members, p, len(groups) - 1, level + 1)
+            else:  # a short common run: search its members again past it
+                split(members, p, parent, level)
 
     split(range(len(ctx)), 0, -1, 0)
     return groups
@@ -95,6 +98,35 @@ def test_planner_matches_the_rule_on_random_forests(seed):
         for b in range(nseq):
             assert group_of[b] == deepest.get(b, -1)
             assert prefix_of[b] == (want[deepest[b]][0] if b in deepest else 0)
+
+
+def test_long_runs_behind_a_short_common_start_are_found():
+    """Four sequences share only their first block; two pairs of them then share
+    30 more.  The four-member candidate is too short (1 < 8 blocks), but each
+    pair is a group of its own, found by searching past the short run."""
+    bs, mb = 16, 40
+    tables = np.arange(6 * mb, dtype=np.int32).reshape(6, mb) + 1000
+    tables[:4, 0] = 7
+    tables[1, 1:31] = tables[0, 1:31]
+    tables[3, 1:31] = tables[2, 1:31]
+    ctx = np.full(6, mb * bs, dtype=np.int32)
+    prefix_of, group_of, groups = parse(plan_words(tables, ctx, bs, 2, 8))
+    assert groups == [(31, [0, 1], 0, -1), (31, [2, 3], 0, -1)]
+    assert prefix_of.tolist() == [31, 31, 31, 31, 0, 0] and group_of.tolist() == [0, 0, 1, 1, -1, -1]
+    assert groups == rule(tables, ctx, bs, 2, 8)
+    # the same below a parent: all six share 9 blocks (the pass covers 8); four of
+    # them share 3 more (a child adding 4 < 8 blocks: dropped), and two pairs of
+    # those share up to block 31 (children of the root, found past the dropped run)
+    tables = np.arange(6 * mb, dtype=np.int32).reshape(6, mb) + 1000
+    tables[:, :9] = tables[0, :9]
+    tables[:4, 9:12] = tables[0, 9:12]
+    tables[1, 12:31] = tables[0, 12:31]
+    tables[3, 12:31] = tables[2, 12:31]
+    prefix_of, group_of, groups = parse(plan_words(tables, ctx, bs, 2, 8))
+    assert groups == rule(tables, ctx, bs, 2, 8)
+    assert sorted((g[0], g[1], g[2], g[3]) for g in groups) == [(9, [0, 1, 2, 3, 4, 5], 0, -1),
+                                                               (31, [0, 1], 8, 0), (31, [2, 3], 8, 0)]
+    assert prefix_of.tolist() == [31, 31, 31, 31, 9, 9]
 
 
 def test_shared_prefix_workload_is_one_group():
