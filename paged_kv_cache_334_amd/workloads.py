@@ -144,10 +144,17 @@ class BlockPool:
 
 
 def f32_to_bf16_bits(values: np.ndarray) -> np.ndarray:
-    """float32 -> bfloat16 bits, round to nearest, ties to even (finite input)."""
-    u = np.ascontiguousarray(values, dtype=np.float32).view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    """float32 -> bfloat16 bits, round to nearest, ties to even (finite input).
+
+    Adds 0x7FFF plus the lowest kept bit to the float32 bits and keeps the top
+    16 bits; done in place on one uint32 copy, the top halves read through a
+    uint16 view (little-endian: the high half of element i is half 2i+1)."""
+    u = np.array(values, dtype=np.float32, copy=True, order="C").view(np.uint32)
+    lsb = u >> np.uint32(16)
+    lsb &= np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    return u.view(np.uint16)[..., 1::2].copy()
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
