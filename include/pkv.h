@@ -189,6 +189,30 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
                                  void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts,
                                  void* stream);
 
+/*
+ * pkv_paged_attn_decode without a workspace argument and without any device
+ * allocation, for callers that cannot allocate: code recorded into a HIP graph,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results and errors as pkv_paged_attn_decode (same kernels, same plan), except
+ * that the split-K and shared-prefix partials go to a scratch array the library
+ * holds in device memory, one per GPU, for the life of the process
+ * (pkv_paged_attn_decode_scratch_limit() bytes: 64 MiB).  A call whose
+ * pkv_paged_attn_workspace_bytes() exceeds that returns PKV_EWORKSPACE before
+ * anything is launched.  The first call on a device looks up that device's
+ * array (no allocation).  Every call on one GPU shares its array: calls that
+ * overlap in time on one GPU (on different streams, or from different
+ * threads) race and must not be issued; calls in order on one stream are
+ * fine.  Nothing in the array needs clearing: every partial a call reads, the
+ * same call wrote first.
+ */
+pkv_status pkv_paged_attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                         int32_t max_context_len, const pkv_pool_desc* pool, float scale,
+                                         int32_t out_dtype, void* out, const pkv_decode_opts* opts, void* stream);
+/* Bytes of the per-GPU scratch array pkv_paged_attn_decode_noalloc uses. */
+size_t pkv_paged_attn_decode_scratch_limit(void);
+
 /* Bytes of workspace pkv_paged_attn_multi_token needs (0 for a single pass). */
 size_t pkv_paged_attn_multi_token_workspace_bytes(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_heads,
                                                   int32_t num_query_tokens, int32_t max_query_len,

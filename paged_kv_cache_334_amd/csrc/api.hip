@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -375,15 +376,16 @@ size_t pkv_paged_attn_workspace_bytes(const pkv_pool_desc* pool, int32_t num_seq
   return workspace_for(plan, num_seqs, num_heads, pool->head_dim);
 }
 
-pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
-                                 const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-                                 int32_t num_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
-                                 const pkv_pool_desc* pool, float scale, int32_t out_dtype, void* out,
-                                 void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts,
-                                 void* stream) {
-  Plan plan;
-  pkv_status st = make_plan(pool, num_seqs, num_heads, max_context_len, max_blocks_per_seq, opts, &plan);
-  if (st != PKV_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Decode with the plan already made (make_plan returned PKV_OK for these arguments).
+pkv_status decode_planned(const Plan& plan, const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                          int32_t num_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
+                          const pkv_pool_desc* pool, float scale, int32_t out_dtype, void* out, void* workspace,
+                          size_t workspace_bytes, const pkv_decode_opts* opts, void* stream) {
   if (num_seqs == 0) return ok();
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
     return fail(PKV_EINVAL, "a data pointer is NULL");
@@ -468,6 +470,77 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* 
     if (e != hipSuccess) return fail(PKV_EHIP, std::string("reduce launch: ") + hipGetErrorString(e));
   }
   return ok();
+}
+
+// Workspace of the allocation-free decode: one array in device memory per
+// GPU, part of the library's code object (each device that loads the library
+// holds its own copy until the process ends).  Its name is a host-side stand-in
+// in host code: kernels get the device address that hipGetSymbolAddress
+// returns, looked up once per device and kept.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+pkv_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_EUNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PKV_EHIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 const pkv_pool_desc* pool, float scale, int32_t out_dtype, void* out,
+                                 void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts,
+                                 void* stream) {
+  Plan plan;
+  pkv_status st = make_plan(pool, num_seqs, num_heads, max_context_len, max_blocks_per_seq, opts, &plan);
+  if (st != PKV_OK) return st;
+  return decode_planned(plan, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads, max_blocks_per_seq,
+                        max_context_len, pool, scale, out_dtype, out, workspace, workspace_bytes, opts, stream);
+}
+
+size_t pkv_paged_attn_decode_scratch_limit(void) { return kScratchBytes; }
+
+pkv_status pkv_paged_attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                         int32_t max_context_len, const pkv_pool_desc* pool, float scale,
+                                         int32_t out_dtype, void* out, const pkv_decode_opts* opts, void* stream) {
+  Plan plan;
+  pkv_status st = make_plan(pool, num_seqs, num_heads, max_context_len, max_blocks_per_seq, opts, &plan);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return ok();
+  const size_t need = workspace_for(plan, num_seqs, num_heads, pool->head_dim);
+  if (need > kScratchBytes)
+    return fail(PKV_EWORKSPACE, "the call needs " + std::to_string(need) + " bytes of workspace, above the " +
+                                    std::to_string(kScratchBytes) +
+                                    " of the library's scratch array; use pkv_paged_attn_decode with a workspace");
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_of_current_device(&ws);
+    if (st != PKV_OK) return st;
+  }
+  return decode_planned(plan, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads, max_blocks_per_seq,
+                        max_context_len, pool, scale, out_dtype, out, ws, need > 0 ? kScratchBytes : 0, opts, stream);
 }
 
 size_t pkv_paged_attn_multi_token_workspace_bytes(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_heads,

@@ -55,6 +55,13 @@ lib.pkv_paged_attn_decode.argtypes = [
     _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, ctypes.POINTER(PoolDesc), ctypes.c_float, _i32, _vp, _vp, _sz,
     ctypes.POINTER(DecodeOpts), _vp,
 ]
+lib.pkv_paged_attn_decode_noalloc.restype = _i32
+lib.pkv_paged_attn_decode_noalloc.argtypes = [
+    _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, ctypes.POINTER(PoolDesc), ctypes.c_float, _i32, _vp,
+    ctypes.POINTER(DecodeOpts), _vp,
+]
+lib.pkv_paged_attn_decode_scratch_limit.restype = _sz
+lib.pkv_paged_attn_decode_scratch_limit.argtypes = []
 lib.pkv_paged_attn_multi_token_workspace_bytes.restype = _sz
 lib.pkv_paged_attn_multi_token_workspace_bytes.argtypes = [ctypes.POINTER(PoolDesc), _i32, _i32, _i32, _i32, _i32,
                                                            ctypes.POINTER(DecodeOpts)]
@@ -262,6 +269,39 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=
                                    _ptr(out), _ptr(workspace), ws_bytes, ctypes.byref(opts), _stream(stream))
     _check(st, "pkv_paged_attn_decode")
     return out
+
+
+def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale, out, max_context_len=None,
+                              partition_tokens=0, kernel="auto", stream=None, blocks_in_flight=0, prefix_plan=None,
+                              heads_per_workgroup=0):
+    """``paged_attn_decode`` through pkv_paged_attn_decode_noalloc: no workspace
+    argument, nothing allocated (``out`` must be given); the partials go to the
+    library's per-GPU scratch array.  Calls must not overlap on one GPU."""
+    desc = pool_desc(k_pool, v_pool)
+    nseq, nh, hd = q.shape
+    if hd != desc.head_dim or _elem(q) != desc.dtype:
+        raise ValueError("q does not match the pools")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if not (q.is_contiguous() and block_tables.is_contiguous() and context_lens.is_contiguous()):
+        raise ValueError("q, block_tables and context_lens must be contiguous")
+    if tuple(out.shape) != (nseq, nh, hd) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Hq, D] tensor")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * desc.block_size
+    odt_code = PKV_BF16 if out.dtype == torch.bfloat16 else PKV_F32
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup)
+    st = lib.pkv_paged_attn_decode_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                           _ptr(context_lens), nseq, nh, max_blocks, int(max_context_len),
+                                           ctypes.byref(desc), float(scale), odt_code, _ptr(out), ctypes.byref(opts),
+                                           _stream(stream))
+    _check(st, "pkv_paged_attn_decode_noalloc")
+    return out
+
+
+def paged_attn_decode_scratch_limit() -> int:
+    return int(lib.pkv_paged_attn_decode_scratch_limit())
 
 
 def paged_attn_multi_token_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, num_query_tokens, max_query_len,

@@ -1,0 +1,95 @@
+"""pkv_paged_attn_decode_noalloc: the decode whose partials go to the
+library's per-GPU scratch array instead of a caller workspace.  Through the C
+ABI, against pkv_paged_attn_decode with a workspace (same kernels and plan, so
+bit-identical) and against the oracle; two calls in a row, the second smaller,
+so the second reads an array the first left full."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import GpuWorkload, check_attention, out_to_f64, to_bits
+from logical_model import oracle_pools
+from paged_kv_cache_334_amd.workloads import generate
+
+ops = pytest.importorskip("paged_kv_cache_334_amd.ops")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def test_oversized_request_is_rejected_before_launch():
+    """A call whose partials exceed the scratch array returns PKV_EWORKSPACE
+    from the host checks (nothing launched, no device touched)."""
+    limit = ops.paged_attn_decode_scratch_limit()
+    assert limit == 64 << 20
+    d = ops.PoolDesc(1 << 16, 8, 16, 128, ops.PKV_BF16)
+    opts = ops.DecodeOpts(16, 0, 0, 0, None, None, 0)  # 16-token partitions
+    nseq, nh, ctx = 512, 64, 4096
+    need = ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), nseq, nh, ctx, ctypes.byref(opts))
+    assert need > limit
+    p = ctypes.c_void_p(4096)
+    st = ops.lib.pkv_paged_attn_decode_noalloc(p, p, p, p, p, nseq, nh, ctx // 16, ctx, ctypes.byref(d), 0.1, 1, p,
+                                               ctypes.byref(opts), None)
+    assert st == 3 and "scratch" in ops.lib.pkv_last_error().decode()
+
+
+def _sub(wl, n, ctx_cap):
+    """The first n sequences, contexts cut to ctx_cap (a smaller second call)."""
+    ctx = np.minimum(wl.context_lens[:n], ctx_cap).astype(np.int32)
+    return ctx
+
+
+@pytest.mark.gpu
+def test_noalloc_matches_workspace_decode():
+    wl = generate("long-32k", num_seqs=4, ctx=(2000, 3000), num_heads=8, num_kv_heads=2, outlier_fraction=0.01)
+    gw = GpuWorkload(wl)
+    desc, kp, vp = oracle_pools(wl)
+    calls = [  # (label, sequences, context cap, partition tokens, out dtype)
+        ("split-K, 4 seqs", 4, 1 << 30, 256, torch.float32),
+        ("split-K, 2 seqs, shorter", 2, 900, 128, torch.float32),
+        ("split-K bf16 out, 3 seqs", 3, 2500, 512, torch.bfloat16),
+        ("single pass, 1 seq", 1, 1 << 30, 1 << 30, torch.float32),
+    ]
+    for label, n, cap, ptoks, odt in calls:
+        _say(f"[noalloc] {label}")
+        ctx = _sub(wl, n, cap)
+        q = gw.q[:n].contiguous()
+        tables = gw.block_tables[:n].contiguous()
+        ctx_dev = torch.from_numpy(ctx).cuda()
+        mx = int(ctx.max())
+        want = ops.paged_attn_decode(q, gw.k_pool, gw.v_pool, tables, ctx_dev, wl.scale, max_context_len=mx,
+                                     partition_tokens=ptoks, out_dtype=odt)
+        got = torch.full_like(want, 7.0)
+        ops.paged_attn_decode_noalloc(q, gw.k_pool, gw.v_pool, tables, ctx_dev, wl.scale, got, max_context_len=mx,
+                                      partition_tokens=ptoks)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(got), to_bits(want)), label
+        ref = oracle.paged_decode(wl.q[:n], kp, vp, desc, wl.block_tables[:n], ctx, wl.scale)
+        check_attention(out_to_f64(got), ref, "bf16", "f32" if odt == torch.float32 else "bf16", f"noalloc/{label}")
+
+
+@pytest.mark.gpu
+def test_noalloc_cascade_matches_workspace_decode():
+    """The shared-prefix pass's partials in the scratch array too: a larger
+    cascade call, then a smaller one."""
+    for label, kw in (("12 seqs", dict(num_seqs=12, shared_prefix=512, ctx=(16, 100))),
+                      ("5 seqs", dict(num_seqs=5, shared_prefix=256, ctx=(1, 40)))):
+        _say(f"[noalloc] cascade {label}")
+        wl = generate("shared-prefix", num_heads=8, num_kv_heads=2, cow_fraction=0.25, **kw)
+        gw = GpuWorkload(wl)
+        plan = ops.plan_shared_prefix(wl.block_tables, wl.context_lens, 16, min_group_seqs=2, min_prefix_blocks=1)
+        assert plan.groups == 1
+        want = gw.decode(prefix_plan=plan, out_dtype=torch.float32)
+        got = torch.full_like(want, 7.0)
+        ops.paged_attn_decode_noalloc(gw.q, gw.k_pool, gw.v_pool, gw.block_tables, gw.context_lens, wl.scale, got,
+                                      max_context_len=wl.max_context, prefix_plan=plan)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(got), to_bits(want)), label
+        desc, kp, vp = oracle_pools(wl)
+        ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale)
+        check_attention(out_to_f64(got), ref, "bf16", "f32", f"noalloc/cascade/{label}")
