@@ -15,7 +15,8 @@
 // Workgroup = 4 waves x 32 query rows (two 16-column MFMA tiles per wave).
 // Per iteration 64 prefix tokens: the next iteration's key and value tiles
 // travel from memory straight into the other LDS buffer (global_load_lds)
-// while the current one is computed (two buffers, one barrier per iteration).
+// while the current one is computed, and each wave then converts the values
+// it loaded to fp16 (two buffers, one barrier per iteration).
 // An iteration is two runs of 32 tokens (two 16-token blocks or one 32-token
 // block).  Each run's logits come from two S tiles whose 16 rows interleave:
 // tile X holds tokens 8j + 4X + r (j, r < 4), so after the product the lane of
@@ -25,10 +26,18 @@
 //  * S^T = K . Q^T, v_mfma_f32_16x16x32_bf16: A = keys (lane: the tile's row
 //    n, lane group kg -> 16-byte chunk 4i+kg), B = queries (lane: column n,
 //    dims 32i+8kg..+7); lane gets S^T[row 4kg+r][column n].
-//  * O^T += V^T . P^T over the run, v_mfma_f32_16x16x32_bf16: k = 8kg + j is
+//  * O^T += V^T . P^T over the run, v_mfma_f32_16x16x32_f16: k = 8kg + j is
 //    token 8kg + j, B = the lane's own 8 weights, A = values of dim 16nt+n at
-//    those tokens.  Weights go in as bf16 hi + lo parts (two instructions),
-//    keeping ~16 significant bits.
+//    those tokens.  Weights and values go in as fp16 (11 significant bits: a
+//    weight's rounding is at most 2^-12 relative, against 2^-9 for bf16, which
+//    the output tolerance could not take over 30000 tokens).  The values
+//    arrive as bf16 and are converted once per stage, in place in LDS, each
+//    wave the pieces it loaded; a bf16 value is exact in fp16 within fp16's
+//    range.  A
+//    stage holding a value fp16 cannot hold (|v| > 65504, or NaN) is staged again
+//    unconverted, and the workgroup finishes its chunk with bf16 values and
+//    weights split into bf16 hi + lo parts (two instructions, ~16 significant
+//    bits), the exact form for any input.
 // The LDS copy permutes 16-byte pieces so that both operand reads are free of
 // bank conflicts (measured with the hardware counter): within a key chunk row
 // the tokens of one S tile sit in 16 consecutive slots (key_slot_token), and a
@@ -78,6 +87,34 @@ __device__ __forceinline__ int key_slot_token(int s, int b) {
 // Piece of a 32-token value row stored at slot s of dim d (and the inverse).
 __device__ __forceinline__ int value_rot(int d) { return (d >> 1) & 3; }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two float32 -> packed fp16, round to nearest even (one v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// The 16 bytes of values at v (bf16, eight of them) converted to fp16 in
+// place.  Returns true when one of them has no finite fp16 copy (|v| > 65504,
+// an infinity or a NaN): a packed fma(h, 0, acc) over the converted values
+// turns NaN exactly then.
+__device__ __forceinline__ bool values_to_f16(unsigned char* v) {
+  uint4* piece = reinterpret_cast<uint4*>(v);
+  const uint4 w = *piece;
+  const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+  uint32_t h[4];
+  f16x2 acc = {0, 0};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = pack_f16(bf16_lo(x[e]), bf16_hi(x[e]));
+    acc = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, h[e]), f16x2{0, 0}, acc);
+  }
+  *piece = make_uint4(h[0], h[1], h[2], h[3]);
+  return __builtin_isnan(acc[0]) || __builtin_isnan(acc[1]);
+}
+
 template <int BS, int G>
 __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   constexpr int NB = TOK / BS;          // blocks per iteration
@@ -86,6 +123,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   static_assert(NB * TILE == STAGE_HALF, "stage size");
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][STAGE_HALF];  // [buffer][K=0/V=1]
+  // per stage parity and wave: a value of the wave's pieces has no finite fp16 copy
+  __shared__ int sm_big[2][NW];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -171,7 +210,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // each lane picks the global chunk that belongs at its spot).  The loads
   // take no registers; the wave waits for them with an explicit counter wait
   // before the barrier that publishes the buffer.
-  auto stage_issue = [&](int it, int buf) {
+  auto stage_issue = [&](int it, int buf, bool values_only) {
     const int first = blk_lo + it * NB;
     if (first - id_base >= 64) {  // next 64 ids
       id_base += 64;
@@ -185,8 +224,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       const int64_t base = (int64_t)__builtin_amdgcn_readlane(ids, first + kb - id_base) * block_bytes;
       const int q = in_tile / 16 + lane;  // 16-byte piece of the tile that this lane's LDS spot holds
       // keys: chunk q / BS, slot q % BS <- that chunk's key_slot_token
-      lds_dma16(lds_addr(&lds[buf][0][piece * 1024]), kpool + base,
-                ((q / BS) * BS + key_slot_token<BS>(q % BS, kb & 1)) * 16);
+      if (!values_only)
+        lds_dma16(lds_addr(&lds[buf][0][piece * 1024]), kpool + base,
+                  ((q / BS) * BS + key_slot_token<BS>(q % BS, kb & 1)) * 16);
       // values: 16-token rows keep the pool's order; 32-token rows are rotated
       const int d = q / (BS / 8);
       const int vpiece = BS == 32 ? ((q & 3) ^ value_rot(d)) : (q & 1);
@@ -194,20 +234,33 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     }
   };
 
-  f32x4 o[2][8];
+  // Accumulators: O^T per column tile, and a ninth tile that multiplies the
+  // weights by a row of ones, so each lane reads its column's weight sum there
+  // (the fp16 path's softmax denominator, from the same rounded weights as the
+  // numerator).  The exact path sums its weights in lsum (per lane, the
+  // lane's own tokens) instead; the two are added at the end.
+  f32x4 o[2][8], o1[2];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
+  for (int ct = 0; ct < 2; ++ct) {
+    o1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
-  // One iteration (64 tokens, always whole) of the wave's rows from LDS buffer
-  // `buf`.  Program order: S^T of both 32-token pairs (matrix cores), then per
-  // pair the online-softmax update and weights (vector unit) followed by its
-  // P.V (matrix cores).  The second pair's S^T runs while the first pair's
-  // weights are computed, and the first pair's P.V while the second's are.
-  auto compute = [&](int buf) {
-    f32x4 s[4][2];  // [run * 2 + S tile][column tile]
+  auto rescale = [&](int ct, float mn) {
+    const float alpha = fast_exp2(m[ct] - mn);
+    lsum[ct] *= alpha;
+    o1[ct] *= alpha;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) o[ct][nt] *= alpha;
+    m[ct] = mn;
+  };
+
+  // S^T of one iteration (64 tokens, always whole) from LDS buffer `buf`:
+  // s[run * 2 + S tile][column tile].
+  auto logits = [&](int buf, f32x4 (&s)[4][2]) {
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
       const unsigned char* kt = &lds[buf][0][(sub >> 1) * RUN_BYTES];
@@ -226,11 +279,114 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
           s[sub][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i], qb[ct][i], s[sub][ct], 0, 0, 0);
       }
     }
+  };
+  // value operand of dim 16nt + n, tokens 8kg..8kg+7 of run `pair`
+  auto value_piece = [&](int buf, int pair, int nt) {
+    const int d = 16 * nt + n;
+    const int off = BS == 32 ? d * 64 + 16 * (kg ^ value_rot(d)) : (kg >> 1) * TILE + d * 32 + 16 * (kg & 1);
+    return *reinterpret_cast<const uint4*>(&lds[buf][1][pair * RUN_BYTES] + off);
+  };
+
+  // Staging with fp16 values.  A wave's loads land the same 16 bytes in each
+  // lane that the lane later converts, so after its own counter wait a wave
+  // converts its pieces of the stage (its share: pieces wave + NW*k of the
+  // values) with no barrier in between, and the one barrier per iteration
+  // publishes keys and converted values together; waves that finish their
+  // products early convert while the others still compute.  A value without a
+  // finite fp16 copy (beyond fp16's range, or a NaN) anywhere in the stage
+  // turns the workgroup to the exact path for the rest of its chunk: the
+  // stage's values are staged again unconverted.  The flags are kept per
+  // stage parity, so a wave ahead by one stage never overwrites flags another
+  // wave has yet to read.
+  auto convert_own = [&](int stage, int buf) {
+    lds_dma_wait_all();
+    bool over = false;
+#pragma unroll
+    for (int k = 0; k < STAGE_HALF / 1024 / NW; ++k)
+      over |= values_to_f16(&lds[buf][1][(wave + NW * k) * 1024 + 16 * lane]);
+    // every lane stores the wave's flag (same value, same address): no branch
+    sm_big[stage & 1][wave] = __ballot(over) != 0;
+  };
+  // Fast path (fp16 values in LDS).  The reference m moves lazily: the
+  // weights 2^(s*scale - m) are formed with the current m and kept while all
+  // of them fit fp16 (below 2^16); the check is a packed fma(w, 0, acc), NaN
+  // once any weight is infinite.  Otherwise (the first iteration, a logit
+  // 16 or more above m, or a NaN logit) m moves to the iteration's column
+  // maximum, the accumulators are rescaled, and the weights are formed again.
+  // Weights then lie in (0, 2^16): fp16 keeps 11 bits of each down to 2^-14.
+  auto compute_fast = [&](int buf, int next, int next_buf) {
+    f32x4 s[4][2];
+    logits(buf, s);
+    uint32_t w[2][2][4];  // [run][column tile][pair of tokens]: fp16 weights, token 8kg + j of the run
+    auto weights = [&]() {
+      f16x2 ovf = {0, 0};
+#pragma unroll
+      for (int pair = 0; pair < 2; ++pair)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const float neg_m = -m[ct];
+          float pr[8];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pr[r] = fast_exp2(fmaf(s[2 * pair][ct][r], p.scale_log2, neg_m));
+            pr[4 + r] = fast_exp2(fmaf(s[2 * pair + 1][ct][r], p.scale_log2, neg_m));
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w[pair][ct][e] = pack_f16(pr[2 * e], pr[2 * e + 1]);
+            ovf = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, w[pair][ct][e]), f16x2{0, 0}, ovf);
+          }
+        }
+      return __ballot(__builtin_isnan(ovf[0]) || __builtin_isnan(ovf[1])) != 0;
+    };
+    if (weights()) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        float a = s[0][ct][0];
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) a = maxp(a, s[sub][ct][r]);
+        const float mx = maxp_xor32(maxp_xor16(a)) * p.scale_log2;  // the scale is >= 0
+        if (!(mx <= m[ct])) rescale(ct, maxp(m[ct], mx));
+      }
+      weights();
+    }
+#pragma unroll
+    for (int pair = 0; pair < 2; ++pair) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        o1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            ones, __builtin_bit_cast(f16x8, make_uint4(w[pair][ct][0], w[pair][ct][1], w[pair][ct][2], w[pair][ct][3])),
+            o1[ct], 0, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const f16x8 va = __builtin_bit_cast(f16x8, value_piece(buf, pair, nt));
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              va, __builtin_bit_cast(f16x8, make_uint4(w[pair][ct][0], w[pair][ct][1], w[pair][ct][2], w[pair][ct][3])),
+              o[ct][nt], 0, 0, 0);
+      }
+    }
+    // The next stage's values, converted in the same straight-line stretch as
+    // the value products: its loads come after theirs in program order (the
+    // buffers cannot be told apart at compile time, so its stores may not pass
+    // their loads), and its vector work fills the matrix cores' cycles.
+    convert_own(next, next_buf);
+  };
+
+  // Exact path (bf16 values in LDS): per 32-token run, the reference moves
+  // when a logit exceeds it by more than kRescaleSlack (weights below 2^8),
+  // and the weights enter the matrix cores as bf16 hi + lo parts.
+  auto compute_exact = [&](int buf) {
+    f32x4 s[4][2];
+    logits(buf, s);
 #pragma unroll
     for (int pair = 0; pair < 2; ++pair) {
       const f32x4* s0 = s[2 * pair];
       const f32x4* s1 = s[2 * pair + 1];
-      // column maxima of the pair's raw logits (the scale, > 0, is applied after)
+      // column maxima of the pair's raw logits (the scale, >= 0, is applied after)
       float mx[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
@@ -240,18 +396,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       }
       if (__ballot(mx[0] > m[0] + kRescaleSlack || mx[1] > m[1] + kRescaleSlack) != 0) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const float mn = maxp(m[ct], mx[ct]);
-          const float alpha = fast_exp2(m[ct] - mn);
-          lsum[ct] *= alpha;
-#pragma unroll
-          for (int nt = 0; nt < 8; ++nt) o[ct][nt] *= alpha;
-          m[ct] = mn;
-        }
+        for (int ct = 0; ct < 2; ++ct) rescale(ct, maxp(m[ct], mx[ct]));
       }
-      // weights as bf16 hi/lo operands: pr[j] is token 8kg + j of the run
-      // (tile 0's rows for j < 4, tile 1's for j >= 4)
-      bf16x8 pb_hi[2], pb_lo[2];
+      // weights: pr[j] is token 8kg + j of the run (tile 0's rows for j < 4, tile 1's for j >= 4)
+      uint32_t hw[2][4], lw[2][4];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const float neg_m = -m[ct];
@@ -262,36 +410,65 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
           pr[4 + r] = fast_exp2(fmaf(s1[ct][r], p.scale_log2, neg_m));
         }
         lsum[ct] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-        uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) split_bf16(pr[2 * e], pr[2 * e + 1], &hw[e], &lw[e]);
-        pb_hi[ct] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-        pb_lo[ct] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        for (int e = 0; e < 4; ++e) split_bf16(pr[2 * e], pr[2 * e + 1], &hw[ct][e], &lw[ct][e]);
       }
-      const unsigned char* vr = &lds[buf][1][pair * RUN_BYTES];
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        // dim 16nt + n, tokens 8kg..8kg+7 of the run
-        const int d = 16 * nt + n;
-        const int off = BS == 32 ? d * 64 + 16 * (kg ^ value_rot(d)) : (kg >> 1) * TILE + d * 32 + 16 * (kg & 1);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vr + off);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, value_piece(buf, pair, nt));
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb_hi[ct], o[ct][nt], 0, 0, 0);
-          o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb_lo[ct], o[ct][nt], 0, 0, 0);
+          const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(hw[ct][0], hw[ct][1], hw[ct][2], hw[ct][3]));
+          const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(lw[ct][0], lw[ct][1], lw[ct][2], lw[ct][3]));
+          o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, o[ct][nt], 0, 0, 0);
+          o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, o[ct][nt], 0, 0, 0);
         }
       }
     }
   };
 
-  stage_issue(0, 0);
-  lds_dma_wait_all();
+  auto stage_overflows = [&](int stage) {
+    bool any = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any |= sm_big[stage & 1][w] != 0;
+    return any;
+  };
+  auto restage_values = [&](int stage, int buf) {
+    stage_issue(stage, buf, true);
+    lds_dma_wait_all();
+    __syncthreads();
+  };
+
+  // The exact path is a loop of its own that the fast one hands over to: one
+  // loop body holding both would need more registers than two waves per SIMD
+  // leave.
+  stage_issue(0, 0, false);
+  convert_own(0, 0);
   __syncthreads();
-  for (int it = 0; it < iters; ++it) {
+  int it = 0;
+  if (stage_overflows(0)) {
+    restage_values(0, 0);
+  } else {
+    for (; it < iters; ++it) {
+      const int buf = it & 1;
+      const bool more = it + 1 < iters;
+      if (more) stage_issue(it + 1, buf ^ 1, false);  // buffer buf^1 was released by the last barrier
+      // after the last stage the conversion runs on the other buffer's old
+      // contents, which nothing reads again, and its flag is not looked at
+      if (wave_active) compute_fast(buf, it + 1, buf ^ 1);
+      else convert_own(it + 1, buf ^ 1);
+      __syncthreads();
+      if (more && stage_overflows(it + 1)) {
+        restage_values(it + 1, buf ^ 1);
+        ++it;  // stage it + 1 holds its values unconverted: the exact loop goes on from there
+        break;
+      }
+    }
+  }
+  for (; it < iters; ++it) {
     const int buf = it & 1;
-    const bool more = it + 1 < iters;
-    if (more) stage_issue(it + 1, buf ^ 1);  // buffer buf^1 was released by the last barrier
-    if (wave_active) compute(buf);
+    if (it + 1 < iters) stage_issue(it + 1, buf ^ 1, false);
+    if (wave_active) compute_exact(buf);
     lds_dma_wait_all();
     __syncthreads();
   }
@@ -300,7 +477,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // partials: row -> (member sequence, query head); slot (b, h, chunk)
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
-    const float l = sum_xor32(sum_xor16(lsum[ct]));
+    const float l = sum_xor32(sum_xor16(lsum[ct])) + o1[ct][0];
     const int row = row0 + 16 * ct + n;
     if (row >= rows) continue;
     const int b = members[row / G];

@@ -151,6 +151,41 @@ def test_bad_prefix_block_gives_nan_rows_of_the_group_only():
     assert np.array_equal(out[others], good[others])
 
 
+@pytest.mark.parametrize("bits,label", [(0x477F, "65280-in-fp16-range"), (0x4780, "65536-beyond-fp16"),
+                                        (0xC780, "minus-65536-beyond-fp16")])
+def test_prefix_values_near_the_fp16_limit(bits, label):
+    """The prefix pass multiplies weights and values in fp16, converting each
+    stage's bf16 values in LDS.  A value the fp16 range holds (65280, the
+    largest bf16 below 65504) goes through the fast path unchanged; one beyond
+    it (+-65536) must send its workgroup to the exact bf16 path for the rest of
+    its chunk (an fp16 copy would be infinite).  A few value elements of the
+    shared prefix are set to that value, in different stages and chunks."""
+    wl = generate("shared-prefix", num_seqs=12, shared_prefix=1024, ctx=(16, 100), num_heads=8, num_kv_heads=2,
+                  cow_fraction=0.25)
+    v = wl.init_v.copy()
+    for tok, h, d in ((70, 0, 3), (500, 1, 77), (900, 0, 127)):  # prefix tokens come first in token order
+        v[tok, h, d] = bits
+    wl.init_v = v
+    gw = GpuWorkload(wl)
+    desc, kp, vp = oracle_pools(wl)
+    ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale)
+    plan = ops.plan_shared_prefix(wl.block_tables, wl.context_lens, 16, min_group_seqs=2, min_prefix_blocks=1)
+    assert plan.groups == 1
+    _say(f"[cascade] prefix value {label}")
+    out = out_to_f64(gw.decode(prefix_plan=plan, out_dtype=torch.float32))
+    assert np.isfinite(out).all(), label
+    # Outputs reach ~1e2 here, so the bound scales with them.  An fp16 weight
+    # keeps 11 significant bits (rounding <= 2^-12 relative) down to 2^-14, below
+    # that an absolute 2^-25, so a product with |v| <= 65280 is off by at most
+    # 2^-12 of itself or 2e-3 absolute; the exact path keeps ~16 bits.  R9's
+    # relative bound (1e-2) holds with room either way.
+    err = np.abs(out - ref)
+    assert (err <= 2e-3 + 2e-3 * np.abs(ref)).all(), f"{label}: max abs {err.max():.3g}"
+    assert np.abs(ref).max() > 10.0  # the large values did reach the output
+    b = out_to_f64(gw.decode(prefix_plan=plan))
+    check_attention(b, ref, "bf16", "bf16", f"cascade/{label}")
+
+
 def test_full_shared_prefix_workload():
     """The full shared-prefix workload (200 sequences, 30000 shared tokens) in the
     benchmark's launch configuration (cascade, default plan thresholds): every
