@@ -73,9 +73,9 @@ typedef enum {
  * or 128, dtype PKV_F32 or PKV_BF16, num_blocks*block_size < 2^31.  Smaller
  * blocks leave less of a sequence's last block unused but mean more table
  * entries per token; larger ones the reverse ("PagedAttention Explained",
- * "Best Practices", "Choose the Right Block Size").  The shared-prefix pass
- * takes blocks of 16 or 32 tokens; every other kernel takes all three (the
- * matrix-core ones walk 8-token blocks in pairs). */
+ * "Best Practices", "Choose the Right Block Size").  Every kernel takes all
+ * three (the matrix-core decode kernels walk 8-token blocks in pairs; the
+ * shared-prefix pass reads four 8-token blocks per 32-token run). */
 typedef struct {
   int32_t num_blocks;
   int32_t num_kv_heads;

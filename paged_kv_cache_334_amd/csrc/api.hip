@@ -99,8 +99,8 @@ pkv_status plan_cascade(const pkv_pool_desc* pool, int32_t num_seqs, int32_t max
     return fail(PKV_EINVAL, "prefix plan: truncated");
   if (!opts->prefix_plan_dev) return fail(PKV_EINVAL, "prefix plan: device copy missing");
   if (groups == 0) return PKV_OK;
-  if (pool->dtype != PKV_BF16 || pool->head_dim != 128 || pool->block_size < 16)
-    return fail(PKV_EUNSUPPORTED, "cascade decode needs bf16 pools with head_dim 128 and blocks of 16 or 32 tokens");
+  if (pool->dtype != PKV_BF16 || pool->head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "cascade decode needs bf16 pools with head_dim 128");
   // every index the kernels take from the plan is checked here, once, on the host
   const int bs = pool->block_size;
   const int32_t* start = w + pkv::kPlanHeader;

@@ -17,8 +17,8 @@
 // travel from memory straight into the other LDS buffer (global_load_lds)
 // while the current one is computed, and each wave then converts the values
 // it loaded to fp16 (two buffers, one barrier per iteration).
-// An iteration is two runs of 32 tokens (two 16-token blocks or one 32-token
-// block).  Each run's logits come from two S tiles whose 16 rows interleave:
+// An iteration is two runs of 32 tokens (four 8-token blocks, two 16-token
+// blocks or one 32-token block).  Each run's logits come from two S tiles whose 16 rows interleave:
 // tile X holds tokens 8j + 4X + r (j, r < 4), so after the product the lane of
 // group kg owns tokens 8kg..8kg+7 of the run across the two tiles, exactly the
 // 8 contraction indices it supplies to P.V, and the value operand is one
@@ -86,6 +86,15 @@ __device__ __forceinline__ int key_slot_token(int s, int b) {
 }
 // Piece of a 32-token value row stored at slot s of dim d (and the inverse).
 __device__ __forceinline__ int value_rot(int d) { return (d >> 1) & 3; }
+
+// 8-token blocks: a 32-token run is four blocks, and one S tile's 16 lanes read
+// four tokens of each (tokens 4X..4X+3 of block n / 4), whose tiles lie 2 KiB
+// apart, i.e. on the same banks.  Block b of the run keeps key chunk c in chunk
+// row c ^ (b & 1) and token t in slot t ^ 4(b >> 1) of that row, so the
+// sixteen 16-byte reads cover sixteen different slots of a 256-byte bank row.
+// Involutive: the same map takes a stored position to the pool's.
+__device__ __forceinline__ int key8_row(int c, int b) { return c ^ (b & 1); }
+__device__ __forceinline__ int key8_slot(int t, int b) { return t ^ (4 * ((b >> 1) & 1)); }
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -223,13 +232,16 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       const int in_tile = piece * 1024 % TILE;
       const int64_t base = (int64_t)__builtin_amdgcn_readlane(ids, first + kb - id_base) * block_bytes;
       const int q = in_tile / 16 + lane;  // 16-byte piece of the tile that this lane's LDS spot holds
-      // keys: chunk q / BS, slot q % BS <- that chunk's key_slot_token
-      if (!values_only)
-        lds_dma16(lds_addr(&lds[buf][0][piece * 1024]), kpool + base,
-                  ((q / BS) * BS + key_slot_token<BS>(q % BS, kb & 1)) * 16);
-      // values: 16-token rows keep the pool's order; 32-token rows are rotated
+      // keys: chunk q / BS, slot q % BS <- that chunk's key_slot_token (16/32-token
+      // blocks), or the swizzled row and slot of 8-token blocks
+      if (!values_only) {
+        const int kq = BS == 8 ? key8_row(q / 8, kb & 3) * 8 + key8_slot(q % 8, kb & 3)
+                               : (q / BS) * BS + key_slot_token<BS>(q % BS, kb & 1);
+        lds_dma16(lds_addr(&lds[buf][0][piece * 1024]), kpool + base, kq * 16);
+      }
+      // values: 8- and 16-token rows keep the pool's order; 32-token rows are rotated
       const int d = q / (BS / 8);
-      const int vpiece = BS == 32 ? ((q & 3) ^ value_rot(d)) : (q & 1);
+      const int vpiece = BS == 32 ? ((q & 3) ^ value_rot(d)) : BS == 16 ? (q & 1) : 0;
       lds_dma16(lds_addr(&lds[buf][1][piece * 1024]), vpool + base, d * (BS * 2) + vpiece * 16);
     }
   };
@@ -266,11 +278,20 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       const unsigned char* kt = &lds[buf][0][(sub >> 1) * RUN_BYTES];
       const int x = sub & 1;
       // the lane's row n of tile x: 32-token blocks slot 16x + n; 16-token blocks
-      // block n / 8 of the run, slot n % 8 + 8 (x ^ block)
-      const int koff = BS == 32 ? 16 * x + n : (n >> 3) * (TILE / 16) + (n & 7) + 8 * (x ^ (n >> 3));
+      // block n / 8 of the run, slot n % 8 + 8 (x ^ block); 8-token blocks block
+      // n / 4, token 4x + n % 4 (in its swizzled row and slot)
       bf16x8 ka[4];
+      if constexpr (BS == 8) {
+        const int b = n >> 2;
+        const int slot = key8_slot(4 * x + (n & 3), b);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kt + ((4 * i + kg) * BS + koff) * 16);
+        for (int i = 0; i < 4; ++i)
+          ka[i] = *reinterpret_cast<const bf16x8*>(kt + b * TILE + (key8_row(4 * i + kg, b) * 8 + slot) * 16);
+      } else {
+        const int koff = BS == 32 ? 16 * x + n : (n >> 3) * (TILE / 16) + (n & 7) + 8 * (x ^ (n >> 3));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kt + ((4 * i + kg) * BS + koff) * 16);
+      }
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -283,7 +304,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // value operand of dim 16nt + n, tokens 8kg..8kg+7 of run `pair`
   auto value_piece = [&](int buf, int pair, int nt) {
     const int d = 16 * nt + n;
-    const int off = BS == 32 ? d * 64 + 16 * (kg ^ value_rot(d)) : (kg >> 1) * TILE + d * 32 + 16 * (kg & 1);
+    const int off = BS == 32   ? d * 64 + 16 * (kg ^ value_rot(d))
+                    : BS == 16 ? (kg >> 1) * TILE + d * 32 + 16 * (kg & 1)
+                               : kg * TILE + d * 16;  // 8-token blocks: tokens 8kg.. are block kg
     return *reinterpret_cast<const uint4*>(&lds[buf][1][pair * RUN_BYTES] + off);
   };
 
@@ -506,7 +529,15 @@ hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, hipStre
   const dim3 grid((unsigned)wgs);
   const dim3 block(64 * NW);
 #define PKV_PREFIX(BS, G) hipLaunchKernelGGL((prefix_kernel<BS, G>), grid, block, 0, s, p)
-  if (block_size == 16) {
+  if (block_size == 8) {
+    switch (group) {
+      case 1: PKV_PREFIX(8, 1); break;
+      case 2: PKV_PREFIX(8, 2); break;
+      case 4: PKV_PREFIX(8, 4); break;
+      case 8: PKV_PREFIX(8, 8); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (block_size == 16) {
     switch (group) {
       case 1: PKV_PREFIX(16, 1); break;
       case 2: PKV_PREFIX(16, 2); break;

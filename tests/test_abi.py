@@ -274,7 +274,7 @@ def test_multi_token_workspace(ops):
 
 def test_block_size_8(ops):
     """8-token blocks are accepted by the decode and multi-token kernels (the
-    matrix-core ones walk them in pairs); the shared-prefix pass refuses them."""
+    matrix-core ones walk them in pairs) and by the shared-prefix pass."""
     d = _desc(ops, block_size=8)
     single = ops.DecodeOpts(1 << 30, 0, 0)
     assert ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(single)) == 0
@@ -285,5 +285,5 @@ def test_block_size_8(ops):
     assert need > 0
     plan = (ctypes.c_int32 * 22)(0x32564b50, 4, 8, 1, 16, 2, 16, 16, 0, 0, 0, 0, -1, -1, 16, 0, 2, 0, 0, -1, 0, 1)
     opts = ops.DecodeOpts(0, 0, 0, 0, ctypes.addressof(plan), 16, 22)
-    assert _decode(ops, d, opts=opts, max_blocks=32) == 2
-    assert "16 or 32" in ops.lib.pkv_last_error().decode()
+    assert _decode(ops, d, opts=opts, max_blocks=32) == 3  # plan accepted, stops at the workspace check
+    assert "workspace" in ops.lib.pkv_last_error().decode()

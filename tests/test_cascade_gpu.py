@@ -46,6 +46,13 @@ CASES = {
                                           num_heads=8, num_kv_heads=2),
     "g2-bs32-remainder": lambda: generate("shared-prefix", num_seqs=7, shared_prefix=480, ctx=(5, 60),
                                           num_heads=4, num_kv_heads=2, block_size=32),
+    # 8-token blocks (a 32-token run of the prefix pass spans four blocks): group 4
+    # with copy-on-write; group 8 with a prefix that is not a whole number of
+    # 64-token iterations (the suffix pass reads the last 4 prefix blocks)
+    "g4-bs8": lambda: generate("shared-prefix", num_seqs=12, shared_prefix=512, ctx=(16, 100), num_heads=8,
+                               num_kv_heads=2, cow_fraction=0.25, block_size=8),
+    "g8-bs8-remainder": lambda: generate("shared-prefix", num_seqs=10, shared_prefix=352, ctx=(1, 60),
+                                         num_heads=16, num_kv_heads=2, block_size=8),
     # more rows than one 128-row tile (150 x 4 = 600 rows), a long prefix split into several chunks
     "g4-many-rows": lambda: generate("shared-prefix", num_seqs=150, shared_prefix=2048, ctx=(1, 40), num_heads=8,
                                      num_kv_heads=2),
@@ -293,7 +300,7 @@ def test_random_beam_trees_match_oracle(seed):
     from beam_tree import random_tree
 
     rng = np.random.default_rng(200 + seed)
-    bs = (16, 32, 16)[seed]
+    bs = (16, 32, 8)[seed]
     wl = generate("shared-prefix", num_seqs=24, shared_prefix=64 * bs, ctx=(1, 40), num_heads=8, num_kv_heads=2,
                   block_size=bs, seed=seed, cow_fraction=0.2)
     random_tree(wl.block_tables, list(rng.permutation(24)), 64, rng)
