@@ -42,6 +42,8 @@
 // bank conflicts (measured with the hardware counter): within a key chunk row
 // the tokens of one S tile sit in 16 consecutive slots (key_slot_token), and a
 // 32-token value row has its four pieces rotated by bits 1-2 of the dim.
+#include <type_traits>
+
 #include "decode_common.h"
 
 namespace pkv {
@@ -53,6 +55,7 @@ constexpr int TOK = kPrefixIterTokens;  // prefix tokens per iteration
 constexpr int NW = kWaves;        // 4
 constexpr int ROWS_PER_WAVE = 32; // two MFMA column tiles
 constexpr int STAGE_HALF = TOK * HD * 2;  // bytes of keys (or values) per iteration: 16 KiB
+constexpr int kPiecesPerWave = STAGE_HALF / 1024 / NW;  // 1 KiB loads per wave per stage, keys (and values): 4
 
 // LDS byte address of a __shared__ location.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -73,6 +76,12 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds, const void* gbase, uint3
       : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of the wave's vector-memory loads are outstanding (the
+// oldest complete first).
+template <int N>
+__device__ __forceinline__ void lds_dma_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Token (inside its block) whose key piece sits in slot s of an LDS key chunk
 // row.  32-token blocks: slots 0-15 hold S tile 0's rows in order, 16-31 tile
@@ -131,9 +140,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   constexpr int RUN_BYTES = 32 * HD * 2; // one 32-token run of keys (or values)
   static_assert(NB * TILE == STAGE_HALF, "stage size");
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][STAGE_HALF];  // [buffer][K=0/V=1]
-  // per stage parity and wave: a value of the wave's pieces has no finite fp16 copy
-  __shared__ int sm_big[2][NW];
+  // Keys in two buffers, values in three: a stage's keys are used one
+  // iteration before its values (its logits are computed while the previous
+  // stage's weights are formed), so values stay one iteration longer.  80 KiB:
+  // two workgroups fill the CU's 160 KiB, with nothing else in LDS.
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf[2][STAGE_HALF];
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf[3][STAGE_HALF];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -219,31 +231,36 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // each lane picks the global chunk that belongs at its spot).  The loads
   // take no registers; the wave waits for them with an explicit counter wait
   // before the barrier that publishes the buffer.
-  auto stage_issue = [&](int it, int buf, bool values_only) {
+  auto stage_issue = [&](int it, int kb_i, int vb_i) {
     const int first = blk_lo + it * NB;
     if (first - id_base >= 64) {  // next 64 ids
       id_base += 64;
       ids = load_ids(id_base);
     }
+    // all of the stage's key loads first, then its value loads: the waits below
+    // count on that order (keys are needed an iteration before the values)
 #pragma unroll
-    for (int k = 0; k < STAGE_HALF / 1024 / NW; ++k) {
-      const int piece = wave + NW * k;  // 1 KiB piece of the stage
-      const int kb = piece * 1024 / TILE;
-      const int in_tile = piece * 1024 % TILE;
-      const int64_t base = (int64_t)__builtin_amdgcn_readlane(ids, first + kb - id_base) * block_bytes;
-      const int q = in_tile / 16 + lane;  // 16-byte piece of the tile that this lane's LDS spot holds
-      // keys: chunk q / BS, slot q % BS <- that chunk's key_slot_token (16/32-token
-      // blocks), or the swizzled row and slot of 8-token blocks
-      if (!values_only) {
-        const int kq = BS == 8 ? key8_row(q / 8, kb & 3) * 8 + key8_slot(q % 8, kb & 3)
-                               : (q / BS) * BS + key_slot_token<BS>(q % BS, kb & 1);
-        lds_dma16(lds_addr(&lds[buf][0][piece * 1024]), kpool + base, kq * 16);
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int k = 0; k < kPiecesPerWave; ++k) {
+        const int piece = wave + NW * k;  // 1 KiB piece of the stage
+        const int kb = piece * 1024 / TILE;
+        const int in_tile = piece * 1024 % TILE;
+        const int64_t base = (int64_t)__builtin_amdgcn_readlane(ids, first + kb - id_base) * block_bytes;
+        const int q = in_tile / 16 + lane;  // 16-byte piece of the tile that this lane's LDS spot holds
+        if (half == 0) {
+          // keys: chunk q / BS, slot q % BS <- that chunk's key_slot_token (16/32-token
+          // blocks), or the swizzled row and slot of 8-token blocks
+          const int kq = BS == 8 ? key8_row(q / 8, kb & 3) * 8 + key8_slot(q % 8, kb & 3)
+                                 : (q / BS) * BS + key_slot_token<BS>(q % BS, kb & 1);
+          lds_dma16(lds_addr(&kbuf[kb_i][piece * 1024]), kpool + base, kq * 16);
+        } else {
+          // values: 8- and 16-token rows keep the pool's order; 32-token rows are rotated
+          const int d = q / (BS / 8);
+          const int vpiece = BS == 32 ? ((q & 3) ^ value_rot(d)) : BS == 16 ? (q & 1) : 0;
+          lds_dma16(lds_addr(&vbuf[vb_i][piece * 1024]), vpool + base, d * (BS * 2) + vpiece * 16);
+        }
       }
-      // values: 8- and 16-token rows keep the pool's order; 32-token rows are rotated
-      const int d = q / (BS / 8);
-      const int vpiece = BS == 32 ? ((q & 3) ^ value_rot(d)) : BS == 16 ? (q & 1) : 0;
-      lds_dma16(lds_addr(&lds[buf][1][piece * 1024]), vpool + base, d * (BS * 2) + vpiece * 16);
-    }
   };
 
   // Accumulators: O^T per column tile, and a ninth tile that multiplies the
@@ -272,10 +289,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
 
   // S^T of one iteration (64 tokens, always whole) from LDS buffer `buf`:
   // s[run * 2 + S tile][column tile].
-  auto logits = [&](int buf, f32x4 (&s)[4][2]) {
+  auto logits = [&](int kb_i, f32x4 (&s)[4][2]) {
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      const unsigned char* kt = &lds[buf][0][(sub >> 1) * RUN_BYTES];
+      const unsigned char* kt = &kbuf[kb_i][(sub >> 1) * RUN_BYTES];
       const int x = sub & 1;
       // the lane's row n of tile x: 32-token blocks slot 16x + n; 16-token blocks
       // block n / 8 of the run, slot n % 8 + 8 (x ^ block); 8-token blocks block
@@ -302,34 +319,24 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     }
   };
   // value operand of dim 16nt + n, tokens 8kg..8kg+7 of run `pair`
-  auto value_piece = [&](int buf, int pair, int nt) {
+  auto value_piece = [&](int vb_i, int pair, int nt) {
     const int d = 16 * nt + n;
     const int off = BS == 32   ? d * 64 + 16 * (kg ^ value_rot(d))
                     : BS == 16 ? (kg >> 1) * TILE + d * 32 + 16 * (kg & 1)
                                : kg * TILE + d * 16;  // 8-token blocks: tokens 8kg.. are block kg
-    return *reinterpret_cast<const uint4*>(&lds[buf][1][pair * RUN_BYTES] + off);
+    return *reinterpret_cast<const uint4*>(&vbuf[vb_i][pair * RUN_BYTES] + off);
   };
 
-  // Staging with fp16 values.  A wave's loads land the same 16 bytes in each
-  // lane that the lane later converts, so after its own counter wait a wave
-  // converts its pieces of the stage (its share: pieces wave + NW*k of the
-  // values) with no barrier in between, and the one barrier per iteration
-  // publishes keys and converted values together; waves that finish their
-  // products early convert while the others still compute.  A value without a
-  // finite fp16 copy (beyond fp16's range, or a NaN) anywhere in the stage
-  // turns the workgroup to the exact path for the rest of its chunk: the
-  // stage's values are staged again unconverted.  The flags are kept per
-  // stage parity, so a wave ahead by one stage never overwrites flags another
-  // wave has yet to read.
-  auto convert_own = [&](int stage, int buf) {
-    lds_dma_wait_all();
-    bool over = false;
+  // The wave's own pieces of a stage's values (pieces wave + NW*k: its loads
+  // landed exactly the 16 bytes each lane converts) to fp16, in place.  The
+  // stage must have landed (the barrier after the wave's counter wait).  A
+  // value fp16 cannot hold becomes +-inf, or stays NaN.
+  auto convert_own = [&](int vb_i) {
 #pragma unroll
     for (int k = 0; k < STAGE_HALF / 1024 / NW; ++k)
-      over |= values_to_f16(&lds[buf][1][(wave + NW * k) * 1024 + 16 * lane]);
-    // every lane stores the wave's flag (same value, same address): no branch
-    sm_big[stage & 1][wave] = __ballot(over) != 0;
+      values_to_f16(&vbuf[vb_i][(wave + NW * k) * 1024 + 16 * lane]);
   };
+
   // Fast path (fp16 values in LDS).  The reference m moves lazily: the
   // weights 2^(s*scale - m) are formed with the current m and kept while all
   // of them fit fp16 (below 2^16); the check is a packed fma(w, 0, acc), NaN
@@ -337,9 +344,19 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // 16 or more above m, or a NaN logit) m moves to the iteration's column
   // maximum, the accumulators are rescaled, and the weights are formed again.
   // Weights then lie in (0, 2^16): fp16 keeps 11 bits of each down to 2^-14.
-  auto compute_fast = [&](int buf, int next, int next_buf) {
-    f32x4 s[4][2];
-    logits(buf, s);
+  // Fast path (fp16 values in LDS), software-pipelined over iterations: the
+  // weights of stage j are formed from logits computed during iteration j - 1,
+  // while the matrix cores compute the logits of stage j + 1; then stage j's
+  // value products run beside the conversion of stage j + 1's values.
+  //
+  // The reference m moves lazily: the weights 2^(s*scale - m) are formed with
+  // the current m and kept while all of them fit fp16 (below 2^16); the check
+  // is a packed fma(w, 0, acc), NaN once any weight is infinite.  Otherwise
+  // (the first iteration, a logit 16 or more above m, or a NaN logit) m moves
+  // to the stage's column maximum, the accumulators are rescaled, and the
+  // weights are formed again.  Weights then lie in (0, 2^16): fp16 keeps 11
+  // bits of each down to 2^-14.
+  auto compute_fast = [&](f32x4 (&s)[4][2], int vb_i, int convert_vb, auto convert_tag) {
     uint32_t w[2][2][4];  // [run][column tile][pair of tokens]: fp16 weights, token 8kg + j of the run
     auto weights = [&]() {
       f16x2 ovf = {0, 0};
@@ -384,7 +401,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
             o1[ct], 0, 0, 0);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const f16x8 va = __builtin_bit_cast(f16x8, value_piece(buf, pair, nt));
+        const f16x8 va = __builtin_bit_cast(f16x8, value_piece(vb_i, pair, nt));
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
           o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -392,19 +409,24 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
               o[ct][nt], 0, 0, 0);
       }
     }
-    // The next stage's values, converted in the same straight-line stretch as
-    // the value products: its loads come after theirs in program order (the
-    // buffers cannot be told apart at compile time, so its stores may not pass
-    // their loads), and its vector work fills the matrix cores' cycles.
-    convert_own(next, next_buf);
+    // the next stage's values: after the value products in program order (the
+    // buffer indices are not known at compile time, so these stores may not
+    // pass their loads), in the same straight-line stretch so that the
+    // conversion's vector work fills the matrix cores' cycles
+    if constexpr (decltype(convert_tag)::value) {
+      // this wave's values of that stage were loaded before the newest stage's
+      // keys and values: those may still be in flight
+      lds_dma_wait<2 * kPiecesPerWave>();
+      convert_own(convert_vb);
+    }
   };
 
   // Exact path (bf16 values in LDS): per 32-token run, the reference moves
   // when a logit exceeds it by more than kRescaleSlack (weights below 2^8),
   // and the weights enter the matrix cores as bf16 hi + lo parts.
-  auto compute_exact = [&](int buf) {
+  auto compute_exact = [&](int kb_i, int vb_i) {
     f32x4 s[4][2];
-    logits(buf, s);
+    logits(kb_i, s);
 #pragma unroll
     for (int pair = 0; pair < 2; ++pair) {
       const f32x4* s0 = s[2 * pair];
@@ -438,7 +460,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const bf16x8 va = __builtin_bit_cast(bf16x8, value_piece(buf, pair, nt));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, value_piece(vb_i, pair, nt));
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(hw[ct][0], hw[ct][1], hw[ct][2], hw[ct][3]));
@@ -450,50 +472,107 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     }
   };
 
-  auto stage_overflows = [&](int stage) {
-    bool any = false;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) any |= sm_big[stage & 1][w] != 0;
-    return any;
-  };
-  auto restage_values = [&](int stage, int buf) {
-    stage_issue(stage, buf, true);
-    lds_dma_wait_all();
+  // Fast path.  Iteration j: the loads of stage j + 2 are issued; the logits
+  // of stage j + 1 (keys published by the last barrier) are computed beside
+  // stage j's weights, whose logits the previous iteration computed; stage j's
+  // value products (values converted during the previous iteration) run beside
+  // the conversion of stage j + 1's values; then the wave waits for its loads
+  // and the barrier publishes all of it.  Buffers: keys of stage j in j % 2,
+  // values in j % 3.
+  // Waits: a stage's keys must have landed (all waves) by the barrier that ends
+  // the iteration before they are used; its values only when this wave
+  // converts its pieces, during that next iteration.  So the barrier waits
+  // with the newest stage's value loads still outstanding, and the
+  // conversion with the newest stage's keys and values outstanding.  Every
+  // iteration issues a stage (the last two load the final stage again into
+  // buffers that are free) so that those counts hold throughout.
+  if (iters > 0) {
+    stage_issue(0, 0, 0);
+    stage_issue(min(1, iters - 1), 1, 1);
+    lds_dma_wait<kPiecesPerWave>();  // all but stage 1's values
     __syncthreads();
-  };
-
-  // The exact path is a loop of its own that the fast one hands over to: one
-  // loop body holding both would need more registers than two waves per SIMD
-  // leave.
-  stage_issue(0, 0, false);
-  convert_own(0, 0);
-  __syncthreads();
-  int it = 0;
-  if (stage_overflows(0)) {
-    restage_values(0, 0);
-  } else {
-    for (; it < iters; ++it) {
-      const int buf = it & 1;
-      const bool more = it + 1 < iters;
-      if (more) stage_issue(it + 1, buf ^ 1, false);  // buffer buf^1 was released by the last barrier
-      // after the last stage the conversion runs on the other buffer's old
-      // contents, which nothing reads again, and its flag is not looked at
-      if (wave_active) compute_fast(buf, it + 1, buf ^ 1);
-      else convert_own(it + 1, buf ^ 1);
+    convert_own(0);
+    // Waves with rows run the loop below; the others (past the group's rows)
+    // only stage, convert and meet the same barriers.  Two loops, so that the
+    // active one holds no branch between the value products and the
+    // conversion.
+    if (wave_active) {
+      f32x4 s[4][2];
+      logits(0, s);
       __syncthreads();
-      if (more && stage_overflows(it + 1)) {
-        restage_values(it + 1, buf ^ 1);
-        ++it;  // stage it + 1 holds its values unconverted: the exact loop goes on from there
-        break;
+      for (int it = 0; it + 1 < iters; ++it) {
+        stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3);  // those buffers' stages are used up
+        f32x4 s_next[4][2];
+        logits((it + 1) % 2, s_next);
+        compute_fast(s, it % 3, (it + 1) % 3, std::true_type{});
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) s[sub][ct] = s_next[sub][ct];
+        lds_dma_wait<kPiecesPerWave>();
+        __syncthreads();
+      }
+      compute_fast(s, (iters - 1) % 3, 0, std::false_type{});
+    } else {
+      __syncthreads();
+      for (int it = 0; it + 1 < iters; ++it) {
+        stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3);
+        lds_dma_wait<2 * kPiecesPerWave>();
+        convert_own((it + 1) % 3);
+        lds_dma_wait<kPiecesPerWave>();
+        __syncthreads();
       }
     }
+    lds_dma_wait_all();  // the last stage's repeated loads
   }
-  for (; it < iters; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < iters) stage_issue(it + 1, buf ^ 1, false);
-    if (wave_active) compute_exact(buf);
+
+  // A value without a finite fp16 copy (|v| > 65504, an infinity) or a NaN
+  // anywhere in the chunk leaves a non-finite accumulator in some wave: the
+  // workgroup then computes its chunk again from scratch on the exact path
+  // (bf16 values, weights as bf16 hi + lo), which gives NaN or infinity only
+  // where the inputs do.  The flags go through the first key buffer, which
+  // nothing reads any more.
+  bool nonfinite = false;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    nonfinite |= !__builtin_isfinite(o1[ct][0]);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) nonfinite |= !__builtin_isfinite(o[ct][nt][r]);
+  }
+  const int wave_nonfinite = __ballot(nonfinite) != 0;
+  int* flags = reinterpret_cast<int*>(&kbuf[0][0]);
+  __syncthreads();
+  flags[wave] = wave_nonfinite;  // every lane stores the same value
+  __syncthreads();
+  bool redo = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) redo |= flags[w] != 0;
+  __syncthreads();  // flags read before the exact path's loads overwrite them
+  if (redo) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      m[ct] = -INFINITY;
+      lsum[ct] = 0.f;
+      o1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (id_base != blk_lo) {  // back to the chunk's first 64 ids
+      id_base = blk_lo;
+      ids = load_ids(id_base);
+    }
+    stage_issue(0, 0, 0);
     lds_dma_wait_all();
     __syncthreads();
+    for (int it = 0; it < iters; ++it) {
+      const int buf = it & 1;
+      if (it + 1 < iters) stage_issue(it + 1, buf ^ 1, buf ^ 1);  // buffers buf^1 were released by the last barrier
+      if (wave_active) compute_exact(buf, buf);
+      lds_dma_wait_all();
+      __syncthreads();
+    }
   }
 
   if (!wave_active) return;
