@@ -88,7 +88,9 @@ typedef struct {
 typedef enum {
   PKV_KERNEL_AUTO = 0,   /* MFMA for bf16, head_dim 128 and 4 or 8 query heads per kv head; vector otherwise */
   PKV_KERNEL_VECTOR = 1, /* per-lane dot products with cross-lane reductions (any supported group) */
-  PKV_KERNEL_MFMA = 2    /* grouped query tile on matrix cores (bf16, head_dim 128, group 4 or 8) */
+  PKV_KERNEL_MFMA = 2,   /* grouped query tile on matrix cores (bf16, head_dim 128, group 4 or 8) */
+  PKV_KERNEL_TILE = 3    /* multi-token calls only: 128-row causal tiles staged through LDS (bf16,
+                            head_dim 128, group 1, 2, 4 or 8); partitions hold whole 64-token stages */
 } pkv_kernel;
 
 /* Optional decode settings (pass NULL for defaults). */
@@ -240,9 +242,14 @@ size_t pkv_paged_attn_multi_token_workspace_bytes(const pkv_pool_desc* pool, int
  *  query_start    [num_seqs + 1] int32, device; non-decreasing, within [0, num_query_tokens]
  *  max_query_len  host bound of n_b (the grid covers that many tokens per sequence)
  *  out            [num_query_tokens][num_heads][head_dim] out_dtype
- *  opts           partition_tokens, kernel (the matrix-core kernel takes bf16,
- *                 head_dim 128 and 1, 2, 4 or 8 query heads per kv head) and
- *                 blocks_in_flight; no shared-prefix plan, one kv head per workgroup
+ *  opts           partition_tokens, kernel (the matrix-core kernels take bf16,
+ *                 head_dim 128 and 1, 2, 4 or 8 query heads per kv head; AUTO
+ *                 picks PKV_KERNEL_TILE for them once max_query_len * group >= 64,
+ *                 where each block read serves up to 128 rows, the 32-row
+ *                 MFMA tiles below that) and blocks_in_flight (MFMA kernel);
+ *                 no shared-prefix plan, one kv head per workgroup.  The tile
+ *                 kernel multiplies bf16 values by weights split into bf16
+ *                 hi + lo parts (the shared-prefix pass's exact form).
  * Other arguments as in pkv_paged_attn_decode.  Device-side preconditions:
  * n_b <= context_lens[b] <= max_context_len and n_b <= max_query_len; a
  * sequence breaking them gets NaN in the rows the grid covers.  A sequence

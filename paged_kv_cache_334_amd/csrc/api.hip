@@ -57,9 +57,9 @@ constexpr int64_t kTargetWorkgroups = 256;
 // whenever the GPU is already full.  Fewer units (long contexts, small
 // batches) are split into equal partitions until about kTargetWorkgroups
 // exist, each wave keeping at least two rounds of in-flight blocks.
-int64_t auto_blocks_per_part(int64_t units, int64_t max_blocks, int64_t round) {
-  if (units >= kTargetWorkgroups || max_blocks <= 2 * round || units == 0) return max_blocks > 0 ? max_blocks : 1;
-  const int64_t parts = (kTargetWorkgroups + units - 1) / units;
+int64_t auto_blocks_per_part(int64_t units, int64_t max_blocks, int64_t round, int64_t target = kTargetWorkgroups) {
+  if (units >= target || max_blocks <= 2 * round || units == 0) return max_blocks > 0 ? max_blocks : 1;
+  const int64_t parts = (target + units - 1) / units;
   int64_t bpp = (max_blocks + parts - 1) / parts;
   if (bpp < 2 * round) bpp = 2 * round;
   return (bpp + round - 1) / round * round;
@@ -83,6 +83,12 @@ struct Plan {
 
 // Prefix-pass workgroups to aim for (two per CU).
 constexpr int64_t kPrefixTargetWorkgroups = 512;
+
+// Multi-token calls whose sequences bring at least this many rows (new tokens
+// x query heads of one kv head) take the 128-row causal tiles when the caller
+// leaves the kernel to the library: from there a tile's single read of each
+// block serves enough rows to beat the 32-row tiles' repeated reads.
+constexpr int64_t kTileMinRows = 64;
 
 // Reads the host plan words: checks them against the call and sizes the
 // prefix pass.  Sets plan->cascade when at least one group exists.
@@ -265,6 +271,7 @@ pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_he
 // Plan of one multi-token call (several new tokens per sequence).
 struct MultiPlan {
   bool mfma = false;
+  bool tile = false;      // 128-row causal tiles staged through LDS (the shared-prefix kernel's causal form)
   int group = 1;
   int col_tiles = 1;      // matrix-core kernel: 16-row column tiles per workgroup
   int rows_per_tile = 1;  // (token, head) rows per workgroup
@@ -288,7 +295,8 @@ pkv_status make_multi_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t 
   const int g = num_heads / pool->num_kv_heads;
   const int bf16 = pool->dtype == PKV_BF16;
   const int kernel = opts ? opts->kernel : PKV_KERNEL_AUTO;
-  if (kernel != PKV_KERNEL_AUTO && kernel != PKV_KERNEL_VECTOR && kernel != PKV_KERNEL_MFMA)
+  if (kernel != PKV_KERNEL_AUTO && kernel != PKV_KERNEL_VECTOR && kernel != PKV_KERNEL_MFMA &&
+      kernel != PKV_KERNEL_TILE)
     return fail(PKV_EINVAL, "unknown kernel selector");
   if (opts && (opts->prefix_plan || opts->prefix_plan_dev))
     return fail(PKV_EUNSUPPORTED, "a shared-prefix plan is not taken with several new tokens per sequence");
@@ -298,13 +306,37 @@ pkv_status make_multi_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t 
   const int inflight = opts ? opts->blocks_in_flight : 0;
   if (inflight < 0 || inflight > 2) return fail(PKV_EINVAL, "blocks_in_flight must be 0, 1 or 2");
   const bool mfma_ok = pkv::multi_mfma_supported(bf16, pool->head_dim, pool->block_size, g);
-  if (kernel == PKV_KERNEL_MFMA && !mfma_ok)
-    return fail(PKV_EUNSUPPORTED, "the matrix-core kernel needs bf16, head_dim 128 and 1, 2, 4 or 8 query heads per kv head");
+  if ((kernel == PKV_KERNEL_MFMA || kernel == PKV_KERNEL_TILE) && !mfma_ok)
+    return fail(PKV_EUNSUPPORTED, "the matrix-core kernels need bf16, head_dim 128 and 1, 2, 4 or 8 query heads per kv head");
+  const int qmax = max_query_len > 0 ? max_query_len : 1;
+  const int bs = pool->block_size;
+  const int64_t max_blocks = (max_context_len + bs - 1) / bs;
+  int64_t part_tokens = opts ? opts->partition_tokens : 0;
+  if (part_tokens < 0) return fail(PKV_EINVAL, "partition_tokens must be >= 0");
+  plan->group = g;
+  plan->tile = kernel == PKV_KERNEL_TILE || (kernel == PKV_KERNEL_AUTO && mfma_ok && (int64_t)qmax * g >= kTileMinRows);
+  if (plan->tile) {
+    // whole 64-token stages per partition
+    const int64_t stage = pkv::kPrefixIterTokens / bs;
+    plan->rows_per_tile = 128;
+    plan->row_tiles = (int)(((int64_t)qmax * g + 127) / 128);
+    int64_t bpp = part_tokens == 0
+                      ? auto_blocks_per_part((int64_t)num_seqs * pool->num_kv_heads * plan->row_tiles, max_blocks,
+                                             stage, kPrefixTargetWorkgroups)
+                      : (part_tokens + bs - 1) / bs;
+    bpp = (bpp + stage - 1) / stage * stage;
+    if (bpp >= max_blocks) bpp = max_blocks > 0 ? max_blocks : 1;
+    plan->blocks_per_part = (int)bpp;
+    plan->num_parts = max_blocks > 0 ? (int)((max_blocks + bpp - 1) / bpp) : 1;
+    if (plan->num_parts > 65535) return fail(PKV_EUNSUPPORTED, "too many partitions; raise partition_tokens");
+    const int64_t units = (int64_t)plan->num_parts * pool->num_kv_heads * num_seqs;
+    if ((units + pkv::kXcds - 1) / pkv::kXcds * pkv::kXcds * plan->row_tiles > 0x7fffffff)
+      return fail(PKV_EUNSUPPORTED, "too many workgroups; raise partition_tokens");
+    return PKV_OK;
+  }
   plan->mfma = kernel == PKV_KERNEL_MFMA || (kernel == PKV_KERNEL_AUTO && mfma_ok);
   if (!plan->mfma && !pkv::vector_supported(bf16, pool->head_dim, pool->block_size, g))
     return fail(PKV_EUNSUPPORTED, "query heads per kv head must be 1, 2, 4 or 8");
-  plan->group = g;
-  const int qmax = max_query_len > 0 ? max_query_len : 1;
   const int tile_bytes = pool->block_size * pool->head_dim * elt_bytes(pool->dtype);
   if (plan->mfma) {
     const int64_t rows = (int64_t)qmax * g;
@@ -323,10 +355,6 @@ pkv_status make_multi_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t 
     if ((int64_t)num_seqs * qmax > 65535)
       return fail(PKV_EUNSUPPORTED, "vector kernel: num_seqs * max_query_len must stay below 65536");
   }
-  const int bs = pool->block_size;
-  const int64_t max_blocks = (max_context_len + bs - 1) / bs;
-  int64_t part_tokens = opts ? opts->partition_tokens : 0;
-  if (part_tokens < 0) return fail(PKV_EINVAL, "partition_tokens must be >= 0");
   int64_t bpp = part_tokens == 0 ? auto_blocks_per_part((int64_t)num_seqs * pool->num_kv_heads * plan->row_tiles,
                                                         max_blocks, (int64_t)pkv::kWaves * plan->inflight)
                                  : (part_tokens + bs - 1) / bs;
@@ -451,7 +479,7 @@ pkv_status decode_planned(const Plan& plan, const void* q, const void* k_pool, c
     p.ws_m = pre;
     p.ws_l = pre + rows;
     p.ws_acc = pre + 2 * rows;
-    hipError_t pe = pkv::launch_prefix(p, pool->block_size, plan.group, s);
+    hipError_t pe = pkv::launch_prefix(p, pool->block_size, plan.group, false, s);
     if (pe != hipSuccess) return fail(PKV_EHIP, std::string("prefix launch: ") + hipGetErrorString(pe));
     a.start_blocks = opts->prefix_plan_dev + pkv::kPlanHeader;
     a.plan = opts->prefix_plan_dev;
@@ -595,7 +623,7 @@ pkv_status pkv_paged_attn_multi_token(const void* q, const void* k_pool, const v
   a.blocks_per_part = plan.blocks_per_part;
   a.num_parts = plan.num_parts;
   // the matrix-core kernel orders sequences longest first (one ranking thread per sequence)
-  a.longest_first = plan.mfma && num_seqs > 1 && num_seqs <= pkv::kMaxRankSeqs && max_context_len < (1 << 23);
+  a.longest_first = plan.mfma && !plan.tile && num_seqs > 1 && num_seqs <= pkv::kMaxRankSeqs && max_context_len < (1 << 23);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = out;
   a.out_bf16 = out_dtype == PKV_BF16;
@@ -613,9 +641,38 @@ pkv_status pkv_paged_attn_multi_token(const void* q, const void* k_pool, const v
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int bf16 = pool->dtype == PKV_BF16;
-  hipError_t e = plan.mfma ? pkv::launch_multi_mfma(a, pool->block_size, plan.group, plan.col_tiles, plan.inflight, s)
-                           : pkv::launch_decode_vector(a, bf16, pool->head_dim, pool->block_size, plan.group,
-                                                       plan.inflight, 1, s);
+  hipError_t e;
+  if (plan.tile) {
+    pkv::PrefixArgs p{};
+    p.q = q;
+    p.k_pool = k_pool;
+    p.v_pool = v_pool;
+    p.block_tables = block_tables;
+    p.num_heads = num_heads;
+    p.num_kv_heads = pool->num_kv_heads;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = pool->num_blocks;
+    p.chunk_blocks = plan.blocks_per_part;
+    p.num_chunks = plan.num_parts;
+    p.num_tiles = plan.row_tiles;
+    p.scale_log2 = a.scale_log2;
+    p.ws_m = a.ws_m;
+    p.ws_l = a.ws_l;
+    p.ws_acc = a.ws_acc;
+    p.context_lens = context_lens;
+    p.query_start = query_start;
+    p.num_seqs = num_seqs;
+    p.num_query_tokens = num_query_tokens;
+    p.max_query_len = max_query_len;
+    p.max_context = max_context_len;
+    p.out = out;
+    p.out_bf16 = a.out_bf16;
+    e = pkv::launch_prefix(p, pool->block_size, plan.group, true, s);
+  } else if (plan.mfma) {
+    e = pkv::launch_multi_mfma(a, pool->block_size, plan.group, plan.col_tiles, plan.inflight, s);
+  } else {
+    e = pkv::launch_decode_vector(a, bf16, pool->head_dim, pool->block_size, plan.group, plan.inflight, 1, s);
+  }
   if (e != hipSuccess) return fail(PKV_EHIP, std::string("multi-token launch: ") + hipGetErrorString(e));
   if (plan.num_parts > 1) {
     e = pkv::launch_multi_reduce(a, pool->head_dim, pool->block_size, plan.group, s);

@@ -123,14 +123,26 @@ struct PrefixArgs {
   int32_t num_kv_heads;
   int32_t max_blocks;
   int32_t num_blocks;
-  int32_t chunk_blocks;  // prefix blocks per workgroup
-  int32_t num_chunks;    // chunks of the longest group (grid)
+  int32_t chunk_blocks;  // prefix blocks per workgroup (causal tiles: blocks per partition)
+  int32_t num_chunks;    // chunks of the longest group (grid; causal tiles: partitions per sequence)
   int32_t num_slots;     // chunk slots per (sequence, query head)
-  int32_t num_tiles;     // 128-row tiles over all groups
+  int32_t num_tiles;     // 128-row tiles over all groups (causal tiles: per sequence and kv head)
   float scale_log2;
   float* ws_m;
   float* ws_l;
   float* ws_acc;
+  // Causal tiles (several new tokens per sequence, the rows of one sequence and
+  // kv head in 128-row tiles; plan unused): the multi-token call's arguments,
+  // with the same meaning as in DecodeArgs.  One partition: the output rows
+  // are written directly; several: partials at (row*num_heads + h)*num_chunks + part.
+  const int32_t* context_lens;
+  const int32_t* query_start;
+  int32_t num_seqs;
+  int32_t num_query_tokens;
+  int32_t max_query_len;
+  int32_t max_context;
+  void* out;
+  int32_t out_bf16;
 };
 
 bool vector_supported(int dtype_bf16, int head_dim, int block_size, int group);
@@ -142,7 +154,9 @@ hipError_t launch_decode_vector(const DecodeArgs& a, int dtype_bf16, int head_di
                                 int inflight, int heads_per_wg, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, int block_size, int group, int inflight,
                               hipStream_t stream);
-hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, hipStream_t stream);
+// causal = false: the shared-prefix pass of cascade decode; true: 128-row
+// causal tiles of several new tokens per sequence.
+hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, bool causal, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeArgs& a, int head_dim, int block_size, hipStream_t stream);
 
 // Several new tokens per sequence (a.query_start set).  Matrix-core kernel:

@@ -133,7 +133,25 @@ __device__ __forceinline__ bool values_to_f16(unsigned char* v) {
   return __builtin_isnan(acc[0]) || __builtin_isnan(acc[1]);
 }
 
-template <int BS, int G>
+// Bits that keep the first `keep` (0..8) of a 16-byte piece's eight 16-bit
+// elements, as four 32-bit masks (element 2e in the low half of word e).
+__device__ __forceinline__ uint4 keep_mask(int keep) {
+  uint32_t m[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m[e] = (2 * e < keep ? 0x0000ffffu : 0u) | (2 * e + 1 < keep ? 0xffff0000u : 0u);
+  return make_uint4(m[0], m[1], m[2], m[3]);
+}
+// Zeros in place of the elements from `keep` on of a 16-byte piece of bf16
+// values (they lie past the tokens a causal tile sees and may hold anything,
+// NaN included; they enter the products with weight zero).
+__device__ __forceinline__ void values_zero_tail(unsigned char* v, int keep) {
+  uint4* piece = reinterpret_cast<uint4*>(v);
+  const uint4 mk = keep_mask(keep);
+  const uint4 w = *piece;
+  *piece = make_uint4(w.x & mk.x, w.y & mk.y, w.z & mk.z, w.w & mk.w);
+}
+
+template <int BS, int G, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   constexpr int NB = TOK / BS;          // blocks per iteration
   constexpr int TILE = BS * HD * 2;     // bytes of one (block, kv head) tile
@@ -157,41 +175,96 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int unit = (slot / p.num_tiles) * kXcds + xcd;
-  if (unit >= p.num_kv_heads * p.num_chunks) return;
-  const int kvh = unit % p.num_kv_heads;
-  const int chunk = unit / p.num_kv_heads;
+  int tile = slot % p.num_tiles;
 
-  // which group and 128-row tile: groups hold their tiles in order
-  const int32_t* plan = p.plan;
-  const int num_groups = plan[kPlanGroups];
-  const int32_t* groups = plan_groups(plan);
-  int tile = slot % p.num_tiles, gi = 0;
-  int gend = 0, gstart = 0, gbegin = 0, gcount = 0, leader = 0, parent = -1;
-  for (; gi < num_groups; ++gi) {
-    const int32_t* gr = groups + kGroupWords * gi;
-    const int tiles = (gr[kGroupCount] * G + 127) / 128;
-    if (tile < tiles) {
-      gend = prefix_covered_blocks(gr[kGroupPrefix], BS);
-      gstart = gr[kGroupStart];
-      gbegin = gr[kGroupBegin];
-      gcount = gr[kGroupCount];
-      leader = gr[kGroupLeader];
-      parent = gr[kGroupParent];
-      break;
+  // What the two modes settle here: the kv head, the chunk's blocks
+  // [blk_lo, blk_hi) of block-table row bt, the rows [0, rows) of the unit and
+  // this wave's first row, and the query row of each (row_q).
+  int kvh, blk_lo, blk_hi, rows;
+  const int32_t* bt;
+  // cascade: the group's members and the slot of the chunk's partials
+  const int32_t* members = nullptr;
+  int slot0 = 0;
+  // causal tiles: the sequence's first query row, tokens new token 0 sees, the
+  // sequence's partitions and this one, and the tokens of the chunk (from its
+  // first) that the tile's last row sees
+  int qs = 0, base = 0, nparts = 1, part = 0, walk_end = 0;
+  if constexpr (CAUSAL) {
+    if (unit >= p.num_chunks * p.num_kv_heads * p.num_seqs) return;
+    part = unit % p.num_chunks;
+    kvh = (unit / p.num_chunks) % p.num_kv_heads;
+    const int b = unit / (p.num_chunks * p.num_kv_heads);
+    qs = p.query_start[b];
+    const int qe = p.query_start[b + 1];
+    if (qs < 0 || qs > qe || qe > p.num_query_tokens) return;  // its rows are unknown: nothing is written
+    const int qlen = qe - qs;
+    const int nrows = min(qlen, p.max_query_len) * G;
+    const int r0 = tile * 128;
+    if (r0 >= nrows) return;
+    rows = min(r0 + 128, nrows);
+    const int ctx_raw = p.context_lens[b];
+    const bool ctx_bad = ctx_raw < qlen || ctx_raw > p.max_context || qlen > p.max_query_len;
+    base = ctx_raw - qlen + 1;
+    const int walk = ctx_bad ? 0 : base + (rows - 1) / G;  // tokens the tile's last row sees
+    const int nblocks = (walk + BS - 1) / BS;
+    nparts = (nblocks + p.chunk_blocks - 1) / p.chunk_blocks;
+    if (part >= nparts) {
+      if (part == 0) {  // a broken length: NaN rows
+        for (int idx = threadIdx.x; idx < (rows - r0) * HD; idx += blockDim.x) {
+          const int row = r0 + idx / HD;
+          const int64_t o = ((int64_t)(qs + row / G) * p.num_heads + kvh * G + row % G) * HD + idx % HD;
+          if (p.out_bf16) reinterpret_cast<uint16_t*>(p.out)[o] = 0x7fc0;
+          else reinterpret_cast<float*>(p.out)[o] = NAN;
+        }
+      }
+      return;
     }
-    tile -= tiles;
+    blk_lo = part * p.chunk_blocks;
+    blk_hi = min(nblocks, blk_lo + p.chunk_blocks);
+    walk_end = min(walk, blk_hi * BS) - blk_lo * BS;
+    bt = p.block_tables + (int64_t)b * p.max_blocks;
+  } else {
+    if (unit >= p.num_kv_heads * p.num_chunks) return;
+    kvh = unit % p.num_kv_heads;
+    const int chunk = unit / p.num_kv_heads;
+    // which group and 128-row tile: groups hold their tiles in order
+    const int32_t* plan = p.plan;
+    const int num_groups = plan[kPlanGroups];
+    const int32_t* groups = plan_groups(plan);
+    int gi = 0;
+    int gend = 0, gstart = 0, gbegin = 0, gcount = 0, leader = 0, parent = -1;
+    for (; gi < num_groups; ++gi) {
+      const int32_t* gr = groups + kGroupWords * gi;
+      const int tiles = (gr[kGroupCount] * G + 127) / 128;
+      if (tile < tiles) {
+        gend = prefix_covered_blocks(gr[kGroupPrefix], BS);
+        gstart = gr[kGroupStart];
+        gbegin = gr[kGroupBegin];
+        gcount = gr[kGroupCount];
+        leader = gr[kGroupLeader];
+        parent = gr[kGroupParent];
+        break;
+      }
+      tile -= tiles;
+    }
+    if (gi == num_groups) return;
+    members = groups + kGroupWords * num_groups + gbegin;
+    // chunk `chunk` of the group's blocks [gstart, gend); a nested group's slots
+    // follow those of its ancestors
+    blk_lo = gstart + chunk * p.chunk_blocks;
+    blk_hi = min(gend, blk_lo + p.chunk_blocks);
+    if (blk_lo >= blk_hi) return;  // the merge counts only the chunks the group's blocks reach
+    slot0 = path_slots(groups, parent, BS, p.chunk_blocks) + chunk;
+    rows = gcount * G;
+    bt = p.block_tables + (int64_t)leader * p.max_blocks;
   }
-  if (gi == num_groups) return;
-  const int32_t* members = groups + kGroupWords * num_groups + gbegin;
-  // chunk `chunk` of the group's blocks [gstart, gend); a nested group's slots
-  // follow those of its ancestors
-  const int blk_lo = gstart + chunk * p.chunk_blocks;
-  const int blk_hi = min(gend, blk_lo + p.chunk_blocks);
-  if (blk_lo >= blk_hi) return;  // the merge counts only the chunks the group's blocks reach
-  const int slot0 = path_slots(groups, parent, BS, p.chunk_blocks) + chunk;
-  const int rows = gcount * G;
   const int row0 = tile * 128 + ROWS_PER_WAVE * wave;  // this wave's first row
   const bool wave_active = row0 < rows;
+  // query row of unit row r (rows past the unit's end: any valid row)
+  auto row_q = [&](int r) -> int64_t {
+    if constexpr (CAUSAL) return (int64_t)(qs + r / G) * p.num_heads + kvh * G + r % G;
+    else return (int64_t)members[r / G] * p.num_heads + kvh * G + r % G;
+  };
 
   // queries: column tile ct, lane column n -> row row0 + 16ct + n
   bf16x8 qb[2][4];
@@ -199,20 +272,28 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   for (int ct = 0; ct < 2; ++ct) {
     const int row = row0 + 16 * ct + n;
     const bool ok = row < rows;
-    const int b = ok ? members[row / G] : 0;
-    const int h = kvh * G + row % G;
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)b * p.num_heads + h) * HD;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (ok ? row_q(row) : 0) * HD;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       qb[ct][i] = __builtin_bit_cast(bf16x8, ok ? load16(qrow + 32 * i + 8 * kg) : make_uint4(0, 0, 0, 0));
   }
 
+  // Causal tiles: the tokens of the chunk (from its first) that the lane's
+  // column sees, per column tile, and the fewest any row of the wave sees (its
+  // first row's).  A stage reaching past that count has logits to mask.
+  int lim[2] = {0, 0};
+  int wave_lim = 0;
+  if constexpr (CAUSAL) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) lim[ct] = min(base + (row0 + 16 * ct + n) / G - blk_lo * BS, walk_end);
+    wave_lim = min(base + row0 / G - blk_lo * BS, walk_end);
+  }
+
   // block ids of the chunk, 64 at a time (lane l: block c0 + l); ids outside the pool -> block 0 and NaN rows
-  const int32_t* bt = p.block_tables + (int64_t)leader * p.max_blocks;
   int bad = 0;
   int id_base = blk_lo;
-  auto load_ids = [&](int base) {
-    const int idx = base + lane;
+  auto load_ids = [&](int first) {
+    const int idx = first + lane;
     int id = idx < blk_hi ? bt[idx] : 0;
     const bool out = idx < blk_hi && (unsigned)id >= (unsigned)p.num_blocks;
     bad |= __ballot(out) != 0;
@@ -278,8 +359,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
   const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
+  // (A column that has seen nothing yet and sees nothing now keeps m = -inf:
+  // its factor is 1, not 2^(-inf + inf).  The exact path rescales both column
+  // tiles when any lane needs it; causal tiles mask whole columns.)
   auto rescale = [&](int ct, float mn) {
-    const float alpha = fast_exp2(m[ct] - mn);
+    const float alpha = CAUSAL && m[ct] == mn ? 1.f : fast_exp2(m[ct] - mn);
     lsum[ct] *= alpha;
     o1[ct] *= alpha;
 #pragma unroll
@@ -327,14 +411,51 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     return *reinterpret_cast<const uint4*>(&vbuf[vb_i][pair * RUN_BYTES] + off);
   };
 
-  // The wave's own pieces of a stage's values (pieces wave + NW*k: its loads
-  // landed exactly the 16 bytes each lane converts) to fp16, in place.  The
-  // stage must have landed (the barrier after the wave's counter wait).  A
-  // value fp16 cannot hold becomes +-inf, or stays NaN.
+  // First token (in its stage) of the eight values in the lane's 16 bytes of
+  // the wave's own value piece k (pieces wave + NW*k: its loads landed exactly
+  // those 16 bytes): the value staging map read backwards.
+  auto own_value_token = [&](int k) {
+    const int piece = wave + NW * k;
+    const int q = piece * 1024 % TILE / 16 + lane;
+    const int d = q / (BS / 8);
+    const int vpiece = BS == 32 ? ((q & 3) ^ value_rot(d)) : BS == 16 ? (q & 1) : 0;
+    return piece * 1024 / TILE * BS + 8 * vpiece;
+  };
+  // The wave's own pieces of a stage's values to fp16, in place.  The stage
+  // must have landed (the barrier after the wave's counter wait).  A value
+  // fp16 cannot hold becomes +-inf, or stays NaN.
   auto convert_own = [&](int vb_i) {
 #pragma unroll
-    for (int k = 0; k < STAGE_HALF / 1024 / NW; ++k)
-      values_to_f16(&vbuf[vb_i][(wave + NW * k) * 1024 + 16 * lane]);
+    for (int k = 0; k < kPiecesPerWave; ++k) values_to_f16(&vbuf[vb_i][(wave + NW * k) * 1024 + 16 * lane]);
+  };
+
+  // Causal tiles: logits of tokens a column does not see -> -inf (weight 0),
+  // s as computed for stage `stage` (token of s[sub][ct][r]: 32 (sub / 2) +
+  // 8kg + 4 (sub % 2) + r of the stage).
+  auto mask_logits = [&](f32x4 (&s)[4][2], int stage) {
+    if constexpr (CAUSAL) {
+      const int t0 = stage * TOK;
+      if (t0 + TOK > wave_lim) {
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (t0 + 32 * (sub >> 1) + 8 * kg + 4 * (sub & 1) + r >= lim[ct]) s[sub][ct][r] = -INFINITY;
+      }
+    }
+  };
+  // Weight 2^(s*scale - m) of logit s.  Causal tiles: a masked logit (-inf)
+  // weighs 0 also where that formula would not give 0 (scale 0, or a column
+  // with m = -inf that has seen nothing yet).
+  auto weight = [&](float x, float neg_m) {
+    const float w = fast_exp2(fmaf(x, p.scale_log2, neg_m));
+    return CAUSAL && x == -INFINITY ? 0.f : w;
+  };
+  // column maximum of raw logits -> the scaled domain (scale >= 0; all masked: -inf)
+  auto scaled_max = [&](float raw) {
+    return CAUSAL && raw == -INFINITY ? -INFINITY : raw * p.scale_log2;
   };
 
   // Fast path (fp16 values in LDS).  The reference m moves lazily: the
@@ -424,9 +545,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // Exact path (bf16 values in LDS): per 32-token run, the reference moves
   // when a logit exceeds it by more than kRescaleSlack (weights below 2^8),
   // and the weights enter the matrix cores as bf16 hi + lo parts.
-  auto compute_exact = [&](int kb_i, int vb_i) {
+  auto compute_exact = [&](int kb_i, int vb_i, int stage) {
     f32x4 s[4][2];
     logits(kb_i, s);
+    mask_logits(s, stage);
 #pragma unroll
     for (int pair = 0; pair < 2; ++pair) {
       const f32x4* s0 = s[2 * pair];
@@ -437,7 +559,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       for (int ct = 0; ct < 2; ++ct) {
         const float a = maxp(maxp(maxp(s0[ct][0], s0[ct][1]), maxp(s0[ct][2], s0[ct][3])),
                              maxp(maxp(s1[ct][0], s1[ct][1]), maxp(s1[ct][2], s1[ct][3])));
-        mx[ct] = maxp_xor32(maxp_xor16(a)) * p.scale_log2;
+        mx[ct] = scaled_max(maxp_xor32(maxp_xor16(a)));
       }
       if (__ballot(mx[0] > m[0] + kRescaleSlack || mx[1] > m[1] + kRescaleSlack) != 0) {
 #pragma unroll
@@ -451,8 +573,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
         float pr[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pr[r] = fast_exp2(fmaf(s0[ct][r], p.scale_log2, neg_m));
-          pr[4 + r] = fast_exp2(fmaf(s1[ct][r], p.scale_log2, neg_m));
+          pr[r] = weight(s0[ct][r], neg_m);
+          pr[4 + r] = weight(s1[ct][r], neg_m);
         }
         lsum[ct] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
 #pragma unroll
@@ -486,70 +608,77 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // conversion with the newest stage's keys and values outstanding.  Every
   // iteration issues a stage (the last two load the final stage again into
   // buffers that are free) so that those counts hold throughout.
-  if (iters > 0) {
-    stage_issue(0, 0, 0);
-    stage_issue(min(1, iters - 1), 1, 1);
-    lds_dma_wait<kPiecesPerWave>();  // all but stage 1's values
-    __syncthreads();
-    convert_own(0);
-    // Waves with rows run the loop below; the others (past the group's rows)
-    // only stage, convert and meet the same barriers.  Two loops, so that the
-    // active one holds no branch between the value products and the
-    // conversion.
-    if (wave_active) {
-      f32x4 s[4][2];
-      logits(0, s);
+  //
+  // Causal tiles skip it and take the exact path below from the start: rows of
+  // a prompt can put nearly all their weight on a few tokens (outlier keys),
+  // and then the fp16 weights' rounding (2^-12 of each) no longer averages out
+  // over many tokens; a small output element could miss its 1% bound.
+  bool redo = CAUSAL;
+  if constexpr (!CAUSAL) {
+    if (iters > 0) {
+      stage_issue(0, 0, 0);
+      stage_issue(min(1, iters - 1), 1, 1);
+      lds_dma_wait<kPiecesPerWave>();  // all but stage 1's values
       __syncthreads();
-      for (int it = 0; it + 1 < iters; ++it) {
-        stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3);  // those buffers' stages are used up
-        f32x4 s_next[4][2];
-        logits((it + 1) % 2, s_next);
-        compute_fast(s, it % 3, (it + 1) % 3, std::true_type{});
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) s[sub][ct] = s_next[sub][ct];
-        lds_dma_wait<kPiecesPerWave>();
+      convert_own(0);
+      // Waves with rows run the loop below; the others (past the group's rows)
+      // only stage, convert and meet the same barriers.  Two loops, so that the
+      // active one holds no branch between the value products and the
+      // conversion.
+      if (wave_active) {
+        f32x4 s[4][2];
+        logits(0, s);
         __syncthreads();
-      }
-      compute_fast(s, (iters - 1) % 3, 0, std::false_type{});
-    } else {
-      __syncthreads();
-      for (int it = 0; it + 1 < iters; ++it) {
-        stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3);
-        lds_dma_wait<2 * kPiecesPerWave>();
-        convert_own((it + 1) % 3);
-        lds_dma_wait<kPiecesPerWave>();
+        for (int it = 0; it + 1 < iters; ++it) {
+          stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3);  // those buffers' stages are used up
+          f32x4 s_next[4][2];
+          logits((it + 1) % 2, s_next);
+          compute_fast(s, it % 3, (it + 1) % 3, std::true_type{});
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) s[sub][ct] = s_next[sub][ct];
+          lds_dma_wait<kPiecesPerWave>();
+          __syncthreads();
+        }
+        compute_fast(s, (iters - 1) % 3, 0, std::false_type{});
+      } else {
         __syncthreads();
+        for (int it = 0; it + 1 < iters; ++it) {
+          stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3);
+          lds_dma_wait<2 * kPiecesPerWave>();
+          convert_own((it + 1) % 3);
+          lds_dma_wait<kPiecesPerWave>();
+          __syncthreads();
+        }
       }
+      lds_dma_wait_all();  // the last stage's repeated loads
     }
-    lds_dma_wait_all();  // the last stage's repeated loads
-  }
 
-  // A value without a finite fp16 copy (|v| > 65504, an infinity) or a NaN
-  // anywhere in the chunk leaves a non-finite accumulator in some wave: the
-  // workgroup then computes its chunk again from scratch on the exact path
-  // (bf16 values, weights as bf16 hi + lo), which gives NaN or infinity only
-  // where the inputs do.  The flags go through the first key buffer, which
-  // nothing reads any more.
-  bool nonfinite = false;
+    // A value without a finite fp16 copy (|v| > 65504, an infinity) or a NaN
+    // anywhere in the chunk leaves a non-finite accumulator in some wave: the
+    // workgroup then computes its chunk again from scratch on the exact path
+    // (bf16 values, weights as bf16 hi + lo), which gives NaN or infinity only
+    // where the inputs do.  The flags go through the first key buffer, which
+    // nothing reads any more.
+    bool nonfinite = false;
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    nonfinite |= !__builtin_isfinite(o1[ct][0]);
+    for (int ct = 0; ct < 2; ++ct) {
+      nonfinite |= !__builtin_isfinite(o1[ct][0]);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+      for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) nonfinite |= !__builtin_isfinite(o[ct][nt][r]);
+        for (int r = 0; r < 4; ++r) nonfinite |= !__builtin_isfinite(o[ct][nt][r]);
+    }
+    const int wave_nonfinite = __ballot(nonfinite) != 0;
+    int* flags = reinterpret_cast<int*>(&kbuf[0][0]);
+    __syncthreads();
+    flags[wave] = wave_nonfinite;  // every lane stores the same value
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) redo |= flags[w] != 0;
+    __syncthreads();  // flags read before the exact path's loads overwrite them
   }
-  const int wave_nonfinite = __ballot(nonfinite) != 0;
-  int* flags = reinterpret_cast<int*>(&kbuf[0][0]);
-  __syncthreads();
-  flags[wave] = wave_nonfinite;  // every lane stores the same value
-  __syncthreads();
-  bool redo = false;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) redo |= flags[w] != 0;
-  __syncthreads();  // flags read before the exact path's loads overwrite them
   if (redo) {
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -569,22 +698,49 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     for (int it = 0; it < iters; ++it) {
       const int buf = it & 1;
       if (it + 1 < iters) stage_issue(it + 1, buf ^ 1, buf ^ 1);  // buffers buf^1 were released by the last barrier
-      if (wave_active) compute_exact(buf, buf);
+      if (CAUSAL && (it + 1) * TOK > walk_end) {  // the values past the tile's tokens -> zeros
+#pragma unroll
+        for (int k = 0; k < kPiecesPerWave; ++k)
+          values_zero_tail(&vbuf[buf][(wave + NW * k) * 1024 + 16 * lane], walk_end - it * TOK - own_value_token(k));
+        __syncthreads();
+      }
+      if (wave_active) compute_exact(buf, buf, it);
       lds_dma_wait_all();
       __syncthreads();
     }
   }
 
   if (!wave_active) return;
-  // partials: row -> (member sequence, query head); slot (b, h, chunk)
+  // Cascade: partials, slot (b, h, chunk) of row -> (member sequence b, query
+  // head h).  Causal tiles: the output row itself when the sequence's walk is
+  // one partition, else partial `part` of the row (the multi-token merge
+  // combines them).
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const float l = sum_xor32(sum_xor16(lsum[ct])) + o1[ct][0];
     const int row = row0 + 16 * ct + n;
     if (row >= rows) continue;
-    const int b = members[row / G];
-    const int h = kvh * G + row % G;
-    const int64_t pi = ((int64_t)b * p.num_heads + h) * p.num_slots + slot0;
+    const int64_t hrow = row_q(row);
+    if (CAUSAL && nparts == 1) {
+      const float inv = 1.f / l;
+      if (p.out_bf16) {
+        uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + hrow * HD;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const f32x4 v = bad ? f32x4{NAN, NAN, NAN, NAN} : o[ct][nt] * inv;
+          *reinterpret_cast<uint2*>(orow + 16 * nt + 4 * kg) =
+              make_uint2(f32_to_bf16_rne(v[0]) | f32_to_bf16_rne(v[1]) << 16,
+                         f32_to_bf16_rne(v[2]) | f32_to_bf16_rne(v[3]) << 16);
+        }
+      } else {
+        float* orow = reinterpret_cast<float*>(p.out) + hrow * HD;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+          *reinterpret_cast<f32x4*>(orow + 16 * nt + 4 * kg) = bad ? f32x4{NAN, NAN, NAN, NAN} : o[ct][nt] * inv;
+      }
+      continue;
+    }
+    const int64_t pi = CAUSAL ? hrow * p.num_chunks + part : hrow * p.num_slots + slot0;
     float* acc = p.ws_acc + pi * HD;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
@@ -601,13 +757,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
 
 }  // namespace
 
-hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, hipStream_t s) {
-  const int64_t units = (int64_t)p.num_kv_heads * p.num_chunks;
+hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, bool causal, hipStream_t s) {
+  const int64_t units = (int64_t)p.num_kv_heads * p.num_chunks * (causal ? p.num_seqs : 1);
   const int64_t wgs = (units + kXcds - 1) / kXcds * kXcds * p.num_tiles;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs);
   const dim3 block(64 * NW);
-#define PKV_PREFIX(BS, G) hipLaunchKernelGGL((prefix_kernel<BS, G>), grid, block, 0, s, p)
+#define PKV_PREFIX(BS, G)                                                        \
+  do {                                                                           \
+    if (causal) hipLaunchKernelGGL((prefix_kernel<BS, G, true>), grid, block, 0, s, p);  \
+    else hipLaunchKernelGGL((prefix_kernel<BS, G, false>), grid, block, 0, s, p);        \
+  } while (0)
   if (block_size == 8) {
     switch (group) {
       case 1: PKV_PREFIX(8, 1); break;

@@ -21,7 +21,7 @@ if not os.path.exists(_LIB_PATH):
 lib = ctypes.CDLL(_LIB_PATH)
 
 PKV_F32, PKV_BF16 = 0, 1
-KERNELS = {"auto": 0, "vector": 1, "mfma": 2}
+KERNELS = {"auto": 0, "vector": 1, "mfma": 2, "tile": 3}
 STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP", 5: "PKV_ENOSPACE"}
 
 

@@ -1,7 +1,8 @@
 """Several new tokens per sequence, causal among them (pkv_paged_attn_multi_token),
 on the GPU against the oracle's paged_attend_causal: small ragged cases on
-every kernel and partitioning, the broken-length paths, and the verify and
-prompt-chunk workloads at full size."""
+every kernel (vector, 32-row MFMA tiles, 128-row LDS-staged tiles) and
+partitioning, the broken-length paths, values at the fp16 limit for the tile
+kernel, and the verify and prompt-chunk workloads at full size."""
 
 import numpy as np
 import pytest
@@ -60,6 +61,12 @@ VARIANTS = [  # (kernel, partition tokens, blocks in flight)
     ("mfma", 40, 0),
     ("vector", 1 << 30, 0),
     ("vector", 48, 0),
+    # 128-row causal tiles: one partition (rows written directly), and
+    # partitions of one and of three 64-token stages (partials + merge)
+    ("tile", 0, 0),
+    ("tile", 1 << 30, 0),
+    ("tile", 64, 0),
+    ("tile", 192, 0),
 ]
 
 
@@ -88,8 +95,8 @@ def test_small_cache_ops_bit_exact(small_case):
 @pytest.mark.parametrize("out_dtype", ["same", "f32"])
 def test_small_multi(small_case, kernel, ptoks, inflight, out_dtype):
     name, wl, gw, _, ref = small_case
-    if kernel == "mfma" and not _mfma_ok(wl):
-        pytest.skip("matrix-core kernel: bf16, head_dim 128")
+    if kernel in ("mfma", "tile") and not _mfma_ok(wl):
+        pytest.skip("matrix-core kernels: bf16, head_dim 128")
     if out_dtype == "f32" and wl.dtype == "f32":
         pytest.skip("same")
     if kernel == "mfma" and inflight == 0 and wl.max_query_len * wl.spec.group > 16:
@@ -130,7 +137,7 @@ def test_zero_scale_gives_mean_of_visible_values():
     desc, k_pool, v_pool = oracle_pools(wl)
     ref = oracle.paged_attend_causal(wl.q, k_pool, v_pool, desc, wl.block_tables, wl.context_lens, wl.query_start,
                                      0.0)
-    for kernel in ("mfma", "vector"):
+    for kernel in ("mfma", "vector", "tile"):
         _say(f"[multi] zero scale, {kernel}")
         out = out_to_f64(gw.multi(kernel=kernel, partition_tokens=32, out_dtype=torch.float32))
         check_attention(out, ref, wl.dtype, "f32", f"zero-scale/{kernel}")
@@ -153,7 +160,7 @@ def test_broken_lengths():
     ref = oracle.paged_attend_causal(wl.q, k_pool, v_pool, desc, wl.block_tables, wl.context_lens, wl.query_start,
                                      wl.scale)
     qs = wl.query_start
-    for kernel in ("mfma", "vector"):
+    for kernel in ("mfma", "vector", "tile"):
         _say(f"[multi] broken lengths, {kernel}")
         ctx = gw.context_lens.clone()
         ctx[1] = int(wl.query_lens[1]) - 1  # fewer tokens than new ones
@@ -198,18 +205,23 @@ def _sub_batch(wl, seqs):
     return rows, wl.q[rows], wl.block_tables[seqs], wl.context_lens[seqs], starts
 
 
+@pytest.mark.parametrize("kernel", ["auto", "mfma"])
 @pytest.mark.parametrize("out_dtype", ["same", "f32"])
 @pytest.mark.parametrize("name", sorted(MULTI_SPECS))
-def test_full_multi(name, out_dtype):
+def test_full_multi(name, out_dtype, kernel):
     """Full-size workloads in the benchmark's launch configuration (automatic
-    plan).  The verify workload is compared on every row; the prompt chunks
-    (512 new tokens per sequence, one oracle attention per token) on their
-    longest and shortest sequences, which keeps the oracle within seconds."""
-    _say(f"[multi-full] building {name}")
+    plan: 32-row MFMA tiles for verify, 128-row tiles for the prompt chunks),
+    and the prompt chunks on the 32-row kernel too.  The verify workload is
+    compared on every row; the prompt chunks (512 new tokens per sequence, one
+    oracle attention per token) on their longest and shortest sequences, which
+    keeps the oracle within seconds."""
+    if kernel == "mfma" and name.startswith("verify"):
+        pytest.skip("the automatic plan is this one")
+    _say(f"[multi-full] building {name} ({kernel})")
     wl = generate(MULTI_SPECS[name])
     gw = GpuWorkload(wl)
     odt = torch.float32 if out_dtype == "f32" else None
-    out = out_to_f64(gw.multi(out_dtype=odt))
+    out = out_to_f64(gw.multi(out_dtype=odt, kernel=kernel))
     assert np.isfinite(out).all()
     desc, k_pool, v_pool = oracle_pools(wl)
     if wl.max_query_len <= 64:
@@ -235,3 +247,46 @@ def test_more_sequences_than_the_ranking_takes():
         out = out_to_f64(gw.multi(kernel="mfma", partition_tokens=ptoks, blocks_in_flight=1, out_dtype=torch.float32))
         torch.cuda.synchronize()
         check_attention(out, ref, wl.dtype, "f32", f"300-seqs/multi/{ptoks}")
+
+
+@pytest.mark.parametrize("bits,label", [(0x477F, "65280-in-fp16-range"), (0x4780, "65536-beyond-fp16"),
+                                        (0xC780, "minus-65536-beyond-fp16")])
+def test_tile_values_near_the_fp16_limit(bits, label):
+    """Large values (65280, the largest bf16 within fp16's range, and +-65536
+    beyond it) through the 128-row tiles, which keep values in bf16 and split
+    the weights into bf16 hi + lo parts: no overflow, and the products keep
+    their precision.  Both with one partition and with several."""
+    wl = generate("gqa-70b", num_seqs=3, ctx=(300, 700), num_heads=16, num_kv_heads=2, query_len=(40, 80))
+    v = wl.init_v.copy()
+    for tok, h, d in ((5, 0, 3), (150, 1, 77), (290, 0, 127)):  # cached tokens (the first sequences come first)
+        v[tok, h, d] = bits
+    wl.init_v = v
+    gw = GpuWorkload(wl)
+    desc, kp, vp = oracle_pools(wl)
+    ref = oracle.paged_attend_causal(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.query_start,
+                                     wl.scale)
+    assert np.abs(ref).max() > 10.0  # the large values reach the output
+    for ptoks in (0, 128):
+        _say(f"[multi] tile, value {label}, partition {ptoks}")
+        out = out_to_f64(gw.multi(kernel="tile", partition_tokens=ptoks, out_dtype=torch.float32))
+        assert np.isfinite(out).all(), label
+        err = np.abs(out - ref)
+        assert (err <= 2e-3 + 2e-3 * np.abs(ref)).all(), f"{label}/{ptoks}: max abs {err.max():.3g}"
+        b = out_to_f64(gw.multi(kernel="tile", partition_tokens=ptoks))
+        check_attention(b, ref, "bf16", "bf16", f"tile/{label}/{ptoks}")
+
+
+def test_tile_bad_block_id_gives_nan_rows():
+    """A block id outside the pool in a sequence's table: that sequence's rows
+    (all kv heads) are NaN on the tile kernel, the other sequences unchanged."""
+    wl = generate("gqa-70b", num_seqs=3, ctx=(200, 400), num_heads=16, num_kv_heads=2, query_len=(20, 40))
+    gw = GpuWorkload(wl)
+    good = out_to_f64(gw.multi(kernel="tile"))
+    bad = gw.block_tables.clone()
+    bad[1, 2] = wl.num_blocks + 3
+    gw.block_tables = bad
+    out = out_to_f64(gw.multi(kernel="tile"))
+    qs = wl.query_start
+    assert np.isnan(out[qs[1]:qs[2]]).all()
+    keep = np.r_[qs[0]:qs[1], qs[2]:qs[3]]
+    assert np.array_equal(out[keep], good[keep])
