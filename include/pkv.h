@@ -114,6 +114,20 @@ typedef struct {
   const int32_t* prefix_plan;
   const int32_t* prefix_plan_dev;
   size_t prefix_plan_words;
+  /* LDS-staged matrix-core kernel (the shared-prefix pass, PKV_KERNEL_TILE):
+   * it forms the softmax weights in fp16 against values converted to fp16,
+   * and walks a chunk again on its exact path (bf16 values, weights as bf16
+   * hi + lo) when a value has no finite fp16 copy, or when some row's weights
+   * sit on fewer than this many effective tokens, (sum w)^2 / sum w^2.  Each
+   * fp16 weight is off by up to 2^-11 of itself: over many comparable weights
+   * that averages out, over a few it can move a small output element by more
+   * than 1% of itself.  A chunk whose rows see fewer tokens than this takes
+   * the exact path from the start.  0 = the library's value, 128 (1e-4 on an
+   * output of 1e-2 is then more than five standard deviations of the rounding
+   * error for unit-scale values); +inf = always the exact path; 1 = the fp16
+   * path wherever its values fit (error up to 2^-11 * (max |v| + |out|)).
+   * Negative or NaN: PKV_EINVAL. */
+  float min_eff_tokens;
 } pkv_decode_opts;
 
 /*

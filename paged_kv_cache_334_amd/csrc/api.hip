@@ -81,6 +81,23 @@ struct Plan {
   int prefix_grid_chunks = 0;   // chunks of the longest group
 };
 
+// Fewest effective tokens (sum w)^2 / sum w^2 a row's fp16 weights may sit on
+// in the LDS-staged kernel, unless the caller says otherwise.  Rounding each
+// weight to fp16 moves an output element by sum_t delta_t (v_t - out) / sum w
+// with |delta_t| <= 2^-11 w_t: for unit-scale values a standard deviation of
+// at most 2^-11 / sqrt(3 n_eff) (about 0.7 of that measured, rounding errors
+// being mostly below the half-ulp bound).  At 128 effective tokens that is
+// 1.8e-5, so 1e-4 (1% of an output of 1e-2) is more than five of them.
+constexpr float kDefaultMinEffTokens = 128.f;
+float min_eff_tokens(const pkv_decode_opts* opts) {
+  const float v = opts ? opts->min_eff_tokens : 0.f;
+  return v == 0.f ? kDefaultMinEffTokens : v;
+}
+pkv_status check_min_eff(const pkv_decode_opts* opts) {
+  if (opts && !(opts->min_eff_tokens >= 0.f)) return fail(PKV_EINVAL, "min_eff_tokens must be >= 0 (or +inf)");
+  return PKV_OK;
+}
+
 // Prefix-pass workgroups to aim for (two per CU).
 constexpr int64_t kPrefixTargetWorkgroups = 512;
 
@@ -211,6 +228,7 @@ pkv_status make_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_he
   if (num_heads <= 0 || num_heads % pool->num_kv_heads != 0)
     return fail(PKV_EINVAL, "num_heads must be a positive multiple of num_kv_heads");
   if (max_context_len < 0) return fail(PKV_EINVAL, "max_context_len must be >= 0");
+  if ((st = check_min_eff(opts)) != PKV_OK) return st;
   const int g = num_heads / pool->num_kv_heads;
   const int bf16 = pool->dtype == PKV_BF16;
   const int kernel = opts ? opts->kernel : PKV_KERNEL_AUTO;
@@ -294,6 +312,7 @@ pkv_status make_multi_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t 
     return fail(PKV_EUNSUPPORTED, "num_seqs and max_query_len must stay below 65536");
   const int g = num_heads / pool->num_kv_heads;
   const int bf16 = pool->dtype == PKV_BF16;
+  if ((st = check_min_eff(opts)) != PKV_OK) return st;
   const int kernel = opts ? opts->kernel : PKV_KERNEL_AUTO;
   if (kernel != PKV_KERNEL_AUTO && kernel != PKV_KERNEL_VECTOR && kernel != PKV_KERNEL_MFMA &&
       kernel != PKV_KERNEL_TILE)
@@ -476,6 +495,7 @@ pkv_status decode_planned(const Plan& plan, const void* q, const void* k_pool, c
     p.num_slots = plan.prefix_chunks;
     p.num_tiles = plan.prefix_tiles;
     p.scale_log2 = a.scale_log2;
+    p.min_eff = min_eff_tokens(opts);
     p.ws_m = pre;
     p.ws_l = pre + rows;
     p.ws_acc = pre + 2 * rows;
@@ -656,6 +676,7 @@ pkv_status pkv_paged_attn_multi_token(const void* q, const void* k_pool, const v
     p.num_chunks = plan.num_parts;
     p.num_tiles = plan.row_tiles;
     p.scale_log2 = a.scale_log2;
+    p.min_eff = min_eff_tokens(opts);
     p.ws_m = a.ws_m;
     p.ws_l = a.ws_l;
     p.ws_acc = a.ws_acc;

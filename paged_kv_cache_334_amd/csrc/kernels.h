@@ -128,6 +128,7 @@ struct PrefixArgs {
   int32_t num_slots;     // chunk slots per (sequence, query head)
   int32_t num_tiles;     // 128-row tiles over all groups (causal tiles: per sequence and kv head)
   float scale_log2;
+  float min_eff;  // fewest effective tokens a row's fp16 weights may sit on (+inf: exact path only)
   float* ws_m;
   float* ws_l;
   float* ws_acc;

@@ -1,4 +1,5 @@
-// Shared-prefix pass of cascade decode (bf16, head_dim 128).
+// Shared-prefix pass of cascade decode, and 128-row causal tiles of several
+// new tokens per sequence (bf16, head_dim 128).
 //
 // Sequences that reference the same physical blocks for their first P blocks
 // (a shared system prompt, a forked beam; "PagedAttention Explained", "Shared
@@ -11,6 +12,16 @@
 // "Paged Attention" glossary, related term "FlashAttention").  Each workgroup
 // covers 128 rows of one group and kv head and one chunk of the prefix, and
 // writes a partial (max, sum, acc) per row; the suffix pass merges them.
+//
+// Causal tiles (a prompt chunk or a verify step appending n_b tokens to
+// sequence b; "PagedAttention Explained", "Enabling Automatic Prefix
+// Caching"): the same loop over the sequence's own blocks, rows = (new token,
+// query head of the kv head), so one read of a block serves up to 128 rows.
+// New token i sees the tokens up to its own position: each column has its
+// own limit, logits past it become -inf, and the values past the last row's
+// limit are zeroed in LDS (they may be another sequence's or NaN).  A
+// sequence's walk is one partition (the tile writes its output rows) or
+// several of whole 64-token stages (partials for the multi-token merge).
 //
 // Workgroup = 4 waves x 32 query rows (two 16-column MFMA tiles per wave).
 // Per iteration 64 prefix tokens: the next iteration's key and value tiles
@@ -29,15 +40,15 @@
 //  * O^T += V^T . P^T over the run, v_mfma_f32_16x16x32_f16: k = 8kg + j is
 //    token 8kg + j, B = the lane's own 8 weights, A = values of dim 16nt+n at
 //    those tokens.  Weights and values go in as fp16 (11 significant bits: a
-//    weight's rounding is at most 2^-12 relative, against 2^-9 for bf16, which
+//    weight's rounding is at most 2^-11 relative, against 2^-8 for bf16, which
 //    the output tolerance could not take over 30000 tokens).  The values
 //    arrive as bf16 and are converted once per stage, in place in LDS, each
 //    wave the pieces it loaded; a bf16 value is exact in fp16 within fp16's
-//    range.  A
-//    stage holding a value fp16 cannot hold (|v| > 65504, or NaN) is staged again
-//    unconverted, and the workgroup finishes its chunk with bf16 values and
-//    weights split into bf16 hi + lo parts (two instructions, ~16 significant
-//    bits), the exact form for any input.
+//    range.  A chunk holding a value fp16 cannot hold (|v| > 65504, or NaN),
+//    or a row whose weights sit on too few effective tokens (p.min_eff),
+//    is walked again with bf16 values and weights split into bf16 hi + lo
+//    parts (two instructions, ~16 significant bits), the exact form for any
+//    input.
 // The LDS copy permutes 16-byte pieces so that both operand reads are free of
 // bank conflicts (measured with the hardware counter): within a key chunk row
 // the tokens of one S tile sit in 16 consecutive slots (key_slot_token), and a
@@ -141,6 +152,16 @@ __device__ __forceinline__ uint4 keep_mask(int keep) {
   for (int e = 0; e < 4; ++e) m[e] = (2 * e < keep ? 0x0000ffffu : 0u) | (2 * e + 1 < keep ? 0xffff0000u : 0u);
   return make_uint4(m[0], m[1], m[2], m[3]);
 }
+// values_to_f16 for a piece whose elements from `keep` on lie past the tokens
+// a causal tile sees: those become zeros first (they may hold anything, NaN
+// included, and enter the products with weight zero).
+__device__ __forceinline__ void values_to_f16_head(unsigned char* v, int keep) {
+  uint4* piece = reinterpret_cast<uint4*>(v);
+  const uint4 mk = keep_mask(keep);
+  const uint4 w = *piece;
+  *piece = make_uint4(w.x & mk.x, w.y & mk.y, w.z & mk.z, w.w & mk.w);
+  values_to_f16(v);
+}
 // Zeros in place of the elements from `keep` on of a 16-byte piece of bf16
 // values (they lie past the tokens a causal tile sees and may hold anything,
 // NaN included; they enter the products with weight zero).
@@ -189,6 +210,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // sequence's partitions and this one, and the tokens of the chunk (from its
   // first) that the tile's last row sees
   int qs = 0, base = 0, nparts = 1, part = 0, walk_end = 0;
+  int fewest = 0;  // fewest tokens of the chunk that a row of the tile sees
   if constexpr (CAUSAL) {
     if (unit >= p.num_chunks * p.num_kv_heads * p.num_seqs) return;
     part = unit % p.num_chunks;
@@ -222,6 +244,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     blk_lo = part * p.chunk_blocks;
     blk_hi = min(nblocks, blk_lo + p.chunk_blocks);
     walk_end = min(walk, blk_hi * BS) - blk_lo * BS;
+    fewest = min(base + r0 / G - blk_lo * BS, walk_end);
     bt = p.block_tables + (int64_t)b * p.max_blocks;
   } else {
     if (unit >= p.num_kv_heads * p.num_chunks) return;
@@ -256,6 +279,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     if (blk_lo >= blk_hi) return;  // the merge counts only the chunks the group's blocks reach
     slot0 = path_slots(groups, parent, BS, p.chunk_blocks) + chunk;
     rows = gcount * G;
+    fewest = (blk_hi - blk_lo) * BS;
     bt = p.block_tables + (int64_t)leader * p.max_blocks;
   }
   const int row0 = tile * 128 + ROWS_PER_WAVE * wave;  // this wave's first row
@@ -357,6 +381,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     for (int nt = 0; nt < 8; ++nt) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  // fast path: sum of the squares of the lane's own (fp16) weights, relative
+  // to the same m; with the weight sum it gives the effective token count
+  float s2[2] = {0.f, 0.f};
   const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
   // (A column that has seen nothing yet and sees nothing now keeps m = -inf:
@@ -365,6 +392,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   auto rescale = [&](int ct, float mn) {
     const float alpha = CAUSAL && m[ct] == mn ? 1.f : fast_exp2(m[ct] - mn);
     lsum[ct] *= alpha;
+    s2[ct] *= alpha * alpha;
     o1[ct] *= alpha;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) o[ct][nt] *= alpha;
@@ -424,9 +452,18 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // The wave's own pieces of a stage's values to fp16, in place.  The stage
   // must have landed (the barrier after the wave's counter wait).  A value
   // fp16 cannot hold becomes +-inf, or stays NaN.
-  auto convert_own = [&](int vb_i) {
+  // With causal tiles, the stage reaching past the tokens the tile sees has
+  // those values zeroed on the way.
+  auto convert_own = [&](int vb_i, int stage) {
+    if (CAUSAL && (stage + 1) * TOK > walk_end) {
 #pragma unroll
-    for (int k = 0; k < kPiecesPerWave; ++k) values_to_f16(&vbuf[vb_i][(wave + NW * k) * 1024 + 16 * lane]);
+      for (int k = 0; k < kPiecesPerWave; ++k)
+        values_to_f16_head(&vbuf[vb_i][(wave + NW * k) * 1024 + 16 * lane],
+                           walk_end - stage * TOK - own_value_token(k));
+    } else {
+#pragma unroll
+      for (int k = 0; k < kPiecesPerWave; ++k) values_to_f16(&vbuf[vb_i][(wave + NW * k) * 1024 + 16 * lane]);
+    }
   };
 
   // Causal tiles: logits of tokens a column does not see -> -inf (weight 0),
@@ -477,7 +514,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // to the stage's column maximum, the accumulators are rescaled, and the
   // weights are formed again.  Weights then lie in (0, 2^16): fp16 keeps 11
   // bits of each down to 2^-14.
-  auto compute_fast = [&](f32x4 (&s)[4][2], int vb_i, int convert_vb, auto convert_tag) {
+  auto compute_fast = [&](f32x4 (&s)[4][2], int stage, int vb_i, int convert_vb, auto convert_tag) {
+    mask_logits(s, stage);
     uint32_t w[2][2][4];  // [run][column tile][pair of tokens]: fp16 weights, token 8kg + j of the run
     auto weights = [&]() {
       f16x2 ovf = {0, 0};
@@ -485,7 +523,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       for (int pair = 0; pair < 2; ++pair)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const float neg_m = -m[ct];
+          // causal tiles: a column with m = -inf gets the largest float
+          // instead, so a masked logit (-inf) still weighs 0 and any other
+          // still overflows (and m moves); the scale is > 0 here
+          const float neg_m = CAUSAL ? fminf(-m[ct], __FLT_MAX__) : -m[ct];
           float pr[8];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -514,6 +555,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       weights();
     }
 #pragma unroll
+    for (int pair = 0; pair < 2; ++pair)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f16x2 h = __builtin_bit_cast(f16x2, w[pair][ct][e]);
+          s2[ct] = __builtin_amdgcn_fdot2(h, h, s2[ct], false);
+        }
+#pragma unroll
     for (int pair = 0; pair < 2; ++pair) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
@@ -538,7 +588,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       // this wave's values of that stage were loaded before the newest stage's
       // keys and values: those may still be in flight
       lds_dma_wait<2 * kPiecesPerWave>();
-      convert_own(convert_vb);
+      convert_own(convert_vb, stage + 1);
     }
   };
 
@@ -609,18 +659,18 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // iteration issues a stage (the last two load the final stage again into
   // buffers that are free) so that those counts hold throughout.
   //
-  // Causal tiles skip it and take the exact path below from the start: rows of
-  // a prompt can put nearly all their weight on a few tokens (outlier keys),
-  // and then the fp16 weights' rounding (2^-12 of each) no longer averages out
-  // over many tokens; a small output element could miss its 1% bound.
-  bool redo = CAUSAL;
-  if constexpr (!CAUSAL) {
+  // The exact path from the start when the caller asks for it, when some row
+  // sees fewer tokens than p.min_eff (its effective count cannot reach it),
+  // and for causal tiles with scale 0 (a masked logit times 0 is no longer
+  // -inf).
+  bool redo = !((float)fewest >= p.min_eff) || (CAUSAL && !(p.scale_log2 > 0.f));
+  if (!redo) {
     if (iters > 0) {
       stage_issue(0, 0, 0);
       stage_issue(min(1, iters - 1), 1, 1);
       lds_dma_wait<kPiecesPerWave>();  // all but stage 1's values
       __syncthreads();
-      convert_own(0);
+      convert_own(0, 0);
       // Waves with rows run the loop below; the others (past the group's rows)
       // only stage, convert and meet the same barriers.  Two loops, so that the
       // active one holds no branch between the value products and the
@@ -633,7 +683,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
           stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3);  // those buffers' stages are used up
           f32x4 s_next[4][2];
           logits((it + 1) % 2, s_next);
-          compute_fast(s, it % 3, (it + 1) % 3, std::true_type{});
+          compute_fast(s, it, it % 3, (it + 1) % 3, std::true_type{});
 #pragma unroll
           for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
@@ -641,13 +691,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
           lds_dma_wait<kPiecesPerWave>();
           __syncthreads();
         }
-        compute_fast(s, (iters - 1) % 3, 0, std::false_type{});
+        compute_fast(s, iters - 1, (iters - 1) % 3, 0, std::false_type{});
       } else {
         __syncthreads();
         for (int it = 0; it + 1 < iters; ++it) {
           stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3);
           lds_dma_wait<2 * kPiecesPerWave>();
-          convert_own((it + 1) % 3);
+          convert_own((it + 1) % 3, it + 1);
           lds_dma_wait<kPiecesPerWave>();
           __syncthreads();
         }
@@ -655,12 +705,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       lds_dma_wait_all();  // the last stage's repeated loads
     }
 
-    // A value without a finite fp16 copy (|v| > 65504, an infinity) or a NaN
-    // anywhere in the chunk leaves a non-finite accumulator in some wave: the
-    // workgroup then computes its chunk again from scratch on the exact path
-    // (bf16 values, weights as bf16 hi + lo), which gives NaN or infinity only
-    // where the inputs do.  The flags go through the first key buffer, which
-    // nothing reads any more.
+    // The workgroup computes its chunk again from scratch on the exact path
+    // (bf16 values, weights as bf16 hi + lo) when some wave has
+    //  * a non-finite accumulator: a value without a finite fp16 copy (|v| >
+    //    65504, an infinity) or a NaN in the chunk; the exact path gives NaN
+    //    or infinity only where the inputs do;
+    //  * a row whose weights sit on too few tokens: effective count (sum w)^2 /
+    //    sum w^2 below p.min_eff.  Each fp16 weight is off by up to 2^-11
+    //    of itself; over many comparable weights those errors average out,
+    //    over a handful (outlier keys) they can move a small output element
+    //    by more than 1% of itself.
+    // The flags go through the first key buffer, which nothing reads any more.
     bool nonfinite = false;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -669,6 +724,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) nonfinite |= !__builtin_isfinite(o[ct][nt][r]);
+      const float l = o1[ct][0];
+      const float sq = sum_xor32(sum_xor16(s2[ct]));
+      nonfinite |= row0 + 16 * ct + n < rows && l > 0.f && l * l < p.min_eff * sq;
     }
     const int wave_nonfinite = __ballot(nonfinite) != 0;
     int* flags = reinterpret_cast<int*>(&kbuf[0][0]);

@@ -44,6 +44,7 @@ class DecodeOpts(ctypes.Structure):
         ("prefix_plan", ctypes.c_void_p),
         ("prefix_plan_dev", ctypes.c_void_p),
         ("prefix_plan_words", ctypes.c_size_t),
+        ("min_eff_tokens", ctypes.c_float),
     ]
 
 
@@ -220,24 +221,26 @@ def plan_shared_prefix(block_tables, context_lens, block_size, min_group_seqs=4,
     return PrefixPlan(host, dev)
 
 
-def _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup=0):
+def _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup=0, min_eff_tokens=0.0):
     base = (int(partition_tokens), KERNELS[kernel], int(blocks_in_flight), int(heads_per_workgroup))
     if prefix_plan is None:
-        return DecodeOpts(*base, None, None, 0)
-    return DecodeOpts(*base, prefix_plan.host.ctypes.data, _ptr(prefix_plan.dev), prefix_plan.host.size)
+        return DecodeOpts(*base, None, None, 0, float(min_eff_tokens))
+    return DecodeOpts(*base, prefix_plan.host.ctypes.data, _ptr(prefix_plan.dev), prefix_plan.host.size,
+                      float(min_eff_tokens))
 
 
 def paged_attn_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, max_context_len, partition_tokens=0,
-                               kernel="auto", blocks_in_flight=0, prefix_plan=None, heads_per_workgroup=0) -> int:
+                               kernel="auto", blocks_in_flight=0, prefix_plan=None, heads_per_workgroup=0,
+                               min_eff_tokens=0.0) -> int:
     desc = pool_desc(k_pool, v_pool)
-    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup)
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup, min_eff_tokens)
     return int(lib.pkv_paged_attn_workspace_bytes(ctypes.byref(desc), num_seqs, num_heads, max_context_len,
                                                   ctypes.byref(opts)))
 
 
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, max_context_len=None,
                       workspace=None, partition_tokens=0, kernel="auto", out_dtype=None, stream=None,
-                      blocks_in_flight=0, prefix_plan=None, heads_per_workgroup=0):
+                      blocks_in_flight=0, prefix_plan=None, heads_per_workgroup=0, min_eff_tokens=0.0):
     """``out[b, h] = softmax(scale * q[b, h] . K^T) . V`` over sequence b's
     paged keys/values.  ``q`` is ``[B, Hq, D]``; ``block_tables`` ``[B, max_blocks]``
     int32; ``context_lens`` ``[B]`` int32.  ``max_context_len`` is a host-side
@@ -258,7 +261,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=
         odt = q.dtype if out_dtype is None else out_dtype
         out = torch.empty((nseq, nh, hd), dtype=odt, device=q.device)
     odt_code = PKV_BF16 if out.dtype == torch.bfloat16 else PKV_F32
-    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup)
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup, min_eff_tokens)
     need = int(lib.pkv_paged_attn_workspace_bytes(ctypes.byref(desc), nseq, nh, int(max_context_len),
                                                   ctypes.byref(opts)))
     if workspace is None and need > 0:
@@ -273,7 +276,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=
 
 def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale, out, max_context_len=None,
                               partition_tokens=0, kernel="auto", stream=None, blocks_in_flight=0, prefix_plan=None,
-                              heads_per_workgroup=0):
+                              heads_per_workgroup=0, min_eff_tokens=0.0):
     """``paged_attn_decode`` through pkv_paged_attn_decode_noalloc: no workspace
     argument, nothing allocated (``out`` must be given); the partials go to the
     library's per-GPU scratch array.  Calls must not overlap on one GPU."""
@@ -291,7 +294,7 @@ def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, sca
     if max_context_len is None:
         max_context_len = max_blocks * desc.block_size
     odt_code = PKV_BF16 if out.dtype == torch.bfloat16 else PKV_F32
-    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup)
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup, min_eff_tokens)
     st = lib.pkv_paged_attn_decode_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
                                            _ptr(context_lens), nseq, nh, max_blocks, int(max_context_len),
                                            ctypes.byref(desc), float(scale), odt_code, _ptr(out), ctypes.byref(opts),
@@ -306,9 +309,9 @@ def paged_attn_decode_scratch_limit() -> int:
 
 def paged_attn_multi_token_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, num_query_tokens, max_query_len,
                                            max_context_len, partition_tokens=0, kernel="auto",
-                                           blocks_in_flight=0) -> int:
+                                           blocks_in_flight=0, min_eff_tokens=0.0) -> int:
     desc = pool_desc(k_pool, v_pool)
-    opts = _opts(partition_tokens, kernel, blocks_in_flight, None)
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, None, 0, min_eff_tokens)
     return int(lib.pkv_paged_attn_multi_token_workspace_bytes(ctypes.byref(desc), num_seqs, num_heads,
                                                               num_query_tokens, max_query_len, max_context_len,
                                                               ctypes.byref(opts)))
@@ -316,7 +319,7 @@ def paged_attn_multi_token_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, 
 
 def paged_attn_multi_token(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, max_query_len,
                            out=None, max_context_len=None, workspace=None, partition_tokens=0, kernel="auto",
-                           out_dtype=None, stream=None, blocks_in_flight=0):
+                           out_dtype=None, stream=None, blocks_in_flight=0, min_eff_tokens=0.0):
     """Several new tokens per sequence, causal among them: row
     ``query_start[b] + i`` of ``q [T, Hq, D]`` (new token i of sequence b, at
     position ``context_lens[b] - n_b + i``) attends over the sequence's tokens up
@@ -341,7 +344,7 @@ def paged_attn_multi_token(q, k_pool, v_pool, block_tables, context_lens, query_
         odt = q.dtype if out_dtype is None else out_dtype
         out = torch.empty((ntok, nh, hd), dtype=odt, device=q.device)
     odt_code = PKV_BF16 if out.dtype == torch.bfloat16 else PKV_F32
-    opts = _opts(partition_tokens, kernel, blocks_in_flight, None)
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, None, 0, min_eff_tokens)
     need = int(lib.pkv_paged_attn_multi_token_workspace_bytes(ctypes.byref(desc), nseq, nh, ntok, int(max_query_len),
                                                               int(max_context_len), ctypes.byref(opts)))
     if workspace is None and need > 0:

@@ -101,3 +101,30 @@ def check_attention(got, ref, dtype_in, dtype_out, label=""):
     worst = (err / bound).max()
     assert worst <= 1.0, f"{label}: error/bound {worst:.3g} (max abs {err.max():.3g})"
     return float(err.max())
+
+
+def value_max(wl):
+    """Largest |value| of the workload's finite cached and new values."""
+    if wl.dtype != BF16:
+        vals = [np.abs(np.asarray(a, np.float64)) for a in (wl.init_v, wl.new_v) if np.size(a)]
+    else:
+        vals = [np.abs((np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+                for a in (wl.init_v, wl.new_v) if np.size(a)]
+    return max(float(np.nanmax(np.where(np.isfinite(v), v, 0.0))) for v in vals)
+
+
+def check_fp16_path(got, ref, wl, label=""):
+    """Bound for the fp16 path of the LDS-staged matrix-core kernel, float32
+    output: each weight rounded to fp16 is off by at most 2^-11 of itself, or by
+    2^-25 below fp16's normal range, and numerator and denominator use the same
+    rounded weights, so an output element moves by at most that fraction of the
+    weighted mean of |v - out|, itself at most max|v| + |out| (the weight sum
+    is at least 1).  Plus 1e-5 for float32 accumulation and the merges."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.isfinite(got).all(), f"{label}: non-finite output"
+    ntok = int(wl.context_lens.max())
+    bound = (2.0 ** -11 * 1.001 + ntok * 2.0 ** -25) * (value_max(wl) + np.abs(ref)) + 1e-5
+    worst = (np.abs(got - ref) / bound).max()
+    assert worst <= 1.0, f"{label}: error/bound {worst:.3g} (max abs {np.abs(got - ref).max():.3g})"
+    return float(worst)

@@ -119,6 +119,19 @@ def test_cache_op_arguments(ops):
     assert ops.lib.pkv_copy_blocks(p, p, None, 0, ctypes.byref(d), None) == 0
 
 
+def test_min_eff_tokens_range(ops):
+    d = _desc(ops)
+    bad = [-1.0, float("nan"), float("-inf")]
+    for v in bad:
+        assert _decode(ops, d, opts=ops.DecodeOpts(0, 0, 0, 0, None, None, 0, v)) == 1, v
+        assert "min_eff_tokens" in ops.lib.pkv_last_error().decode()
+    # accepted: +inf (exact path only), 1, and 0 (the library's value); the
+    # workspace does not depend on it
+    split = [ops.DecodeOpts(64, 0, 0, 0, None, None, 0, v) for v in (float("inf"), 1.0, 0.0)]
+    sizes = {ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(d), 4, 32, 256, ctypes.byref(o)) for o in split}
+    assert sizes == {4 * 32 * 4 * (128 + 2) * 4}
+
+
 def test_blocks_in_flight_range(ops):
     d = _desc(ops)
     assert _decode(ops, d, opts=ops.DecodeOpts(0, 0, 3)) == 1

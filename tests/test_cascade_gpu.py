@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_harness import GpuWorkload, check_attention, out_to_f64
+from gpu_harness import GpuWorkload, check_attention, check_fp16_path, out_to_f64
 from logical_model import oracle_pools
 from paged_kv_cache_334_amd.workloads import generate, prefix_group_of
 
@@ -92,6 +92,25 @@ def test_cascade_matches_oracle(case, out_dtype):
     check_attention(out_to_f64(out), ref, "bf16", out_dtype, f"cascade/{name}")
 
 
+def test_cascade_fp16_path(case):
+    """The prefix pass's fp16 path wherever the values fit (min_eff_tokens 1:
+    no chunk goes back to the exact path for having few effective tokens),
+    against its own error bound; with the default (128) the short chunks of
+    these small cases take the exact path."""
+    name, wl, gw, ref, plan = case
+    _say(f"[cascade] fp16 path {name}")
+    out = gw.decode(prefix_plan=plan, out_dtype=torch.float32, min_eff_tokens=1.0)
+    check_fp16_path(out_to_f64(out), ref, wl, f"cascade-fp16/{name}")
+
+
+def test_cascade_exact_path_only(case):
+    """min_eff_tokens +inf: every chunk on the exact path, inside the strict bound."""
+    name, wl, gw, ref, plan = case
+    _say(f"[cascade] exact path {name}")
+    out = gw.decode(prefix_plan=plan, out_dtype=torch.float32, min_eff_tokens=float("inf"))
+    check_attention(out_to_f64(out), ref, "bf16", "f32", f"cascade-exact/{name}")
+
+
 def test_cascade_close_to_plain_decode(case):
     name, wl, gw, _, plan = case
     _say(f"[cascade] vs plain {name}")
@@ -158,9 +177,10 @@ def test_bad_prefix_block_gives_nan_rows_of_the_group_only():
     assert np.array_equal(out[others], good[others])
 
 
+@pytest.mark.parametrize("min_eff", [0.0, 1.0])
 @pytest.mark.parametrize("bits,label", [(0x477F, "65280-in-fp16-range"), (0x4780, "65536-beyond-fp16"),
                                         (0xC780, "minus-65536-beyond-fp16")])
-def test_prefix_values_near_the_fp16_limit(bits, label):
+def test_prefix_values_near_the_fp16_limit(bits, label, min_eff):
     """The prefix pass multiplies weights and values in fp16, converting each
     stage's bf16 values in LDS.  A value the fp16 range holds (65280, the
     largest bf16 below 65504) goes through the fast path unchanged; one beyond
@@ -178,18 +198,18 @@ def test_prefix_values_near_the_fp16_limit(bits, label):
     ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale)
     plan = ops.plan_shared_prefix(wl.block_tables, wl.context_lens, 16, min_group_seqs=2, min_prefix_blocks=1)
     assert plan.groups == 1
-    _say(f"[cascade] prefix value {label}")
-    out = out_to_f64(gw.decode(prefix_plan=plan, out_dtype=torch.float32))
+    _say(f"[cascade] prefix value {label}, min_eff {min_eff}")
+    out = out_to_f64(gw.decode(prefix_plan=plan, out_dtype=torch.float32, min_eff_tokens=min_eff))
     assert np.isfinite(out).all(), label
     # Outputs reach ~1e2 here, so the bound scales with them.  An fp16 weight
-    # keeps 11 significant bits (rounding <= 2^-12 relative) down to 2^-14, below
+    # keeps 11 significant bits (rounding <= 2^-11 relative) down to 2^-14, below
     # that an absolute 2^-25, so a product with |v| <= 65280 is off by at most
-    # 2^-12 of itself or 2e-3 absolute; the exact path keeps ~16 bits.  R9's
-    # relative bound (1e-2) holds with room either way.
+    # 2^-11 of itself or 2e-3 absolute; the exact path keeps ~16 bits.  The
+    # 1e-2 relative bound holds with room either way.
     err = np.abs(out - ref)
     assert (err <= 2e-3 + 2e-3 * np.abs(ref)).all(), f"{label}: max abs {err.max():.3g}"
     assert np.abs(ref).max() > 10.0  # the large values did reach the output
-    b = out_to_f64(gw.decode(prefix_plan=plan))
+    b = out_to_f64(gw.decode(prefix_plan=plan, min_eff_tokens=min_eff))
     check_attention(b, ref, "bf16", "bf16", f"cascade/{label}")
 
 

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 from paged_kv_cache_334_amd import ops  # noqa: F401  (fails loudly when the library is missing)
 
 import oracle
-from gpu_harness import GpuWorkload, check_attention, out_to_f64, to_bits
+from gpu_harness import GpuWorkload, check_attention, check_fp16_path, out_to_f64, to_bits
 from logical_model import oracle_pools
 from paged_kv_cache_334_amd.workloads import MULTI_SPECS, WorkloadSpec, generate
 
@@ -107,6 +107,20 @@ def test_small_multi(small_case, kernel, ptoks, inflight, out_dtype):
     torch.cuda.synchronize()
     check_attention(out, ref, wl.dtype, "f32" if (odt is not None or wl.dtype == "f32") else "bf16",
                     f"{name}/{kernel}/{ptoks}")
+
+
+@pytest.mark.parametrize("ptoks", [0, 64])
+def test_small_multi_tile_fp16_path(small_case, ptoks):
+    """The tiles' fp16 path wherever the values fit (min_eff_tokens 1: no walk
+    goes back to the exact path for having few effective tokens), against its
+    own error bound; with the default (128) the small rows here would take the
+    exact path."""
+    name, wl, gw, _, ref = small_case
+    if not _mfma_ok(wl):
+        pytest.skip("matrix-core kernels: bf16, head_dim 128")
+    _say(f"[multi] {name} tile fp16 path ptoks={ptoks}")
+    out = out_to_f64(gw.multi(kernel="tile", partition_tokens=ptoks, min_eff_tokens=1.0, out_dtype=torch.float32))
+    check_fp16_path(out, ref, wl, f"{name}/tile-fp16/{ptoks}")
 
 
 def test_small_multi_deterministic(small_case):
@@ -249,13 +263,15 @@ def test_more_sequences_than_the_ranking_takes():
         check_attention(out, ref, wl.dtype, "f32", f"300-seqs/multi/{ptoks}")
 
 
+@pytest.mark.parametrize("min_eff", [0.0, 1.0])
 @pytest.mark.parametrize("bits,label", [(0x477F, "65280-in-fp16-range"), (0x4780, "65536-beyond-fp16"),
                                         (0xC780, "minus-65536-beyond-fp16")])
-def test_tile_values_near_the_fp16_limit(bits, label):
-    """Large values (65280, the largest bf16 within fp16's range, and +-65536
-    beyond it) through the 128-row tiles, which keep values in bf16 and split
-    the weights into bf16 hi + lo parts: no overflow, and the products keep
-    their precision.  Both with one partition and with several."""
+def test_tile_values_near_the_fp16_limit(bits, label, min_eff):
+    """Large values through the 128-row tiles: 65280 (the largest bf16 within
+    fp16's range) stays on the fp16 path, +-65536 beyond it sends its tile back
+    over its walk on the exact path (bf16 values, weights as bf16 hi + lo).
+    With the default effective-token floor and with none (1), and with one
+    partition and with several."""
     wl = generate("gqa-70b", num_seqs=3, ctx=(300, 700), num_heads=16, num_kv_heads=2, query_len=(40, 80))
     v = wl.init_v.copy()
     for tok, h, d in ((5, 0, 3), (150, 1, 77), (290, 0, 127)):  # cached tokens (the first sequences come first)
@@ -267,12 +283,13 @@ def test_tile_values_near_the_fp16_limit(bits, label):
                                      wl.scale)
     assert np.abs(ref).max() > 10.0  # the large values reach the output
     for ptoks in (0, 128):
-        _say(f"[multi] tile, value {label}, partition {ptoks}")
-        out = out_to_f64(gw.multi(kernel="tile", partition_tokens=ptoks, out_dtype=torch.float32))
+        _say(f"[multi] tile, value {label}, partition {ptoks}, min_eff {min_eff}")
+        out = out_to_f64(gw.multi(kernel="tile", partition_tokens=ptoks, out_dtype=torch.float32,
+                                  min_eff_tokens=min_eff))
         assert np.isfinite(out).all(), label
         err = np.abs(out - ref)
         assert (err <= 2e-3 + 2e-3 * np.abs(ref)).all(), f"{label}/{ptoks}: max abs {err.max():.3g}"
-        b = out_to_f64(gw.multi(kernel="tile", partition_tokens=ptoks))
+        b = out_to_f64(gw.multi(kernel="tile", partition_tokens=ptoks, min_eff_tokens=min_eff))
         check_attention(b, ref, "bf16", "bf16", f"tile/{label}/{ptoks}")
 
 
