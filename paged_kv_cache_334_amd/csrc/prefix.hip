@@ -401,26 +401,30 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
 
   // S^T of one iteration (64 tokens, always whole) from LDS buffer `buf`:
   // s[run * 2 + S tile][column tile].
+  // key operands of S tile `sub` (run sub / 2, tile sub % 2) of the stage in kbuf[kb_i]
+  auto load_keys = [&](int kb_i, int sub, bf16x8 (&ka)[4]) {
+    const unsigned char* kt = &kbuf[kb_i][(sub >> 1) * RUN_BYTES];
+    const int x = sub & 1;
+    // the lane's row n of tile x: 32-token blocks slot 16x + n; 16-token blocks
+    // block n / 8 of the run, slot n % 8 + 8 (x ^ block); 8-token blocks block
+    // n / 4, token 4x + n % 4 (in its swizzled row and slot)
+    if constexpr (BS == 8) {
+      const int b = n >> 2;
+      const int slot = key8_slot(4 * x + (n & 3), b);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ka[i] = *reinterpret_cast<const bf16x8*>(kt + b * TILE + (key8_row(4 * i + kg, b) * 8 + slot) * 16);
+    } else {
+      const int koff = BS == 32 ? 16 * x + n : (n >> 3) * (TILE / 16) + (n & 7) + 8 * (x ^ (n >> 3));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kt + ((4 * i + kg) * BS + koff) * 16);
+    }
+  };
   auto logits = [&](int kb_i, f32x4 (&s)[4][2]) {
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      const unsigned char* kt = &kbuf[kb_i][(sub >> 1) * RUN_BYTES];
-      const int x = sub & 1;
-      // the lane's row n of tile x: 32-token blocks slot 16x + n; 16-token blocks
-      // block n / 8 of the run, slot n % 8 + 8 (x ^ block); 8-token blocks block
-      // n / 4, token 4x + n % 4 (in its swizzled row and slot)
       bf16x8 ka[4];
-      if constexpr (BS == 8) {
-        const int b = n >> 2;
-        const int slot = key8_slot(4 * x + (n & 3), b);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ka[i] = *reinterpret_cast<const bf16x8*>(kt + b * TILE + (key8_row(4 * i + kg, b) * 8 + slot) * 16);
-      } else {
-        const int koff = BS == 32 ? 16 * x + n : (n >> 3) * (TILE / 16) + (n & 7) + 8 * (x ^ (n >> 3));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kt + ((4 * i + kg) * BS + koff) * 16);
-      }
+      load_keys(kb_i, sub, ka);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -514,9 +518,48 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // to the stage's column maximum, the accumulators are rescaled, and the
   // weights are formed again.  Weights then lie in (0, 2^16): fp16 keeps 11
   // bits of each down to 2^-14.
-  auto compute_fast = [&](f32x4 (&s)[4][2], int stage, int vb_i, int convert_vb, auto convert_tag) {
-    mask_logits(s, stage);
-    uint32_t w[2][2][4];  // [run][column tile][pair of tokens]: fp16 weights, token 8kg + j of the run
+  // Stage j + 1's logits (sn, keys in kbuf[kb_i]) on the matrix cores and
+  // stage j's fp16 weights (from s, already masked) on the vector unit, one
+  // logit instruction and one weight per step, in an order the scheduler must
+  // keep: each step's vector work issues while the step's matrix instruction
+  // runs.  Returns true when some weight overflowed fp16 (as weights() does).
+  auto logits_with_weights = [&](int kb_i, f32x4 (&sn)[4][2], const f32x4 (&s)[4][2], uint32_t (&w)[2][2][4]) {
+    f16x2 ovf = {0, 0};
+    float neg_m[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) neg_m[ct] = CAUSAL ? fminf(-m[ct], __FLT_MAX__) : -m[ct];
+    bf16x8 ka[2][4];
+    load_keys(kb_i, 0, ka[0]);
+    float prev = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      if (sub < 3) load_keys(kb_i, sub + 1, ka[(sub + 1) & 1]);
+      sn[sub][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sn[sub][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = q >> 1, ct = q & 1;
+        sn[sub][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[sub & 1][i], qb[ct][i], sn[sub][ct], 0, 0, 0);
+        // weight k of this stage: run k / 16, column tile (k / 8) % 2, token 8kg + k % 8 of the run
+        const int k = sub * 8 + q;
+        const int pair = k >> 4, wct = (k >> 3) & 1, idx = k & 7;
+        const float pr = fast_exp2(fmaf(s[2 * pair + (idx >> 2)][wct][idx & 3], p.scale_log2, neg_m[wct]));
+        if (k & 1) {
+          w[pair][wct][idx >> 1] = pack_f16(prev, pr);
+          ovf = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, w[pair][wct][idx >> 1]), f16x2{0, 0}, ovf);
+        } else {
+          prev = pr;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    return __ballot(__builtin_isnan(ovf[0]) || __builtin_isnan(ovf[1])) != 0;
+  };
+  // w / again: the stage's weights and their overflow flag when the caller
+  // formed them already (fused_tag true: logits_with_weights), else formed here.
+  auto compute_fast = [&](f32x4 (&s)[4][2], int stage, int vb_i, int convert_vb, auto convert_tag,
+                          uint32_t (&w)[2][2][4], bool again, auto fused_tag) {
+    if constexpr (!decltype(fused_tag)::value) mask_logits(s, stage);
     auto weights = [&]() {
       f16x2 ovf = {0, 0};
 #pragma unroll
@@ -541,7 +584,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
         }
       return __ballot(__builtin_isnan(ovf[0]) || __builtin_isnan(ovf[1])) != 0;
     };
-    if (weights()) {
+    if constexpr (!decltype(fused_tag)::value) again = weights();
+    if (again) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         float a = s[0][ct][0];
@@ -682,8 +726,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
         for (int it = 0; it + 1 < iters; ++it) {
           stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3);  // those buffers' stages are used up
           f32x4 s_next[4][2];
-          logits((it + 1) % 2, s_next);
-          compute_fast(s, it, it % 3, (it + 1) % 3, std::true_type{});
+          uint32_t w[2][2][4];
+          mask_logits(s, it);
+          const bool again = logits_with_weights((it + 1) % 2, s_next, s, w);
+          compute_fast(s, it, it % 3, (it + 1) % 3, std::true_type{}, w, again, std::true_type{});
 #pragma unroll
           for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
@@ -691,7 +737,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
           lds_dma_wait<kPiecesPerWave>();
           __syncthreads();
         }
-        compute_fast(s, iters - 1, (iters - 1) % 3, 0, std::false_type{});
+        uint32_t w[2][2][4];
+        compute_fast(s, iters - 1, (iters - 1) % 3, 0, std::false_type{}, w, false, std::false_type{});
       } else {
         __syncthreads();
         for (int it = 0; it + 1 < iters; ++it) {
