@@ -524,7 +524,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // keep: each step's vector work issues while the step's matrix instruction
   // runs.  Returns true when some weight overflowed fp16 (as weights() does).
   auto logits_with_weights = [&](int kb_i, f32x4 (&sn)[4][2], const f32x4 (&s)[4][2], uint32_t (&w)[2][2][4]) {
-    f16x2 ovf = {0, 0};
+    f16x2 ovf[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};  // four chains: no serial dependence
     float neg_m[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) neg_m[ct] = CAUSAL ? fminf(-m[ct], __FLT_MAX__) : -m[ct];
@@ -546,14 +546,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
         const float pr = fast_exp2(fmaf(s[2 * pair + (idx >> 2)][wct][idx & 3], p.scale_log2, neg_m[wct]));
         if (k & 1) {
           w[pair][wct][idx >> 1] = pack_f16(prev, pr);
-          ovf = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, w[pair][wct][idx >> 1]), f16x2{0, 0}, ovf);
+          ovf[(k >> 1) & 3] = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, w[pair][wct][idx >> 1]), f16x2{0, 0},
+                                                        ovf[(k >> 1) & 3]);
+          asm volatile("" ::"v"(ovf[(k >> 1) & 3]));  // keeps the check in this step, not sunk to the end
         } else {
           prev = pr;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    return __ballot(__builtin_isnan(ovf[0]) || __builtin_isnan(ovf[1])) != 0;
+    const f16x2 o = (ovf[0] + ovf[1]) + (ovf[2] + ovf[3]);  // NaN if any chain is
+    return __ballot(__builtin_isnan(o[0]) || __builtin_isnan(o[1])) != 0;
   };
   // w / again: the stage's weights and their overflow flag when the caller
   // formed them already (fused_tag true: logits_with_weights), else formed here.
