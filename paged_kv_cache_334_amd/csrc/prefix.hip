@@ -499,32 +499,28 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     return CAUSAL && raw == -INFINITY ? -INFINITY : raw * p.scale_log2;
   };
 
-  // Fast path (fp16 values in LDS).  The reference m moves lazily: the
-  // weights 2^(s*scale - m) are formed with the current m and kept while all
-  // of them fit fp16 (below 2^16); the check is a packed fma(w, 0, acc), NaN
-  // once any weight is infinite.  Otherwise (the first iteration, a logit
-  // 16 or more above m, or a NaN logit) m moves to the iteration's column
-  // maximum, the accumulators are rescaled, and the weights are formed again.
-  // Weights then lie in (0, 2^16): fp16 keeps 11 bits of each down to 2^-14.
-  // Fast path (fp16 values in LDS), software-pipelined over iterations: the
-  // weights of stage j are formed from logits computed during iteration j - 1,
-  // while the matrix cores compute the logits of stage j + 1; then stage j's
-  // value products run beside the conversion of stage j + 1's values.
+  // Fast path (fp16 values in LDS), software-pipelined over iterations: stage
+  // j's weights are formed while the matrix cores compute stage j + 1's
+  // logits (logits_with_weights), then stage j's value products run beside
+  // the conversion of stage j + 1's values (compute_fast).
   //
-  // The reference m moves lazily: the weights 2^(s*scale - m) are formed with
-  // the current m and kept while all of them fit fp16 (below 2^16); the check
-  // is a packed fma(w, 0, acc), NaN once any weight is infinite.  Otherwise
-  // (the first iteration, a logit 16 or more above m, or a NaN logit) m moves
-  // to the stage's column maximum, the accumulators are rescaled, and the
-  // weights are formed again.  Weights then lie in (0, 2^16): fp16 keeps 11
-  // bits of each down to 2^-14.
+  // The reference m is the first stage's column maximum.  Weights
+  // 2^(s*scale - m) then stay below 2^16, finite in fp16, unless a later logit
+  // exceeds m by 16 or more; such a weight makes the accumulators infinite and
+  // sends the chunk to the exact path at its end.  The last stage (and a walk
+  // of one stage) forms its weights in compute_fast, which moves m instead: a
+  // packed fma(w, 0, acc) turns NaN once a weight is infinite, and m then
+  // moves to the stage's column maximum, the accumulators are rescaled and the
+  // weights formed again.  fp16 keeps 11 bits of each weight down to 2^-14.
   // Stage j + 1's logits (sn, keys in kbuf[kb_i]) on the matrix cores and
   // stage j's fp16 weights (from s, already masked) on the vector unit, one
   // logit instruction and one weight per step, in an order the scheduler must
   // keep: each step's vector work issues while the step's matrix instruction
-  // runs.  Returns true when some weight overflowed fp16 (as weights() does).
+  // runs.  No overflow check here: m was set from the first stage's column
+  // maxima, and a weight that overflows fp16 later (a logit 16 or more above
+  // them) makes the accumulators infinite, which sends the chunk to the exact
+  // path at its end.
   auto logits_with_weights = [&](int kb_i, f32x4 (&sn)[4][2], const f32x4 (&s)[4][2], uint32_t (&w)[2][2][4]) {
-    f16x2 ovf[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};  // four chains: no serial dependence
     float neg_m[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) neg_m[ct] = CAUSAL ? fminf(-m[ct], __FLT_MAX__) : -m[ct];
@@ -546,17 +542,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
         const float pr = fast_exp2(fmaf(s[2 * pair + (idx >> 2)][wct][idx & 3], p.scale_log2, neg_m[wct]));
         if (k & 1) {
           w[pair][wct][idx >> 1] = pack_f16(prev, pr);
-          ovf[(k >> 1) & 3] = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, w[pair][wct][idx >> 1]), f16x2{0, 0},
-                                                        ovf[(k >> 1) & 3]);
-          asm volatile("" ::"v"(ovf[(k >> 1) & 3]));  // keeps the check in this step, not sunk to the end
+
         } else {
           prev = pr;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    const f16x2 o = (ovf[0] + ovf[1]) + (ovf[2] + ovf[3]);  // NaN if any chain is
-    return __ballot(__builtin_isnan(o[0]) || __builtin_isnan(o[1])) != 0;
   };
   // w / again: the stage's weights and their overflow flag when the caller
   // formed them already (fused_tag true: logits_with_weights), else formed here.
@@ -725,14 +717,27 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       if (wave_active) {
         f32x4 s[4][2];
         logits(0, s);
+        mask_logits(s, 0);
+        // m from the first stage's column maxima (scale >= 0; a column that
+        // sees nothing keeps -inf)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          float a = s[0][ct][0];
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a = maxp(a, s[sub][ct][r]);
+          const float raw = maxp_xor32(maxp_xor16(a));
+          m[ct] = CAUSAL && raw == -INFINITY ? -INFINITY : raw * p.scale_log2;
+        }
         __syncthreads();
         for (int it = 0; it + 1 < iters; ++it) {
           stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3);  // those buffers' stages are used up
           f32x4 s_next[4][2];
           uint32_t w[2][2][4];
           mask_logits(s, it);
-          const bool again = logits_with_weights((it + 1) % 2, s_next, s, w);
-          compute_fast(s, it, it % 3, (it + 1) % 3, std::true_type{}, w, again, std::true_type{});
+          logits_with_weights((it + 1) % 2, s_next, s, w);
+          compute_fast(s, it, it % 3, (it + 1) % 3, std::true_type{}, w, false, std::true_type{});
 #pragma unroll
           for (int sub = 0; sub < 4; ++sub)
 #pragma unroll

@@ -15,7 +15,7 @@ from paged_kv_cache_334_amd import ops  # noqa: F401  (fails loudly when the lib
 import oracle
 from gpu_harness import GpuWorkload, check_attention, check_fp16_path, out_to_f64, to_bits
 from logical_model import oracle_pools
-from paged_kv_cache_334_amd.workloads import MULTI_SPECS, WorkloadSpec, generate
+from paged_kv_cache_334_amd.workloads import MULTI_SPECS, WorkloadSpec, bf16_bits_to_f32, f32_to_bf16_bits, generate
 
 
 def _say(msg):
@@ -307,3 +307,33 @@ def test_tile_bad_block_id_gives_nan_rows():
     assert np.isnan(out[qs[1]:qs[2]]).all()
     keep = np.r_[qs[0]:qs[1], qs[2]:qs[3]]
     assert np.array_equal(out[keep], good[keep])
+
+
+@pytest.mark.parametrize("min_eff", [0.0, 1.0])
+@pytest.mark.parametrize("ptoks", [0, 128])
+def test_tile_logit_far_above_the_first_stage(ptoks, min_eff):
+    """Causal tiles on the fp16 path take their softmax reference from the
+    first 64 tokens of their walk; keys past them whose logits lie 16 or more
+    (base 2) above overflow an fp16 weight, and the walk must come out right
+    through the exact path.  Cached keys past the first stage of each sequence
+    are scaled by 40.  With the default effective-token floor the rows those
+    keys dominate take the exact path anyway (strict bound); with the floor at
+    1 the rows they dominate without overflowing stay on the fp16 path, whose
+    own bound applies."""
+    wl = generate("gqa-70b", num_seqs=3, ctx=(400, 700), num_heads=16, num_kv_heads=2, query_len=(40, 80))
+    k = bf16_bits_to_f32(wl.init_k).copy()
+    starts = np.concatenate([[0], np.cumsum(wl.context_lens - wl.query_lens)])
+    for b in range(3):
+        k[starts[b] + np.array([150, 151, 290])] *= 40.0  # cached tokens, sequence by sequence
+    wl.init_k = f32_to_bf16_bits(k)
+    gw = GpuWorkload(wl)
+    desc, kp, vp = oracle_pools(wl)
+    ref = oracle.paged_attend_causal(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.query_start,
+                                     wl.scale)
+    _say(f"[multi] tile, large logits, partition {ptoks}, min_eff {min_eff}")
+    out = out_to_f64(gw.multi(kernel="tile", partition_tokens=ptoks, min_eff_tokens=min_eff,
+                              out_dtype=torch.float32))
+    if min_eff == 1.0:
+        check_fp16_path(out, ref, wl, f"tile/large-logits/{ptoks}")
+    else:
+        check_attention(out, ref, "bf16", "f32", f"tile/large-logits/{ptoks}")
