@@ -24,11 +24,11 @@
 // several of whole 64-token stages (partials for the multi-token merge).
 //
 // Workgroup = 4 waves x 32 query rows (two 16-column MFMA tiles per wave).
-// Per iteration 64 prefix tokens: the next iteration's key and value tiles
-// travel from memory straight into the other LDS buffer (global_load_lds)
-// while the current one is computed, and each wave then converts the values
-// it loaded to fp16 (two buffers, one barrier per iteration).
-// An iteration is two runs of 32 tokens (four 8-token blocks, two 16-token
+// Per iteration (a stage of 64 tokens) the key and value tiles of the stage
+// two ahead travel from memory straight into LDS (global_load_lds; keys in
+// two buffers, values in three), each wave converts the values it loaded
+// for the next stage to fp16, and one barrier publishes the stage.
+// A stage is two runs of 32 tokens (four 8-token blocks, two 16-token
 // blocks or one 32-token block).  Each run's logits come from two S tiles whose 16 rows interleave:
 // tile X holds tokens 8j + 4X + r (j, r < 4), so after the product the lane of
 // group kg owns tokens 8kg..8kg+7 of the run across the two tiles, exactly the
@@ -40,15 +40,16 @@
 //  * O^T += V^T . P^T over the run, v_mfma_f32_16x16x32_f16: k = 8kg + j is
 //    token 8kg + j, B = the lane's own 8 weights, A = values of dim 16nt+n at
 //    those tokens.  Weights and values go in as fp16 (11 significant bits: a
-//    weight's rounding is at most 2^-11 relative, against 2^-8 for bf16, which
-//    the output tolerance could not take over 30000 tokens).  The values
+//    weight's rounding is at most 2^-11 relative, against 2^-8 for bf16,
+//    which left too little room to the 1% output bound in a float64
+//    simulation of 30000-token rows).  The values
 //    arrive as bf16 and are converted once per stage, in place in LDS, each
 //    wave the pieces it loaded; a bf16 value is exact in fp16 within fp16's
 //    range.  A chunk holding a value fp16 cannot hold (|v| > 65504, or NaN),
-//    or a row whose weights sit on too few effective tokens (p.min_eff),
-//    is walked again with bf16 values and weights split into bf16 hi + lo
-//    parts (two instructions, ~16 significant bits), the exact form for any
-//    input.
+//    a logit far above the first stage's maximum (an infinite weight), or a
+//    row whose weights sit on too few effective tokens (p.min_eff), is walked
+//    again with bf16 values and weights split into bf16 hi + lo parts (two
+//    instructions, ~16 significant bits), the exact form for any input.
 // The LDS copy permutes 16-byte pieces so that both operand reads are free of
 // bank conflicts (measured with the hardware counter): within a key chunk row
 // the tokens of one S tile sit in 16 consecutive slots (key_slot_token), and a
@@ -399,8 +400,6 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     m[ct] = mn;
   };
 
-  // S^T of one iteration (64 tokens, always whole) from LDS buffer `buf`:
-  // s[run * 2 + S tile][column tile].
   // key operands of S tile `sub` (run sub / 2, tile sub % 2) of the stage in kbuf[kb_i]
   auto load_keys = [&](int kb_i, int sub, bf16x8 (&ka)[4]) {
     const unsigned char* kt = &kbuf[kb_i][(sub >> 1) * RUN_BYTES];
@@ -420,6 +419,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       for (int i = 0; i < 4; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kt + ((4 * i + kg) * BS + koff) * 16);
     }
   };
+  // S^T of one iteration (64 tokens, always whole) from key buffer kb_i:
+  // s[run * 2 + S tile][column tile].
   auto logits = [&](int kb_i, f32x4 (&s)[4][2]) {
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
@@ -512,6 +513,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // packed fma(w, 0, acc) turns NaN once a weight is infinite, and m then
   // moves to the stage's column maximum, the accumulators are rescaled and the
   // weights formed again.  fp16 keeps 11 bits of each weight down to 2^-14.
+  //
   // Stage j + 1's logits (sn, keys in kbuf[kb_i]) on the matrix cores and
   // stage j's fp16 weights (from s, already masked) on the vector unit, one
   // logit instruction and one weight per step, in an order the scheduler must
@@ -542,7 +544,6 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
         const float pr = fast_exp2(fmaf(s[2 * pair + (idx >> 2)][wct][idx & 3], p.scale_log2, neg_m[wct]));
         if (k & 1) {
           w[pair][wct][idx >> 1] = pack_f16(prev, pr);
-
         } else {
           prev = pr;
         }
@@ -550,10 +551,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       }
     }
   };
-  // w / again: the stage's weights and their overflow flag when the caller
-  // formed them already (fused_tag true: logits_with_weights), else formed here.
+  // w: the stage's weights, formed by the caller (fused_tag true:
+  // logits_with_weights) or here, with the overflow check that moves m.
   auto compute_fast = [&](f32x4 (&s)[4][2], int stage, int vb_i, int convert_vb, auto convert_tag,
-                          uint32_t (&w)[2][2][4], bool again, auto fused_tag) {
+                          uint32_t (&w)[2][2][4], auto fused_tag) {
     if constexpr (!decltype(fused_tag)::value) mask_logits(s, stage);
     auto weights = [&]() {
       f16x2 ovf = {0, 0};
@@ -579,19 +580,20 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
         }
       return __ballot(__builtin_isnan(ovf[0]) || __builtin_isnan(ovf[1])) != 0;
     };
-    if constexpr (!decltype(fused_tag)::value) again = weights();
-    if (again) {
+    if constexpr (!decltype(fused_tag)::value) {
+      if (weights()) {
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        float a = s[0][ct][0];
+        for (int ct = 0; ct < 2; ++ct) {
+          float a = s[0][ct][0];
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub)
+          for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) a = maxp(a, s[sub][ct][r]);
-        const float mx = maxp_xor32(maxp_xor16(a)) * p.scale_log2;  // the scale is >= 0
-        if (!(mx <= m[ct])) rescale(ct, maxp(m[ct], mx));
+            for (int r = 0; r < 4; ++r) a = maxp(a, s[sub][ct][r]);
+          const float mx = maxp_xor32(maxp_xor16(a)) * p.scale_log2;  // the scale is >= 0
+          if (!(mx <= m[ct])) rescale(ct, maxp(m[ct], mx));
+        }
+        weights();
       }
-      weights();
     }
 #pragma unroll
     for (int pair = 0; pair < 2; ++pair)
@@ -737,7 +739,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
           uint32_t w[2][2][4];
           mask_logits(s, it);
           logits_with_weights((it + 1) % 2, s_next, s, w);
-          compute_fast(s, it, it % 3, (it + 1) % 3, std::true_type{}, w, false, std::true_type{});
+          compute_fast(s, it, it % 3, (it + 1) % 3, std::true_type{}, w, std::true_type{});
 #pragma unroll
           for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
@@ -746,7 +748,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
           __syncthreads();
         }
         uint32_t w[2][2][4];
-        compute_fast(s, iters - 1, (iters - 1) % 3, 0, std::false_type{}, w, false, std::false_type{});
+        compute_fast(s, iters - 1, (iters - 1) % 3, 0, std::false_type{}, w, std::false_type{});
       } else {
         __syncthreads();
         for (int it = 0; it + 1 < iters; ++it) {
