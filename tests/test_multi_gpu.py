@@ -337,3 +337,21 @@ def test_tile_logit_far_above_the_first_stage(ptoks, min_eff):
         check_fp16_path(out, ref, wl, f"tile/large-logits/{ptoks}")
     else:
         check_attention(out, ref, "bf16", "f32", f"tile/large-logits/{ptoks}")
+
+
+def test_tile_long_context_many_partitions():
+    """One sequence with a 12000-token context and 96 new tokens (group 4: 384
+    rows, three 128-row tiles): the automatic plan splits the walk into many
+    64-token-stage partitions whose partials the multi-token merge combines;
+    every row against the oracle, both output forms, and against one
+    partition per walk."""
+    wl = generate("long-32k", num_seqs=1, ctx=(12000, 12000), num_heads=8, num_kv_heads=2, query_len=96,
+                  outlier_fraction=0.0)
+    gw = GpuWorkload(wl)
+    desc, kp, vp = oracle_pools(wl)
+    ref = oracle.paged_attend_causal(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.query_start,
+                                     wl.scale)
+    for ptoks, odt in ((0, torch.float32), (0, None), (1 << 30, torch.float32)):
+        _say(f"[multi] tile, 12000-token context, partition {ptoks}, out {odt}")
+        out = out_to_f64(gw.multi(kernel="tile", partition_tokens=ptoks, out_dtype=odt))
+        check_attention(out, ref, "bf16", "f32" if odt is not None else "bf16", f"tile/long/{ptoks}/{odt}")
