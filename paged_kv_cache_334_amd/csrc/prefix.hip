@@ -382,9 +382,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     for (int nt = 0; nt < 8; ++nt) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
-  // fast path: sum of the squares of the lane's own (fp16) weights, relative
-  // to the same m; with the weight sum it gives the effective token count
-  float s2[2] = {0.f, 0.f};
+  // fast path: the Gram matrix W W^T of each column tile's (fp16) weights,
+  // relative to the same m; its diagonal, each row's sum of squared weights,
+  // with the weight sum gives the effective token count
+  f32x4 g2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
   // (A column that has seen nothing yet and sees nothing now keeps m = -inf:
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   auto rescale = [&](int ct, float mn) {
     const float alpha = CAUSAL && m[ct] == mn ? 1.f : fast_exp2(m[ct] - mn);
     lsum[ct] *= alpha;
-    s2[ct] *= alpha * alpha;
+    g2[ct] *= alpha * alpha;
     o1[ct] *= alpha;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) o[ct][nt] *= alpha;
@@ -598,15 +599,6 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
         weights();
       }
     }
-#pragma unroll
-    for (int pair = 0; pair < 2; ++pair)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const f16x2 h = __builtin_bit_cast(f16x2, w[pair][ct][e]);
-          s2[ct] = __builtin_amdgcn_fdot2(h, h, s2[ct], false);
-        }
     // The value products and the conversion beside them run at raised wave
     // priority (from the fused step's last quarter on): when the SIMD's other
     // wave, of the other workgroup on the CU, is in its own fused step, its
@@ -617,10 +609,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
 #pragma unroll
     for (int pair = 0; pair < 2; ++pair) {
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        o1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            ones, __builtin_bit_cast(f16x8, make_uint4(w[pair][ct][0], w[pair][ct][1], w[pair][ct][2], w[pair][ct][3])),
-            o1[ct], 0, 0, 0);
+      for (int ct = 0; ct < 2; ++ct) {
+        const f16x8 wp = __builtin_bit_cast(f16x8, make_uint4(w[pair][ct][0], w[pair][ct][1], w[pair][ct][2], w[pair][ct][3]));
+        o1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, wp, o1[ct], 0, 0, 0);
+        // the same register as both operands: row i of A and column j of B are
+        // both query row i (j) of the tile, over the run's 32 tokens
+        g2[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wp, wp, g2[ct], 0, 0, 0);
+      }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const f16x8 va = __builtin_bit_cast(f16x8, value_piece(vb_i, pair, nt));
@@ -793,7 +788,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) nonfinite |= !__builtin_isfinite(o[ct][nt][r]);
       const float l = o1[ct][0];
-      const float sq = sum_xor32(sum_xor16(s2[ct]));
+      // row n's sum of squares: the Gram diagonal element (n, n), which lane
+      // 16 (n / 4) + n holds in register n % 4
+      const f32x4 gg = g2[ct];
+      const int r = n & 3;
+      const float own = r == 0 ? gg[0] : r == 1 ? gg[1] : r == 2 ? gg[2] : gg[3];
+      const float sq = __shfl(own, 16 * (n >> 2) + n);
       nonfinite |= row0 + 16 * ct + n < rows && l > 0.f && l * l < p.min_eff * sq;
     }
     const int wave_nonfinite = __ballot(nonfinite) != 0;
