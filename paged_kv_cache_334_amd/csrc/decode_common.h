@@ -241,8 +241,10 @@ __device__ __forceinline__ void pipelined_rounds(int rounds, Tile* ta, Tile* tb,
 // partition turns the row into NaN.  After a shared-prefix pass the chunk
 // partials of the prefix are folded in too, kPreBatch at a time: their loads
 // are issued together (one memory round trip per batch, not one per partial)
-// and the running maximum moves once per batch.
-constexpr int kPreBatch = 8;
+// and the running maximum moves once per batch.  16 covers the 9 chunks of a
+// 30000-token prefix in one trip (8 took two: shared-prefix call 188 -> 183
+// us, one more register).
+constexpr int kPreBatch = 16;
 
 template <int G, int HD, int NW>
 __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const PartRange& r,
