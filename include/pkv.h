@@ -128,6 +128,13 @@ typedef struct {
    * path wherever its values fit (error up to 2^-11 * (max |v| + |out|)).
    * Negative or NaN: PKV_EINVAL. */
   float min_eff_tokens;
+  /* Multi-token calls on PKV_KERNEL_TILE: 0 = the library's choice, a one-pass
+   * fp16 copy of the values the tiles walk, made at the start of the call in
+   * the workspace (pkv_paged_attn_multi_token_workspace_bytes counts it) when
+   * it takes at most 1 GiB, so that the tiles skip their own conversion;
+   * -1 = never (each tile converts the values it stages, in LDS).  Other
+   * values: PKV_EINVAL.  Ignored by the other calls and kernels. */
+  int32_t tile_value_copy;
 } pkv_decode_opts;
 
 /*
@@ -262,8 +269,10 @@ size_t pkv_paged_attn_multi_token_workspace_bytes(const pkv_pool_desc* pool, int
  *                 where each block read serves up to 128 rows, the 32-row
  *                 MFMA tiles below that) and blocks_in_flight (MFMA kernel);
  *                 no shared-prefix plan, one kv head per workgroup.  The tile
- *                 kernel multiplies bf16 values by weights split into bf16
- *                 hi + lo parts (the shared-prefix pass's exact form).
+ *                 kernel forms fp16 weights against fp16 values (from the
+ *                 workspace copy or converted in LDS, tile_value_copy) and
+ *                 takes the exact form (bf16 values, weights as bf16 hi + lo)
+ *                 where min_eff_tokens says, as the shared-prefix pass does.
  * Other arguments as in pkv_paged_attn_decode.  Device-side preconditions:
  * n_b <= context_lens[b] <= max_context_len and n_b <= max_query_len; a
  * sequence breaking them gets NaN in the rows the grid covers.  A sequence

@@ -106,6 +106,8 @@ constexpr int64_t kPrefixTargetWorkgroups = 512;
 // leaves the kernel to the library: from there a tile's single read of each
 // block serves enough rows to beat the 32-row tiles' repeated reads.
 constexpr int64_t kTileMinRows = 64;
+// Largest fp16 value copy the causal tiles make in the workspace (tile_value_copy).
+constexpr int64_t kValueCopyMaxBytes = int64_t(1) << 30;
 
 // Reads the host plan words: checks them against the call and sizes the
 // prefix pass.  Sets plan->cascade when at least one group exists.
@@ -297,6 +299,9 @@ struct MultiPlan {
   int inflight = 1;
   int blocks_per_part = 1;
   int num_parts = 1;
+  // causal tiles: blocks per sequence in the fp16 value copy (0: no copy), and its bytes
+  int copy_blocks = 0;
+  size_t copy_bytes = 0;
 };
 
 pkv_status make_multi_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_heads, int32_t num_query_tokens,
@@ -310,6 +315,8 @@ pkv_status make_multi_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t 
     return fail(PKV_EINVAL, "num_heads must be a positive multiple of num_kv_heads");
   if (num_seqs > 65535 || max_query_len > 65535)
     return fail(PKV_EUNSUPPORTED, "num_seqs and max_query_len must stay below 65536");
+  if (opts && opts->tile_value_copy != 0 && opts->tile_value_copy != -1)
+    return fail(PKV_EINVAL, "tile_value_copy must be 0 or -1");
   const int g = num_heads / pool->num_kv_heads;
   const int bf16 = pool->dtype == PKV_BF16;
   if ((st = check_min_eff(opts)) != PKV_OK) return st;
@@ -348,6 +355,15 @@ pkv_status make_multi_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t 
     plan->blocks_per_part = (int)bpp;
     plan->num_parts = max_blocks > 0 ? (int)((max_blocks + bpp - 1) / bpp) : 1;
     if (plan->num_parts > 65535) return fail(PKV_EUNSUPPORTED, "too many partitions; raise partition_tokens");
+    // the fp16 value copy: whole stages of every sequence's blocks (a stage past
+    // the last block reads zeros there)
+    const int64_t copy_blocks = (max_blocks + stage - 1) / stage * stage;
+    const int64_t copy_bytes =
+        (int64_t)num_seqs * copy_blocks * pool->num_kv_heads * pool->block_size * pool->head_dim * 2;
+    if ((!opts || opts->tile_value_copy == 0) && copy_blocks > 0 && copy_bytes <= kValueCopyMaxBytes) {
+      plan->copy_blocks = (int)copy_blocks;
+      plan->copy_bytes = (size_t)copy_bytes;
+    }
     const int64_t units = (int64_t)plan->num_parts * pool->num_kv_heads * num_seqs;
     if ((units + pkv::kXcds - 1) / pkv::kXcds * pkv::kXcds * plan->row_tiles > 0x7fffffff)
       return fail(PKV_EUNSUPPORTED, "too many workgroups; raise partition_tokens");
@@ -390,9 +406,16 @@ pkv_status make_multi_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t 
   return PKV_OK;
 }
 
-size_t multi_workspace(const MultiPlan& plan, int32_t num_query_tokens, int32_t num_heads, int32_t head_dim) {
+// Workspace of a multi-token call: split-K partials (num_parts > 1), then the
+// causal tiles' fp16 value copy at a 256-byte boundary.
+size_t multi_partials(const MultiPlan& plan, int32_t num_query_tokens, int32_t num_heads, int32_t head_dim) {
   if (plan.num_parts <= 1) return 0;
   return (size_t)num_query_tokens * num_heads * plan.num_parts * (2 + (size_t)head_dim) * sizeof(float);
+}
+size_t multi_workspace(const MultiPlan& plan, int32_t num_query_tokens, int32_t num_heads, int32_t head_dim) {
+  const size_t partials = multi_partials(plan, num_query_tokens, num_heads, head_dim);
+  if (!plan.copy_bytes) return partials;
+  return (partials + 255) / 256 * 256 + plan.copy_bytes;
 }
 
 // Workspace: split-K partials (num_parts > 1), then the prefix-pass partials.
@@ -688,6 +711,13 @@ pkv_status pkv_paged_attn_multi_token(const void* q, const void* k_pool, const v
     p.max_context = max_context_len;
     p.out = out;
     p.out_bf16 = a.out_bf16;
+    if (plan.copy_bytes) {
+      p.v_copy = static_cast<char*>(workspace) +
+                 (multi_partials(plan, num_query_tokens, num_heads, pool->head_dim) + 255) / 256 * 256;
+      p.copy_blocks = plan.copy_blocks;
+      e = pkv::launch_value_copy(p, pool->block_size, s);
+      if (e != hipSuccess) return fail(PKV_EHIP, std::string("value copy launch: ") + hipGetErrorString(e));
+    }
     e = pkv::launch_prefix(p, pool->block_size, plan.group, true, s);
   } else if (plan.mfma) {
     e = pkv::launch_multi_mfma(a, pool->block_size, plan.group, plan.col_tiles, plan.inflight, s);

@@ -144,6 +144,11 @@ struct PrefixArgs {
   int32_t max_context;
   void* out;
   int32_t out_bf16;
+  // Causal tiles: an fp16 copy of the values (NULL: the tiles convert in LDS),
+  // tile (sequence b, logical block j, kv head h) at ((b * copy_blocks + j) *
+  // num_kv_heads + h) in the pool's tile layout, tokens past the context zero.
+  void* v_copy;
+  int32_t copy_blocks;
 };
 
 bool vector_supported(int dtype_bf16, int head_dim, int block_size, int group);
@@ -158,6 +163,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, int block_size,
 // causal = false: the shared-prefix pass of cascade decode; true: 128-row
 // causal tiles of several new tokens per sequence.
 hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, bool causal, hipStream_t stream);
+// Fills p.v_copy for the causal tiles (num_seqs x copy_blocks blocks of num_kv_heads tiles).
+hipError_t launch_value_copy(const PrefixArgs& p, int block_size, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeArgs& a, int head_dim, int block_size, hipStream_t stream);
 
 // Several new tokens per sequence (a.query_start set).  Matrix-core kernel:

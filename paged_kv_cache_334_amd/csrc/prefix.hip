@@ -210,13 +210,14 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // causal tiles: the sequence's first query row, tokens new token 0 sees, the
   // sequence's partitions and this one, and the tokens of the chunk (from its
   // first) that the tile's last row sees
-  int qs = 0, base = 0, nparts = 1, part = 0, walk_end = 0;
+  int qs = 0, base = 0, nparts = 1, part = 0, walk_end = 0, seq = 0;
   int fewest = 0;  // fewest tokens of the chunk that a row of the tile sees
   if constexpr (CAUSAL) {
     if (unit >= p.num_chunks * p.num_kv_heads * p.num_seqs) return;
     part = unit % p.num_chunks;
     kvh = (unit / p.num_chunks) % p.num_kv_heads;
     const int b = unit / (p.num_chunks * p.num_kv_heads);
+    seq = b;
     qs = p.query_start[b];
     const int qe = p.query_start[b + 1];
     if (qs < 0 || qs > qe || qe > p.num_query_tokens) return;  // its rows are unknown: nothing is written
@@ -330,6 +331,14 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (int64_t)kvh * TILE;
   const int64_t block_bytes = (int64_t)p.num_kv_heads * TILE;
   const int iters = (blk_hi - blk_lo + NB - 1) / NB;
+  // Causal tiles with the workspace copy: the fast path stages the sequence's
+  // values from it, already fp16 and zero past the context, and skips its own
+  // conversion (the exact path still reads the pool).  Logical block j of the
+  // sequence sits at vcopy + j * block_bytes.
+  const bool from_copy = CAUSAL && p.v_copy != nullptr;
+  const char* vcopy =
+      from_copy ? static_cast<const char*>(p.v_copy) + ((int64_t)seq * p.copy_blocks * p.num_kv_heads + kvh) * TILE
+                : nullptr;
 
   // Staging: per iteration each wave moves four 1 KiB pieces of the keys and
   // four of the values straight from HBM/L2 into LDS (global_load_lds: lane l
@@ -337,7 +346,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // each lane picks the global chunk that belongs at its spot).  The loads
   // take no registers; the wave waits for them with an explicit counter wait
   // before the barrier that publishes the buffer.
-  auto stage_issue = [&](int it, int kb_i, int vb_i) {
+  auto stage_issue = [&](int it, int kb_i, int vb_i, bool copy = false) {
     const int first = blk_lo + it * NB;
     if (first - id_base >= 64) {  // next 64 ids
       id_base += 64;
@@ -364,7 +373,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
           // values: 8- and 16-token rows keep the pool's order; 32-token rows are rotated
           const int d = q / (BS / 8);
           const int vpiece = BS == 32 ? ((q & 3) ^ value_rot(d)) : BS == 16 ? (q & 1) : 0;
-          lds_dma16(lds_addr(&vbuf[vb_i][piece * 1024]), vpool + base, d * (BS * 2) + vpiece * 16);
+          const char* vsrc = copy ? vcopy + (int64_t)(first + kb) * block_bytes : vpool + base;
+          lds_dma16(lds_addr(&vbuf[vb_i][piece * 1024]), vsrc, d * (BS * 2) + vpiece * 16);
         }
       }
   };
@@ -461,6 +471,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // With causal tiles, the stage reaching past the tokens the tile sees has
   // those values zeroed on the way.
   auto convert_own = [&](int vb_i, int stage) {
+    if (from_copy) return;  // converted by the copy, zeros past the context
     if (CAUSAL && (stage + 1) * TOK > walk_end) {
 #pragma unroll
       for (int k = 0; k < kPiecesPerWave; ++k)
@@ -713,8 +724,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   bool redo = !((float)fewest >= p.min_eff) || (CAUSAL && !(p.scale_log2 > 0.f));
   if (!redo) {
     if (iters > 0) {
-      stage_issue(0, 0, 0);
-      stage_issue(min(1, iters - 1), 1, 1);
+      stage_issue(0, 0, 0, from_copy);
+      stage_issue(min(1, iters - 1), 1, 1, from_copy);
       lds_dma_wait<kPiecesPerWave>();  // all but stage 1's values
       __syncthreads();
       convert_own(0, 0);
@@ -740,7 +751,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
         }
         __syncthreads();
         for (int it = 0; it + 1 < iters; ++it) {
-          stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3);  // those buffers' stages are used up
+          stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3, from_copy);  // those buffers' stages are used up
           f32x4 s_next[4][2];
           uint32_t w[2][2][4];
           mask_logits(s, it);
@@ -758,7 +769,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       } else {
         __syncthreads();
         for (int it = 0; it + 1 < iters; ++it) {
-          stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3);
+          stage_issue(min(it + 2, iters - 1), it % 2, (it + 2) % 3, from_copy);
           lds_dma_wait<2 * kPiecesPerWave>();
           convert_own((it + 1) % 3, it + 1);
           lds_dma_wait<kPiecesPerWave>();
@@ -881,7 +892,61 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   }
 }
 
+
+// The causal tiles' fp16 copy of the values: one workgroup per (sequence,
+// logical block), all kv heads of the block.  Blocks the context reaches are
+// read through the block table and converted as the tiles would convert them
+// (bf16 -> fp16, round to nearest even; beyond fp16's range: +-inf); tokens
+// past the context, blocks past it up to the end of its last 64-token stage,
+// and blocks with an id outside the pool become zeros (such ids make the tile
+// kernel's rows NaN anyway).  Blocks past that stage are never read and are
+// left as they are.
+template <int BS>
+__global__ __launch_bounds__(256) void value_copy_kernel(PrefixArgs p) {
+  constexpr int TILE = BS * HD * 2;
+  constexpr int PIECES = TILE / 16;  // 16-byte pieces of a tile: dim q / (BS / 8), tokens 8 (q % (BS / 8)) ..
+  constexpr int NB = TOK / BS;
+  const int64_t bj = blockIdx.x;
+  const int j = (int)(bj % p.copy_blocks);
+  const int b = (int)(bj / p.copy_blocks);
+  const int ctx = min(max(p.context_lens[b], 0), p.max_context);
+  const int nblk = (ctx + BS - 1) / BS;
+  if (j >= (nblk + NB - 1) / NB * NB) return;
+  int id = -1;
+  if (j < nblk && j < p.max_blocks) {
+    id = p.block_tables[(int64_t)b * p.max_blocks + j];
+    if ((unsigned)id >= (unsigned)p.num_blocks) id = -1;
+  }
+  const char* src = reinterpret_cast<const char*>(p.v_pool) + (int64_t)(id < 0 ? 0 : id) * p.num_kv_heads * TILE;
+  uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(p.v_copy) + bj * p.num_kv_heads * TILE);
+  const int total = p.num_kv_heads * PIECES;
+  for (int x = threadIdx.x; x < total; x += 256) {
+    const int q = x % PIECES;
+    uint4 h = make_uint4(0, 0, 0, 0);
+    if (id >= 0) {
+      const int keep = min(max(ctx - (j * BS + 8 * (q % (BS / 8))), 0), 8);
+      const uint4 mk = keep_mask(keep);
+      const uint4 w = load16(src + 16 * (int64_t)x);
+      const uint32_t v[4] = {w.x & mk.x, w.y & mk.y, w.z & mk.z, w.w & mk.w};
+      h = make_uint4(pack_f16(bf16_lo(v[0]), bf16_hi(v[0])), pack_f16(bf16_lo(v[1]), bf16_hi(v[1])),
+                     pack_f16(bf16_lo(v[2]), bf16_hi(v[2])), pack_f16(bf16_lo(v[3]), bf16_hi(v[3])));
+    }
+    dst[x] = h;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_value_copy(const PrefixArgs& p, int block_size, hipStream_t s) {
+  const int64_t blocks = (int64_t)p.num_seqs * p.copy_blocks;
+  if (blocks <= 0 || blocks > 0x7fffffff || !p.v_copy) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (block_size == 8) hipLaunchKernelGGL(value_copy_kernel<8>, grid, block, 0, s, p);
+  else if (block_size == 16) hipLaunchKernelGGL(value_copy_kernel<16>, grid, block, 0, s, p);
+  else if (block_size == 32) hipLaunchKernelGGL(value_copy_kernel<32>, grid, block, 0, s, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, bool causal, hipStream_t s) {
   const int64_t units = (int64_t)p.num_kv_heads * p.num_chunks * (causal ? p.num_seqs : 1);

@@ -45,6 +45,7 @@ class DecodeOpts(ctypes.Structure):
         ("prefix_plan_dev", ctypes.c_void_p),
         ("prefix_plan_words", ctypes.c_size_t),
         ("min_eff_tokens", ctypes.c_float),
+        ("tile_value_copy", ctypes.c_int32),
     ]
 
 
@@ -221,12 +222,13 @@ def plan_shared_prefix(block_tables, context_lens, block_size, min_group_seqs=4,
     return PrefixPlan(host, dev)
 
 
-def _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup=0, min_eff_tokens=0.0):
+def _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup=0, min_eff_tokens=0.0,
+          tile_value_copy=0):
     base = (int(partition_tokens), KERNELS[kernel], int(blocks_in_flight), int(heads_per_workgroup))
     if prefix_plan is None:
-        return DecodeOpts(*base, None, None, 0, float(min_eff_tokens))
+        return DecodeOpts(*base, None, None, 0, float(min_eff_tokens), int(tile_value_copy))
     return DecodeOpts(*base, prefix_plan.host.ctypes.data, _ptr(prefix_plan.dev), prefix_plan.host.size,
-                      float(min_eff_tokens))
+                      float(min_eff_tokens), int(tile_value_copy))
 
 
 def paged_attn_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, max_context_len, partition_tokens=0,
@@ -309,9 +311,9 @@ def paged_attn_decode_scratch_limit() -> int:
 
 def paged_attn_multi_token_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, num_query_tokens, max_query_len,
                                            max_context_len, partition_tokens=0, kernel="auto",
-                                           blocks_in_flight=0, min_eff_tokens=0.0) -> int:
+                                           blocks_in_flight=0, min_eff_tokens=0.0, tile_value_copy=0) -> int:
     desc = pool_desc(k_pool, v_pool)
-    opts = _opts(partition_tokens, kernel, blocks_in_flight, None, 0, min_eff_tokens)
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, None, 0, min_eff_tokens, tile_value_copy)
     return int(lib.pkv_paged_attn_multi_token_workspace_bytes(ctypes.byref(desc), num_seqs, num_heads,
                                                               num_query_tokens, max_query_len, max_context_len,
                                                               ctypes.byref(opts)))
@@ -319,7 +321,7 @@ def paged_attn_multi_token_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, 
 
 def paged_attn_multi_token(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, max_query_len,
                            out=None, max_context_len=None, workspace=None, partition_tokens=0, kernel="auto",
-                           out_dtype=None, stream=None, blocks_in_flight=0, min_eff_tokens=0.0):
+                           out_dtype=None, stream=None, blocks_in_flight=0, min_eff_tokens=0.0, tile_value_copy=0):
     """Several new tokens per sequence, causal among them: row
     ``query_start[b] + i`` of ``q [T, Hq, D]`` (new token i of sequence b, at
     position ``context_lens[b] - n_b + i``) attends over the sequence's tokens up
@@ -344,7 +346,7 @@ def paged_attn_multi_token(q, k_pool, v_pool, block_tables, context_lens, query_
         odt = q.dtype if out_dtype is None else out_dtype
         out = torch.empty((ntok, nh, hd), dtype=odt, device=q.device)
     odt_code = PKV_BF16 if out.dtype == torch.bfloat16 else PKV_F32
-    opts = _opts(partition_tokens, kernel, blocks_in_flight, None, 0, min_eff_tokens)
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, None, 0, min_eff_tokens, tile_value_copy)
     need = int(lib.pkv_paged_attn_multi_token_workspace_bytes(ctypes.byref(desc), nseq, nh, ntok, int(max_query_len),
                                                               int(max_context_len), ctypes.byref(opts)))
     if workspace is None and need > 0:

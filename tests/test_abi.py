@@ -285,6 +285,34 @@ def test_multi_token_workspace(ops):
                                                               ctypes.byref(single)) == 0
 
 
+def test_tile_value_copy(ops):
+    """The causal tiles' fp16 value copy is counted in the multi-token
+    workspace: whole 64-token stages of every sequence's blocks, after the
+    split-K partials at a 256-byte boundary.  tile_value_copy = -1 drops it;
+    other values are rejected before any launch."""
+    d = _desc(ops)  # 8 kv heads, group 4, 16-token blocks, head_dim 128
+
+    def need(opts):
+        return ops.lib.pkv_paged_attn_multi_token_workspace_bytes(ctypes.byref(d), 4, 32, 128, 32, 256,
+                                                                  ctypes.byref(opts))
+
+    # 4 sequences x 32 new tokens x group 4 = 128 rows per sequence: the tile kernel
+    copy = 4 * 16 * 8 * (16 * 128 * 2)  # sequences x blocks (256 / 16, whole stages) x kv heads x tile bytes
+    assert need(ops.DecodeOpts(1 << 30, 0, 0)) == copy
+    assert need(ops.DecodeOpts(1 << 30, 3, 0, 0, None, None, 0, 0.0, -1)) == 0
+    partials = 128 * 32 * 4 * (128 + 2) * 4  # 4 partitions of 64 tokens
+    assert need(ops.DecodeOpts(64, 3, 0)) == (partials + 255) // 256 * 256 + copy
+    assert need(ops.DecodeOpts(64, 3, 0, 0, None, None, 0, 0.0, -1)) == partials
+    # fewer rows than the tile kernel's threshold: no tiles, no copy
+    assert ops.lib.pkv_paged_attn_multi_token_workspace_bytes(ctypes.byref(d), 4, 32, 12, 3, 256,
+                                                              ctypes.byref(ops.DecodeOpts(1 << 30, 0, 0))) == 0
+    for v in (1, 2, -2):
+        bad = ops.DecodeOpts(1 << 30, 3, 0, 0, None, None, 0, 0.0, v)
+        assert need(bad) == 0
+        assert _multi(ops, d, nseq=4, ntok=128, max_q=32, opts=bad) == 1
+        assert "tile_value_copy" in ops.lib.pkv_last_error().decode()
+
+
 def test_block_size_8(ops):
     """8-token blocks are accepted by the decode and multi-token kernels (the
     matrix-core ones walk them in pairs) and by the shared-prefix pass."""

@@ -1,6 +1,7 @@
 """Several new tokens per sequence, causal among them (pkv_paged_attn_multi_token),
 on the GPU against the oracle's paged_attend_causal: small ragged cases on
-every kernel (vector, 32-row MFMA tiles, 128-row LDS-staged tiles) and
+every kernel (vector, 32-row MFMA tiles, 128-row LDS-staged tiles with and
+without the workspace's fp16 value copy) and
 partitioning, the broken-length paths, values at the fp16 limit for the tile
 kernel, and the verify and prompt-chunk workloads at full size."""
 
@@ -109,18 +110,38 @@ def test_small_multi(small_case, kernel, ptoks, inflight, out_dtype):
                     f"{name}/{kernel}/{ptoks}")
 
 
+@pytest.mark.parametrize("copy", [0, -1])
 @pytest.mark.parametrize("ptoks", [0, 64])
-def test_small_multi_tile_fp16_path(small_case, ptoks):
+def test_small_multi_tile_fp16_path(small_case, ptoks, copy):
     """The tiles' fp16 path wherever the values fit (min_eff_tokens 1: no walk
     goes back to the exact path for having few effective tokens), against its
     own error bound; with the default (128) the small rows here would take the
-    exact path."""
+    exact path.  Values from the workspace's fp16 copy (copy 0) or converted
+    in LDS by each tile (copy -1): the same bits either way."""
     name, wl, gw, _, ref = small_case
     if not _mfma_ok(wl):
         pytest.skip("matrix-core kernels: bf16, head_dim 128")
-    _say(f"[multi] {name} tile fp16 path ptoks={ptoks}")
-    out = out_to_f64(gw.multi(kernel="tile", partition_tokens=ptoks, min_eff_tokens=1.0, out_dtype=torch.float32))
-    check_fp16_path(out, ref, wl, f"{name}/tile-fp16/{ptoks}")
+    _say(f"[multi] {name} tile fp16 path ptoks={ptoks} copy={copy}")
+    out = gw.multi(kernel="tile", partition_tokens=ptoks, min_eff_tokens=1.0, out_dtype=torch.float32,
+                   tile_value_copy=copy)
+    check_fp16_path(out_to_f64(out), ref, wl, f"{name}/tile-fp16/{ptoks}/{copy}")
+    if copy == -1:
+        other = gw.multi(kernel="tile", partition_tokens=ptoks, min_eff_tokens=1.0, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(out, other), f"{name}: the value copy changed the result"
+
+
+@pytest.mark.parametrize("ptoks", [0, 64, 192])
+def test_small_multi_tile_without_value_copy(small_case, ptoks):
+    """The tiles converting their values in LDS (tile_value_copy -1), on the
+    default effective-token floor, against the oracle in both output forms."""
+    name, wl, gw, _, ref = small_case
+    if not _mfma_ok(wl):
+        pytest.skip("matrix-core kernels: bf16, head_dim 128")
+    for odt in (None, torch.float32):
+        _say(f"[multi] {name} tile without value copy ptoks={ptoks} out={odt}")
+        out = out_to_f64(gw.multi(kernel="tile", partition_tokens=ptoks, out_dtype=odt, tile_value_copy=-1))
+        check_attention(out, ref, "bf16", "f32" if odt is not None else "bf16", f"{name}/tile-nocopy/{ptoks}")
 
 
 def test_small_multi_deterministic(small_case):
