@@ -711,6 +711,7 @@ pkv_status pkv_paged_attn_multi_token(const void* q, const void* k_pool, const v
     p.max_context = max_context_len;
     p.out = out;
     p.out_bf16 = a.out_bf16;
+    p.longest_first = num_seqs > 1 && num_seqs <= pkv::kMaxRankSeqs && max_context_len < (1 << 23);
     if (plan.copy_bytes) {
       p.v_copy = static_cast<char*>(workspace) +
                  (multi_partials(plan, num_query_tokens, num_heads, pool->head_dim) + 255) / 256 * 256;

@@ -149,6 +149,10 @@ struct PrefixArgs {
   // num_kv_heads + h) in the pool's tile layout, tokens past the context zero.
   void* v_copy;
   int32_t copy_blocks;
+  // Causal tiles: sequences in order of decreasing context length (ties by
+  // index), each one's row tiles from the last (longest walk) down.  The host
+  // sets it for 2..kMaxRankSeqs sequences and max_context < 2^23.
+  int32_t longest_first;
 };
 
 bool vector_supported(int dtype_bf16, int head_dim, int block_size, int group);

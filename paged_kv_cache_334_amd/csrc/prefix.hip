@@ -173,6 +173,9 @@ __device__ __forceinline__ void values_zero_tail(unsigned char* v, int keep) {
   *piece = make_uint4(w.x & mk.x, w.y & mk.y, w.z & mk.z, w.w & mk.w);
 }
 
+static_assert(64 * NW >= kMaxRankSeqs, "longest-first ranking: one sequence per thread");
+static_assert(2 * kMaxRankSeqs * sizeof(int) <= STAGE_HALF, "ranking scratch inside one value buffer");
+
 template <int BS, int G, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   constexpr int NB = TOK / BS;          // blocks per iteration
@@ -197,7 +200,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int unit = (slot / p.num_tiles) * kXcds + xcd;
-  int tile = slot % p.num_tiles;
+  // Causal tiles in longest-first order: later row tiles walk more tokens, so
+  // a unit's tiles run from the last down (the first one then also brings
+  // every key and value the others read into the L2).
+  int tile = CAUSAL && p.longest_first ? p.num_tiles - 1 - slot % p.num_tiles : slot % p.num_tiles;
 
   // What the two modes settle here: the kv head, the chunk's blocks
   // [blk_lo, blk_hi) of block-table row bt, the rows [0, rows) of the unit and
@@ -216,7 +222,34 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     if (unit >= p.num_chunks * p.num_kv_heads * p.num_seqs) return;
     part = unit % p.num_chunks;
     kvh = (unit / p.num_chunks) % p.num_kv_heads;
-    const int b = unit / (p.num_chunks * p.num_kv_heads);
+    int b = unit / (p.num_chunks * p.num_kv_heads);
+    if (p.longest_first) {
+      // b becomes the sequence of rank b by decreasing context length, every
+      // workgroup ranking the lengths for itself (one sequence per thread):
+      // key (length + 1) * 256 + 255 - index, distinct and larger for longer
+      // sequences (and for smaller indices among equal lengths; a broken
+      // length counts as -1), rank = how many keys are larger.  The scratch is
+      // the third value buffer, which no load writes before the pipeline's
+      // first barrier.
+      int* sm_key = reinterpret_cast<int*>(&vbuf[2][0]);
+      int* sm_pick = sm_key + kMaxRankSeqs;
+      const int t = threadIdx.x;
+      uint32_t key = 0;
+      if (t < p.num_seqs) {
+        const int raw = p.context_lens[t];
+        const int len = raw < 0 || raw > p.max_context ? -1 : raw;
+        key = (uint32_t)(len + 1) * 256u + (uint32_t)(255 - t);
+        sm_key[t] = (int)key;
+      }
+      __syncthreads();
+      if (t < p.num_seqs) {
+        int rank = 0;
+        for (int o = 0; o < p.num_seqs; ++o) rank += (uint32_t)sm_key[o] > key;
+        if (rank == b) sm_pick[0] = t;
+      }
+      __syncthreads();
+      b = sm_pick[0];
+    }
     seq = b;
     qs = p.query_start[b];
     const int qe = p.query_start[b + 1];

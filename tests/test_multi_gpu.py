@@ -269,19 +269,24 @@ def test_full_multi(name, out_dtype, kernel):
     check_attention(out[rows], ref, wl.dtype, "f32" if odt is not None else "bf16", f"{name}/full/{out_dtype}")
 
 
-def test_more_sequences_than_the_ranking_takes():
-    """300 sequences of 1-4 new tokens: the matrix-core kernel's natural-order
-    walk (longest-first ranking covers at most 256 sequences)."""
-    wl = generate("gqa-70b", num_seqs=300, ctx=(1, 60), num_heads=16, num_kv_heads=2, query_len=(1, 4))
+@pytest.mark.parametrize("num_seqs", [256, 300])
+def test_more_sequences_than_the_ranking_takes(num_seqs):
+    """256 sequences of 1-4 new tokens (the most the longest-first ranking of
+    the matrix-core kernel and the 128-row tiles takes, many lengths tied) and
+    300 (natural order), on both kernels."""
+    wl = generate("gqa-70b", num_seqs=num_seqs, ctx=(1, 60), num_heads=16, num_kv_heads=2, query_len=(1, 4))
     gw = GpuWorkload(wl)
     desc, k_pool, v_pool = oracle_pools(wl)
     ref = oracle.paged_attend_causal(wl.q, k_pool, v_pool, desc, wl.block_tables, wl.context_lens, wl.query_start,
                                      wl.scale)
-    for ptoks in (1 << 30, 32):
-        _say(f"[multi] 300 sequences, partition {ptoks}")
-        out = out_to_f64(gw.multi(kernel="mfma", partition_tokens=ptoks, blocks_in_flight=1, out_dtype=torch.float32))
-        torch.cuda.synchronize()
-        check_attention(out, ref, wl.dtype, "f32", f"300-seqs/multi/{ptoks}")
+    for kernel in ("mfma", "tile"):
+        for ptoks in (1 << 30, 32):
+            _say(f"[multi] {num_seqs} sequences, {kernel}, partition {ptoks}")
+            inflight = 1 if kernel == "mfma" else 0
+            out = out_to_f64(gw.multi(kernel=kernel, partition_tokens=ptoks, blocks_in_flight=inflight,
+                                      out_dtype=torch.float32))
+            torch.cuda.synchronize()
+            check_attention(out, ref, wl.dtype, "f32", f"{num_seqs}-seqs/{kernel}/{ptoks}")
 
 
 @pytest.mark.parametrize("min_eff", [0.0, 1.0])
