@@ -110,6 +110,7 @@ struct PartRange {
   int nblocks;  // blocks of the sequence
   int nparts;   // partitions the sequence spans
   int blk_lo, blk_hi;
+  int pre;      // shared-prefix partials merged at the end (0: none)
 };
 
 template <int BS>
@@ -129,6 +130,13 @@ __device__ __forceinline__ PartRange part_range(const DecodeArgs& a, const SeqPi
   if (r.start > 0 && r.nparts == 0) r.nparts = 1;  // an empty suffix still merges the prefix partials
   r.blk_lo = r.start + r.part * a.blocks_per_part;
   r.blk_hi = min(r.nblocks, r.blk_lo + a.blocks_per_part);
+  // The prefix partials of the sequence's group path, merged when this pass is
+  // its only suffix partition.  Counted here, before the walk, so that the
+  // dependent reads up the group tree overlap the first tile loads instead of
+  // adding their round trips to the end of the workgroup.
+  r.pre = (r.start > 0 && r.nparts == 1)
+              ? path_slots(plan_groups(a.plan), plan_group_of(a.plan)[r.b], a.plan[kPlanBlockSize], a.prefix_chunk_blocks)
+              : 0;
   return r;
 }
 
@@ -257,10 +265,8 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
   for (int idx = threadIdx.x; idx < G * HD; idx += 64 * NW) {
     const int h = idx / HD, d = idx % HD;
     const int hq = h0 + h;
-    // partials of the shared-prefix pass, merged here when this pass is the only suffix partition
-    const int pre = (r.start > 0 && r.nparts == 1)
-                        ? path_slots(plan_groups(a.plan), plan_group_of(a.plan)[r.b], a.plan[kPlanBlockSize], a.prefix_chunk_blocks)
-                        : 0;
+    // partials of the shared-prefix pass (counted in part_range)
+    const int pre = r.pre;
     const int64_t pre_base = ((int64_t)r.b * a.num_heads + hq) * a.prefix_chunks;
     float big_m = -INFINITY;
 #pragma unroll
