@@ -3,6 +3,8 @@
 // per-wave softmax states into an output row or a split-K partial.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -262,8 +264,12 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
 #pragma unroll
   for (int w = 0; w < NW; ++w) any_bad |= sm_bad[w];
   const int h0 = r.kvh * G;
-  for (int idx = threadIdx.x; idx < G * HD; idx += 64 * NW) {
-    const int h = idx / HD, d = idx % HD;
+  // E elements of row h, dims d0 + stride * e: one thread's share.  All its
+  // prefix-partial loads of a batch are issued together, so a thread with
+  // several elements of one row pays one round trip per batch, not one per
+  // element, and loads the row's maxima and sums once.
+  auto merge_row = [&](auto e_tag, int h, int d0, int stride) {
+    constexpr int E = decltype(e_tag)::value;
     const int hq = h0 + h;
     // partials of the shared-prefix pass (counted in part_range)
     const int pre = r.pre;
@@ -271,22 +277,26 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
     float big_m = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][h]);
-    float l = 0.f, acc = 0.f;
+    float l = 0.f, acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float f = (sm_m[w][h] == -INFINITY) ? 0.f : fast_exp2(sm_m[w][h] - big_m);
       l = fmaf(f, sm_l[w][h], l);
-      acc = fmaf(f, sm_acc[w][h][d], acc);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(f, sm_acc[w][h][d0 + stride * e], acc[e]);
     }
     for (int c0 = 0; c0 < pre; c0 += kPreBatch) {
       // slots past the last partial are read in bounds (clamped) and dropped by a select
-      float pm[kPreBatch], pl[kPreBatch], pa[kPreBatch];
+      float pm[kPreBatch], pl[kPreBatch], pa[kPreBatch][E];
 #pragma unroll
       for (int k = 0; k < kPreBatch; ++k) {
         const int64_t s = pre_base + min(c0 + k, pre - 1);
         pm[k] = a.pre_m[s];
         pl[k] = a.pre_l[s];
-        pa[k] = a.pre_acc[s * HD + d];
+#pragma unroll
+        for (int e = 0; e < E; ++e) pa[k][e] = a.pre_acc[s * HD + d0 + stride * e];
       }
       float bm = -INFINITY;
 #pragma unroll
@@ -294,7 +304,8 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
       if (bm > big_m) {  // move the reference once for the batch
         const float f = big_m == -INFINITY ? 0.f : fast_exp2(big_m - bm);
         l *= f;
-        acc *= f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] *= f;
         big_m = bm;
       }
 #pragma unroll
@@ -302,26 +313,40 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
         // a NaN partial (bad block id in the prefix) stays NaN through the exponent
         const float f = c0 + k < pre ? fast_exp2(pm[k] - big_m) : 0.f;
         l = fmaf(f, c0 + k < pre ? pl[k] : 0.f, l);
-        acc = fmaf(f, c0 + k < pre ? pa[k] : 0.f, acc);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(f, c0 + k < pre ? pa[k][e] : 0.f, acc[e]);
       }
     }
     if (any_bad) {
       big_m = NAN;
-      acc = NAN;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = NAN;
     }
-    if (r.nparts == 1) {
-      const float o = acc / l;
-      const int64_t oi = ((int64_t)r.qrow * a.num_heads + hq) * HD + d;
-      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_rne(o);
-      else reinterpret_cast<float*>(a.out)[oi] = o;
-    } else {
-      const int64_t pi = ((int64_t)r.qrow * a.num_heads + hq) * a.num_parts + r.part;
-      a.ws_acc[pi * HD + d] = acc;
-      if (d == 0) {
-        a.ws_m[pi] = big_m;
-        a.ws_l[pi] = l;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int d = d0 + stride * e;
+      if (r.nparts == 1) {
+        const float o = acc[e] / l;
+        const int64_t oi = ((int64_t)r.qrow * a.num_heads + hq) * HD + d;
+        if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_rne(o);
+        else reinterpret_cast<float*>(a.out)[oi] = o;
+      } else {
+        const int64_t pi = ((int64_t)r.qrow * a.num_heads + hq) * a.num_parts + r.part;
+        a.ws_acc[pi * HD + d] = acc[e];
+        if (d == 0) {
+          a.ws_m[pi] = big_m;
+          a.ws_l[pi] = l;
+        }
       }
     }
+  };
+  constexpr int T = 64 * NW;
+  if constexpr (G * HD >= T && T % G == 0 && HD % (T / G) == 0) {
+    // T / G threads per row, HD * G / T consecutive-stride elements each
+    constexpr int TPR = T / G;
+    merge_row(std::integral_constant<int, HD / TPR>{}, (int)threadIdx.x / TPR, (int)threadIdx.x % TPR, TPR);
+  } else {
+    for (int idx = threadIdx.x; idx < G * HD; idx += T) merge_row(std::integral_constant<int, 1>{}, idx / HD, idx % HD, 1);
   }
 }
 
