@@ -42,6 +42,9 @@ pkv_status check_pool(const pkv_pool_desc* pool) {
   if (pool->head_dim != 64 && pool->head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
   if ((int64_t)pool->num_blocks * pool->block_size >= (int64_t(1) << 31))
     return fail(PKV_EINVAL, "num_blocks * block_size must stay below 2^31");
+  // one block of every kv head, in bytes: the kernels form block offsets as id * that in 32 x 32 -> 64 bits
+  if ((int64_t)pool->num_kv_heads * pool->block_size * pool->head_dim * (pool->dtype == PKV_F32 ? 4 : 2) >= (int64_t(1) << 31))
+    return fail(PKV_EINVAL, "num_kv_heads * block_size * head_dim * element size must stay below 2^31");
   return PKV_OK;
 }
 

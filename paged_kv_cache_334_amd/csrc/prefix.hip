@@ -362,7 +362,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
 
   const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (int64_t)kvh * TILE;
   const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (int64_t)kvh * TILE;
-  const int64_t block_bytes = (int64_t)p.num_kv_heads * TILE;
+  // bytes of one block of every kv head: below 2^31 (the host checks the pool)
+  const uint32_t block_bytes = (uint32_t)p.num_kv_heads * TILE;
   const int iters = (blk_hi - blk_lo + NB - 1) / NB;
   // Causal tiles with the workspace copy: the fast path stages the sequence's
   // values from it, already fp16 and zero past the context, and skips its own
@@ -394,7 +395,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
         const int piece = wave + NW * k;  // 1 KiB piece of the stage
         const int kb = piece * 1024 / TILE;
         const int in_tile = piece * 1024 % TILE;
-        const int64_t base = (int64_t)__builtin_amdgcn_readlane(ids, first + kb - id_base) * block_bytes;
+        // ids are in [0, num_blocks) here (load_ids): 32 x 32 -> 64-bit product
+        const uint64_t base = (uint64_t)(uint32_t)__builtin_amdgcn_readlane(ids, first + kb - id_base) * block_bytes;
         const int q = in_tile / 16 + lane;  // 16-byte piece of the tile that this lane's LDS spot holds
         if (half == 0) {
           // keys: chunk q / BS, slot q % BS <- that chunk's key_slot_token (16/32-token
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
           // values: 8- and 16-token rows keep the pool's order; 32-token rows are rotated
           const int d = q / (BS / 8);
           const int vpiece = BS == 32 ? ((q & 3) ^ value_rot(d)) : BS == 16 ? (q & 1) : 0;
-          const char* vsrc = copy ? vcopy + (int64_t)(first + kb) * block_bytes : vpool + base;
+          const char* vsrc = copy ? vcopy + (uint64_t)(uint32_t)(first + kb) * block_bytes : vpool + base;
           lds_dma16(lds_addr(&vbuf[vb_i][piece * 1024]), vsrc, d * (BS * 2) + vpiece * 16);
         }
       }

@@ -75,6 +75,20 @@ def test_bad_pool_is_rejected(ops, kw, status):
     assert ops.lib.pkv_last_error().decode()
 
 
+@pytest.mark.parametrize("heads,dtype", [(1 << 19, "PKV_BF16"), (1 << 18, "PKV_F32")])
+def test_block_bytes_bound(ops, heads, dtype):
+    """One block of every kv head must stay below 2^31 bytes (the kernels form
+    block offsets as a 32 x 32 -> 64-bit product); the pool check says so
+    before anything else is looked at."""
+    d = _desc(ops, num_kv_heads=heads, dtype=getattr(ops, dtype))
+    assert _decode(ops, d, num_heads=heads) == 1
+    assert "element size must stay below 2^31" in ops.lib.pkv_last_error().decode()
+    # half as many heads passes the pool check: a split plan then sizes its workspace
+    ok = _desc(ops, num_kv_heads=heads // 2, dtype=getattr(ops, dtype))
+    split = ops.DecodeOpts(64, 0, 0)
+    assert ops.lib.pkv_paged_attn_workspace_bytes(ctypes.byref(ok), 4, heads // 2, 256, ctypes.byref(split)) > 0
+
+
 def test_bad_decode_arguments(ops):
     d = _desc(ops)
     assert _decode(ops, d, num_heads=12) == 1            # not a multiple of kv heads
