@@ -56,6 +56,11 @@ CASES = {
     # more rows than one 128-row tile (150 x 4 = 600 rows), a long prefix split into several chunks
     "g4-many-rows": lambda: generate("shared-prefix", num_seqs=150, shared_prefix=2048, ctx=(1, 40), num_heads=8,
                                      num_kv_heads=2),
+    # group 8, one tile per kv head and a 1280-token prefix: 20 one-iteration
+    # chunks, so the suffix merge folds them in two batches, four elements of one
+    # head row per thread
+    "g8-many-chunks": lambda: generate("shared-prefix", num_seqs=6, shared_prefix=1280, ctx=(1, 30), num_heads=16,
+                                       num_kv_heads=2),
 }
 
 
