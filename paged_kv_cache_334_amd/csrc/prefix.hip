@@ -654,6 +654,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int pair = 0; pair < 2; ++pair) {
+      // all eight value pieces of the run read before its matrix instructions
+      // (the scheduler otherwise keeps two in flight and waits on each pair):
+      // shared-prefix -2.9 us, prefill -2.8 us per call, interleaved A/B
+      uint4 vp[8];
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) vp[nt] = value_piece(vb_i, pair, nt);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const f16x8 wp = __builtin_bit_cast(f16x8, make_uint4(w[pair][ct][0], w[pair][ct][1], w[pair][ct][2], w[pair][ct][3]));
@@ -664,7 +671,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const f16x8 va = __builtin_bit_cast(f16x8, value_piece(vb_i, pair, nt));
+        const f16x8 va = __builtin_bit_cast(f16x8, vp[nt]);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
           o[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
