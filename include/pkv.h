@@ -135,6 +135,18 @@ typedef struct {
    * -1 = never (each tile converts the values it stages, in LDS).  Other
    * values: PKV_EINVAL.  Ignored by the other calls and kernels. */
   int32_t tile_value_copy;
+  /* Cascade decode: an fp16 copy of this plan's shared-prefix values, made by
+   * pkv_prefix_values_f16 (DEVICE memory, 16-byte aligned), and its size in
+   * bytes; NULL / 0 = none.  With it the shared-prefix pass stages those
+   * values as they are instead of converting the bf16 values it reads to fp16
+   * (the same bits; its exact path still reads the pool).  The copy holds as
+   * long as the plan and the values of the prefix blocks do not change, which
+   * copy-on-write guarantees for blocks that stay shared; the caller makes it
+   * again otherwise.  A size below pkv_prefix_values_f16_bytes() for the plan,
+   * or a misaligned pointer: PKV_EINVAL.  Ignored without a plan and by the
+   * multi-token call. */
+  const void* prefix_values_f16;
+  size_t prefix_values_f16_bytes;
 } pkv_decode_opts;
 
 /*
@@ -174,6 +186,36 @@ typedef struct {
 size_t pkv_plan_shared_prefix(const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                               int32_t max_blocks_per_seq, int32_t block_size, int32_t min_group_seqs,
                               int32_t min_prefix_blocks, int32_t* plan, size_t plan_words);
+
+/*
+ * fp16 copy of a plan's shared-prefix values, for pkv_decode_opts.prefix_values_f16.
+ * Shared blocks are read-only while they are shared (a write to one first
+ * copies it: "PagedAttention Explained", "Shared Prefix Caching"), so the
+ * fp16 form the shared-prefix pass feeds to the matrix cores can be made once
+ * per plan and reused by every decode step that uses the plan, instead of once
+ * per 128-row tile and step.  Bf16 pools with head_dim 128 only.
+ *
+ * Layout: the pass blocks of each group in plan order (group g's blocks
+ * [start_g, covered end_g) of its leader's table, the blocks its pass walks),
+ * each block's values for every kv head in the pool's tile layout, converted
+ * to fp16 (round to nearest even; beyond fp16's range: +-inf, which the pass
+ * then sends to its exact path).  A block id outside the pool gives zeros.
+ *
+ * pkv_prefix_values_f16_bytes: bytes of that copy for a HOST plan; 0 for an
+ * invalid plan, a pool other than bf16 / head_dim 128, or a plan with no pass
+ * blocks.
+ *
+ * pkv_prefix_values_f16: writes the copy to out (DEVICE, 16-byte aligned, at
+ * least that many bytes) on stream, reading v_pool and the block tables
+ * (DEVICE) through the plan (HOST words, checked as the decode call checks
+ * them, and their DEVICE copy).  No copy needed (no pass blocks): PKV_OK with
+ * nothing launched.
+ */
+size_t pkv_prefix_values_f16_bytes(const pkv_pool_desc* pool, const int32_t* plan, size_t plan_words);
+pkv_status pkv_prefix_values_f16(const void* v_pool, const int32_t* block_tables, int32_t num_seqs,
+                                 int32_t max_blocks_per_seq, const pkv_pool_desc* pool, const int32_t* plan,
+                                 const int32_t* plan_dev, size_t plan_words, void* out, size_t out_bytes,
+                                 void* stream);
 
 /* Bytes of workspace pkv_paged_attn_decode needs for these shapes and options
  * (0 when the call runs as a single pass).  Returns 0 for invalid shapes. */

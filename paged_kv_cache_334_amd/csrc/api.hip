@@ -438,6 +438,19 @@ size_t workspace_for(const Plan& plan, int32_t num_seqs, int32_t num_heads, int3
   return split_bytes(plan, num_seqs, num_heads, head_dim) + prefix_bytes(plan, num_seqs, num_heads, head_dim);
 }
 
+// Pass blocks of a checked plan's groups (the fp16 prefix-value copy's blocks).
+int64_t prefix_copy_blocks(const pkv_pool_desc* pool, const int32_t* w) {
+  const int32_t* gw = pkv::plan_groups(w);
+  int64_t n = 0;
+  for (int32_t gi = 0; gi < w[pkv::kPlanGroups]; ++gi)
+    n += pkv::group_pass_blocks(gw + pkv::kGroupWords * gi, pool->block_size);
+  return n;
+}
+
+size_t prefix_copy_bytes(const pkv_pool_desc* pool, const int32_t* w) {
+  return (size_t)prefix_copy_blocks(pool, w) * pool->num_kv_heads * pool->block_size * pool->head_dim * 2;
+}
+
 }  // namespace
 
 extern "C" {
@@ -447,6 +460,55 @@ size_t pkv_paged_attn_workspace_bytes(const pkv_pool_desc* pool, int32_t num_seq
   Plan plan;
   if (make_plan(pool, num_seqs, num_heads, max_context_len, INT32_MAX, opts, &plan) != PKV_OK) return 0;
   return workspace_for(plan, num_seqs, num_heads, pool->head_dim);
+}
+
+size_t pkv_prefix_values_f16_bytes(const pkv_pool_desc* pool, const int32_t* plan, size_t plan_words) {
+  if (check_pool(pool) != PKV_OK || pool->dtype != PKV_BF16 || pool->head_dim != 128) return 0;
+  if (!plan || plan_words < (size_t)pkv::kPlanHeader || plan[0] != pkv::kPlanMagic) return 0;
+  // checked as a decode call checks it (any device pointer will do for the size)
+  pkv_decode_opts o{};
+  o.prefix_plan = plan;
+  o.prefix_plan_dev = plan;
+  o.prefix_plan_words = plan_words;
+  Plan p;
+  if (plan_cascade(pool, plan[pkv::kPlanSeqs], INT32_MAX, 1, &o, &p) != PKV_OK || !p.cascade) return 0;
+  return prefix_copy_bytes(pool, plan);
+}
+
+pkv_status pkv_prefix_values_f16(const void* v_pool, const int32_t* block_tables, int32_t num_seqs,
+                                 int32_t max_blocks_per_seq, const pkv_pool_desc* pool, const int32_t* plan,
+                                 const int32_t* plan_dev, size_t plan_words, void* out, size_t out_bytes,
+                                 void* stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (pool->dtype != PKV_BF16 || pool->head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "the fp16 prefix-value copy needs a bf16 pool with head_dim 128");
+  if (num_seqs < 0 || max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "bad num_seqs or max_blocks_per_seq");
+  if (!plan || !plan_dev) return fail(PKV_EINVAL, "prefix plan: host or device words missing");
+  pkv_decode_opts o{};
+  o.prefix_plan = plan;
+  o.prefix_plan_dev = plan_dev;
+  o.prefix_plan_words = plan_words;
+  Plan p;
+  if ((st = plan_cascade(pool, num_seqs, max_blocks_per_seq, 1, &o, &p)) != PKV_OK) return st;
+  if (!p.cascade) return ok();  // no pass blocks: nothing to copy
+  const int64_t blocks = prefix_copy_blocks(pool, plan);
+  if (blocks > 0x7fffffff) return fail(PKV_EUNSUPPORTED, "prefix plan: too many pass blocks");
+  if (!v_pool || !block_tables || !out) return fail(PKV_EINVAL, "a data pointer is NULL");
+  if (!aligned16(v_pool) || !aligned16(out)) return fail(PKV_EINVAL, "v_pool and out must be 16-byte aligned");
+  if (out_bytes < prefix_copy_bytes(pool, plan))
+    return fail(PKV_EINVAL, "out is smaller than pkv_prefix_values_f16_bytes()");
+  pkv::PrefixArgs a{};
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.plan = plan_dev;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = pool->num_blocks;
+  a.v_copy = out;
+  hipError_t e = pkv::launch_prefix_value_copy(a, pool->block_size, (int)blocks, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_EHIP, std::string("prefix value copy launch: ") + hipGetErrorString(e));
+  return ok();
 }
 
 }  // extern "C"
@@ -473,6 +535,10 @@ pkv_status decode_planned(const Plan& plan, const void* q, const void* k_pool, c
   const size_t need = workspace_for(plan, num_seqs, num_heads, pool->head_dim);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(PKV_EWORKSPACE, "workspace missing, misaligned or smaller than pkv_paged_attn_workspace_bytes()");
+  const bool f16_copy = plan.cascade && opts->prefix_values_f16 != nullptr;
+  if (f16_copy && (!aligned16(opts->prefix_values_f16) ||
+                   opts->prefix_values_f16_bytes < prefix_copy_bytes(pool, opts->prefix_plan)))
+    return fail(PKV_EINVAL, "prefix_values_f16 misaligned or smaller than pkv_prefix_values_f16_bytes()");
 
   pkv::DecodeArgs a{};
   a.q = q;
@@ -525,6 +591,7 @@ pkv_status decode_planned(const Plan& plan, const void* q, const void* k_pool, c
     p.ws_m = pre;
     p.ws_l = pre + rows;
     p.ws_acc = pre + 2 * rows;
+    p.v_copy = f16_copy ? const_cast<void*>(opts->prefix_values_f16) : nullptr;
     hipError_t pe = pkv::launch_prefix(p, pool->block_size, plan.group, false, s);
     if (pe != hipSuccess) return fail(PKV_EHIP, std::string("prefix launch: ") + hipGetErrorString(pe));
     a.start_blocks = opts->prefix_plan_dev + pkv::kPlanHeader;

@@ -95,6 +95,13 @@ __host__ __device__ inline const int32_t* plan_groups(const int32_t* plan) {
   return plan + kPlanHeader + 2 * plan[kPlanSeqs];
 }
 // Prefix chunks of one group (chunk_blocks blocks each, the last one shorter).
+// Blocks of a group's own pass, [start, covered end): its part of the fp16
+// copy of the prefix values (pkv_prefix_values_f16), in plan order.
+__host__ __device__ inline int group_pass_blocks(const int32_t* gr, int block_size) {
+  const int n = prefix_covered_blocks(gr[kGroupPrefix], block_size) - gr[kGroupStart];
+  return n > 0 ? n : 0;
+}
+
 __host__ __device__ inline int group_chunks(const int32_t* gr, int block_size, int chunk_blocks) {
   const int n = prefix_covered_blocks(gr[kGroupPrefix], block_size) - gr[kGroupStart];
   return n > 0 ? (n + chunk_blocks - 1) / chunk_blocks : 0;
@@ -144,9 +151,13 @@ struct PrefixArgs {
   int32_t max_context;
   void* out;
   int32_t out_bf16;
-  // Causal tiles: an fp16 copy of the values (NULL: the tiles convert in LDS),
-  // tile (sequence b, logical block j, kv head h) at ((b * copy_blocks + j) *
-  // num_kv_heads + h) in the pool's tile layout, tokens past the context zero.
+  // An fp16 copy of the values the fast path stages (NULL: it converts them
+  // in LDS), in the pool's tile layout.  Causal tiles: tile (sequence b,
+  // logical block j, kv head h) at ((b * copy_blocks + j) * num_kv_heads + h),
+  // tokens past the context zero (made by the call).  Shared-prefix pass: the
+  // groups' pass blocks in plan order, tile (block j of group g, kv head h) at
+  // ((first_g + j - start_g) * num_kv_heads + h), first_g = the pass blocks
+  // of the groups before g (made by pkv_prefix_values_f16).
   void* v_copy;
   int32_t copy_blocks;
   // Causal tiles: sequences in order of decreasing context length (ties by
@@ -169,6 +180,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int head_dim, int block_size,
 hipError_t launch_prefix(const PrefixArgs& p, int block_size, int group, bool causal, hipStream_t stream);
 // Fills p.v_copy for the causal tiles (num_seqs x copy_blocks blocks of num_kv_heads tiles).
 hipError_t launch_value_copy(const PrefixArgs& p, int block_size, hipStream_t stream);
+// Fills p.v_copy with the fp16 values of the plan's pass blocks (total_blocks of them).
+hipError_t launch_prefix_value_copy(const PrefixArgs& p, int block_size, int total_blocks, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeArgs& a, int head_dim, int block_size, hipStream_t stream);
 
 // Several new tokens per sequence (a.query_start set).  Matrix-core kernel:

@@ -213,6 +213,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // cascade: the group's members and the slot of the chunk's partials
   const int32_t* members = nullptr;
   int slot0 = 0;
+  // shared-prefix pass: the group's first block in the fp16 value copy, and
+  // the block of the group's pass that it holds
+  int copy_first = 0, copy_start = 0;
   // causal tiles: the sequence's first query row, tokens new token 0 sees, the
   // sequence's partitions and this one, and the tokens of the chunk (from its
   // first) that the tile's last row sees
@@ -294,9 +297,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
     for (; gi < num_groups; ++gi) {
       const int32_t* gr = groups + kGroupWords * gi;
       const int tiles = (gr[kGroupCount] * G + 127) / 128;
+      if (tile >= tiles) copy_first += group_pass_blocks(gr, BS);
       if (tile < tiles) {
         gend = prefix_covered_blocks(gr[kGroupPrefix], BS);
         gstart = gr[kGroupStart];
+        copy_start = gstart;
         gbegin = gr[kGroupBegin];
         gcount = gr[kGroupCount];
         leader = gr[kGroupLeader];
@@ -365,14 +370,18 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // bytes of one block of every kv head: below 2^31 (the host checks the pool)
   const uint32_t block_bytes = (uint32_t)p.num_kv_heads * TILE;
   const int iters = (blk_hi - blk_lo + NB - 1) / NB;
-  // Causal tiles with the workspace copy: the fast path stages the sequence's
-  // values from it, already fp16 and zero past the context, and skips its own
-  // conversion (the exact path still reads the pool).  Logical block j of the
-  // sequence sits at vcopy + j * block_bytes.
-  const bool from_copy = CAUSAL && p.v_copy != nullptr;
+  // With an fp16 copy of the values (causal tiles: the call's workspace copy,
+  // zero past the context; shared-prefix pass: the caller's copy of the
+  // groups' pass blocks) the fast path stages them from it and skips its own
+  // conversion; the exact path still reads the pool.
+  const bool from_copy = p.v_copy != nullptr;
+  // block j of the walk at vcopy + j * block_bytes (the shared-prefix pass's
+  // j starts at the group's start block: its copy begins at copy_first)
   const char* vcopy =
-      from_copy ? static_cast<const char*>(p.v_copy) + ((int64_t)seq * p.copy_blocks * p.num_kv_heads + kvh) * TILE
-                : nullptr;
+      !from_copy ? nullptr
+      : CAUSAL   ? static_cast<const char*>(p.v_copy) + ((int64_t)seq * p.copy_blocks * p.num_kv_heads + kvh) * TILE
+                 : reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(p.v_copy) +
+                                                 ((int64_t)(copy_first - copy_start) * p.num_kv_heads + kvh) * TILE);
 
   // Staging: per iteration each wave moves four 1 KiB pieces of the keys and
   // four of the values straight from HBM/L2 into LDS (global_load_lds: lane l
@@ -977,7 +986,52 @@ __global__ __launch_bounds__(256) void value_copy_kernel(PrefixArgs p) {
   }
 }
 
+// The fp16 copy of the plan's shared-prefix values (pkv_prefix_values_f16):
+// workgroup x takes pass block x of all groups in plan order, group g's blocks
+// [start_g, covered end_g) of its leader's table, every kv head of it.  A
+// block id outside the pool gives zeros (the pass turns the group's rows into
+// NaN on its own).  A value beyond fp16's range becomes +-inf, as in the
+// pass's own conversion, and sends its chunk to the exact path.
+template <int BS>
+__global__ __launch_bounds__(256) void prefix_value_copy_kernel(PrefixArgs p) {
+  constexpr int TILE = BS * HD * 2;
+  const int32_t* groups = plan_groups(p.plan);
+  const int num_groups = p.plan[kPlanGroups];
+  int x = blockIdx.x, gi = 0;
+  for (; gi < num_groups; ++gi) {
+    const int n = group_pass_blocks(groups + kGroupWords * gi, BS);
+    if (x < n) break;
+    x -= n;
+  }
+  if (gi == num_groups) return;
+  const int32_t* gr = groups + kGroupWords * gi;
+  int id = p.block_tables[(int64_t)gr[kGroupLeader] * p.max_blocks + gr[kGroupStart] + x];
+  if ((unsigned)id >= (unsigned)p.num_blocks) id = -1;
+  const char* src = reinterpret_cast<const char*>(p.v_pool) + (int64_t)(id < 0 ? 0 : id) * p.num_kv_heads * TILE;
+  uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(p.v_copy) + (int64_t)blockIdx.x * p.num_kv_heads * TILE);
+  const int total = p.num_kv_heads * TILE / 16;
+  for (int y = threadIdx.x; y < total; y += 256) {
+    uint4 h = make_uint4(0, 0, 0, 0);
+    if (id >= 0) {
+      const uint4 w = load16(src + 16 * (int64_t)y);
+      h = make_uint4(pack_f16(bf16_lo(w.x), bf16_hi(w.x)), pack_f16(bf16_lo(w.y), bf16_hi(w.y)),
+                     pack_f16(bf16_lo(w.z), bf16_hi(w.z)), pack_f16(bf16_lo(w.w), bf16_hi(w.w)));
+    }
+    dst[y] = h;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_prefix_value_copy(const PrefixArgs& p, int block_size, int total_blocks, hipStream_t s) {
+  if (total_blocks <= 0 || !p.v_copy || !p.plan) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)total_blocks), block(256);
+  if (block_size == 8) hipLaunchKernelGGL(prefix_value_copy_kernel<8>, grid, block, 0, s, p);
+  else if (block_size == 16) hipLaunchKernelGGL(prefix_value_copy_kernel<16>, grid, block, 0, s, p);
+  else if (block_size == 32) hipLaunchKernelGGL(prefix_value_copy_kernel<32>, grid, block, 0, s, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_value_copy(const PrefixArgs& p, int block_size, hipStream_t s) {
   const int64_t blocks = (int64_t)p.num_seqs * p.copy_blocks;

@@ -46,12 +46,18 @@ class DecodeOpts(ctypes.Structure):
         ("prefix_plan_words", ctypes.c_size_t),
         ("min_eff_tokens", ctypes.c_float),
         ("tile_value_copy", ctypes.c_int32),
+        ("prefix_values_f16", ctypes.c_void_p),
+        ("prefix_values_f16_bytes", ctypes.c_size_t),
     ]
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 lib.pkv_paged_attn_workspace_bytes.restype = _sz
 lib.pkv_paged_attn_workspace_bytes.argtypes = [ctypes.POINTER(PoolDesc), _i32, _i32, _i32, ctypes.POINTER(DecodeOpts)]
+lib.pkv_prefix_values_f16_bytes.restype = _sz
+lib.pkv_prefix_values_f16_bytes.argtypes = [ctypes.POINTER(PoolDesc), _vp, _sz]
+lib.pkv_prefix_values_f16.restype = _i32
+lib.pkv_prefix_values_f16.argtypes = [_vp, _vp, _i32, _i32, ctypes.POINTER(PoolDesc), _vp, _vp, _sz, _vp, _sz, _vp]
 lib.pkv_paged_attn_decode.restype = _i32
 lib.pkv_paged_attn_decode.argtypes = [
     _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, ctypes.POINTER(PoolDesc), ctypes.c_float, _i32, _vp, _vp, _sz,
@@ -223,12 +229,42 @@ def plan_shared_prefix(block_tables, context_lens, block_size, min_group_seqs=4,
 
 
 def _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup=0, min_eff_tokens=0.0,
-          tile_value_copy=0):
+          tile_value_copy=0, prefix_values=None):
     base = (int(partition_tokens), KERNELS[kernel], int(blocks_in_flight), int(heads_per_workgroup))
+    vals = (None, 0) if prefix_values is None else (_ptr(prefix_values),
+                                                     prefix_values.numel() * prefix_values.element_size())
     if prefix_plan is None:
-        return DecodeOpts(*base, None, None, 0, float(min_eff_tokens), int(tile_value_copy))
+        return DecodeOpts(*base, None, None, 0, float(min_eff_tokens), int(tile_value_copy), *vals)
     return DecodeOpts(*base, prefix_plan.host.ctypes.data, _ptr(prefix_plan.dev), prefix_plan.host.size,
-                      float(min_eff_tokens), int(tile_value_copy))
+                      float(min_eff_tokens), int(tile_value_copy), *vals)
+
+
+def prefix_values_f16_bytes(k_pool, v_pool, prefix_plan) -> int:
+    """Bytes of the fp16 copy of the plan's shared-prefix values (0: none)."""
+    desc = pool_desc(k_pool, v_pool)
+    return int(lib.pkv_prefix_values_f16_bytes(ctypes.byref(desc), prefix_plan.host.ctypes.data,
+                                               prefix_plan.host.size))
+
+
+def prefix_values_f16(k_pool, v_pool, block_tables, prefix_plan, out=None, stream=None):
+    """The fp16 copy of the plan's shared-prefix values (pkv_prefix_values_f16),
+    for ``prefix_values=`` of the decode calls: made once per plan and reused
+    while the plan and the prefix blocks do not change.  Returns the uint8
+    device tensor, or None when the plan has no pass blocks."""
+    desc = pool_desc(k_pool, v_pool)
+    if block_tables.dtype != torch.int32 or not block_tables.is_contiguous():
+        raise TypeError("block_tables must be contiguous int32")
+    need = prefix_values_f16_bytes(k_pool, v_pool, prefix_plan)
+    if need == 0:
+        return None
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=v_pool.device)
+    nseq, mb = block_tables.shape
+    st = lib.pkv_prefix_values_f16(_ptr(v_pool), _ptr(block_tables), nseq, mb, ctypes.byref(desc),
+                                   prefix_plan.host.ctypes.data, _ptr(prefix_plan.dev), prefix_plan.host.size,
+                                   _ptr(out), out.numel() * out.element_size(), _stream(stream))
+    _check(st, "pkv_prefix_values_f16")
+    return out
 
 
 def paged_attn_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, max_context_len, partition_tokens=0,
@@ -242,7 +278,8 @@ def paged_attn_workspace_bytes(k_pool, v_pool, num_seqs, num_heads, max_context_
 
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, max_context_len=None,
                       workspace=None, partition_tokens=0, kernel="auto", out_dtype=None, stream=None,
-                      blocks_in_flight=0, prefix_plan=None, heads_per_workgroup=0, min_eff_tokens=0.0):
+                      blocks_in_flight=0, prefix_plan=None, heads_per_workgroup=0, min_eff_tokens=0.0,
+                      prefix_values=None):
     """``out[b, h] = softmax(scale * q[b, h] . K^T) . V`` over sequence b's
     paged keys/values.  ``q`` is ``[B, Hq, D]``; ``block_tables`` ``[B, max_blocks]``
     int32; ``context_lens`` ``[B]`` int32.  ``max_context_len`` is a host-side
@@ -263,7 +300,8 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=
         odt = q.dtype if out_dtype is None else out_dtype
         out = torch.empty((nseq, nh, hd), dtype=odt, device=q.device)
     odt_code = PKV_BF16 if out.dtype == torch.bfloat16 else PKV_F32
-    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup, min_eff_tokens)
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup, min_eff_tokens,
+                 prefix_values=prefix_values)
     need = int(lib.pkv_paged_attn_workspace_bytes(ctypes.byref(desc), nseq, nh, int(max_context_len),
                                                   ctypes.byref(opts)))
     if workspace is None and need > 0:
@@ -278,7 +316,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=
 
 def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale, out, max_context_len=None,
                               partition_tokens=0, kernel="auto", stream=None, blocks_in_flight=0, prefix_plan=None,
-                              heads_per_workgroup=0, min_eff_tokens=0.0):
+                              heads_per_workgroup=0, min_eff_tokens=0.0, prefix_values=None):
     """``paged_attn_decode`` through pkv_paged_attn_decode_noalloc: no workspace
     argument, nothing allocated (``out`` must be given); the partials go to the
     library's per-GPU scratch array.  Calls must not overlap on one GPU."""
@@ -296,7 +334,8 @@ def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, sca
     if max_context_len is None:
         max_context_len = max_blocks * desc.block_size
     odt_code = PKV_BF16 if out.dtype == torch.bfloat16 else PKV_F32
-    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup, min_eff_tokens)
+    opts = _opts(partition_tokens, kernel, blocks_in_flight, prefix_plan, heads_per_workgroup, min_eff_tokens,
+                 prefix_values=prefix_values)
     st = lib.pkv_paged_attn_decode_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
                                            _ptr(context_lens), nseq, nh, max_blocks, int(max_context_len),
                                            ctypes.byref(desc), float(scale), odt_code, _ptr(out), ctypes.byref(opts),

@@ -242,6 +242,52 @@ def test_prefix_plan_is_checked_before_launch(ops):
     assert _decode(ops, d, opts=opts, ws=16, ws_bytes=ws - 16) == 3
 
 
+def test_prefix_values_f16_checks(ops):
+    """Size of the fp16 copy of a plan's prefix values (pass blocks of every
+    group, every kv head), and the argument checks of its maker and of the
+    decode option, all before anything is launched."""
+    import numpy as np
+
+    d = _desc(ops)
+    tables = np.tile(np.arange(16, dtype=np.int32), (4, 1))  # 4 sequences sharing 16 blocks (4 pass iterations)
+    ctx = np.full(4, 256, dtype=np.int32)
+    words = ops.plan_shared_prefix(tables, ctx, 16, 2, 1, device=None).host
+    tile = 16 * 128 * 2  # one block of one kv head, fp16
+    size = lambda w, desc=d: ops.lib.pkv_prefix_values_f16_bytes(ctypes.byref(desc), w.ctypes.data, w.size)
+    assert size(words) == 16 * 8 * tile
+    # nested: root over the first 8 blocks, two children over blocks 8..15 each
+    t2 = tables.copy()
+    t2[2:, 8:] += 100
+    nested = ops.plan_shared_prefix(t2, ctx, 16, 2, 1, device=None).host
+    assert size(nested) == (8 + 8 + 8) * 8 * tile
+    assert size(words, _desc(ops, dtype=ops.PKV_F32)) == 0
+    assert size(words, _desc(ops, head_dim=64)) == 0
+    bad = words.copy()
+    bad[0] = 0
+    assert size(bad) == 0
+
+    p = ctypes.c_void_p(16)
+    need = 16 * 8 * tile
+
+    def make(v=p, plan_dev=p, desc=d, out=p, out_bytes=need, w=words):
+        return ops.lib.pkv_prefix_values_f16(v, p, 4, 16, ctypes.byref(desc), w.ctypes.data, plan_dev, w.size,
+                                             out, out_bytes, None)
+    assert make(plan_dev=None) == 1
+    assert make(desc=_desc(ops, dtype=ops.PKV_F32)) == 2
+    assert make(w=bad) == 1
+    assert make(v=None) == 1
+    assert make(out=ctypes.c_void_p(8)) == 1                 # misaligned
+    assert make(out_bytes=need - 1) == 1
+    assert "smaller than pkv_prefix_values_f16_bytes" in ops.lib.pkv_last_error().decode()
+
+    def decode(vals, vbytes):
+        opts = ops.DecodeOpts(0, 0, 0, 0, words.ctypes.data, 16, words.size, 0.0, 0, vals, vbytes)
+        return _decode(ops, d, opts=opts, ws=16, ws_bytes=1 << 30)
+    assert decode(16, need - 16) == 1                        # smaller than the plan's copy
+    assert decode(8, need) == 1                              # misaligned
+    assert "prefix_values_f16" in ops.lib.pkv_last_error().decode()
+
+
 def test_swap_arguments(ops):
     d = _desc(ops)
     p = ctypes.c_void_p(16)

@@ -116,6 +116,45 @@ def test_cascade_exact_path_only(case):
     check_attention(out_to_f64(out), ref, "bf16", "f32", f"cascade-exact/{name}")
 
 
+@pytest.mark.parametrize("min_eff", [0.0, 1.0])
+def test_cascade_with_prefix_f16_copy(case, min_eff):
+    """The prefix pass staging the caller's fp16 copy of the prefix values
+    (pkv_prefix_values_f16) gives the same bits as converting them itself,
+    on the default floor and with the fp16 path wherever the values fit."""
+    name, wl, gw, _, plan = case
+    _say(f"[cascade] fp16 prefix copy {name} min_eff={min_eff}")
+    copy = ops.prefix_values_f16(gw.k_pool, gw.v_pool, gw.block_tables, plan)
+    if copy is None:
+        assert ops.prefix_values_f16_bytes(gw.k_pool, gw.v_pool, plan) == 0
+        pytest.skip("no pass blocks in this plan")
+    for odt in (torch.float32, None):
+        a = gw.decode(prefix_plan=plan, out_dtype=odt, min_eff_tokens=min_eff)
+        b = gw.decode(prefix_plan=plan, out_dtype=odt, min_eff_tokens=min_eff, prefix_values=copy)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16) if odt is None else a, b.view(torch.int16) if odt is None else b), name
+
+
+def test_prefix_f16_copy_contents(case):
+    """The copy holds each group's pass blocks (start to covered end) of its
+    leader's table, in plan order, every kv head, as fp16 of the pool's bf16
+    values."""
+    name, wl, gw, _, plan = case
+    copy = ops.prefix_values_f16(gw.k_pool, gw.v_pool, gw.block_tables, plan)
+    if copy is None:
+        pytest.skip("no pass blocks in this plan")
+    s = wl.spec
+    w = plan.host
+    nseq, ngroups = int(w[1]), int(w[3])
+    groups = w[6 + 2 * nseq:6 + 2 * nseq + 6 * ngroups].reshape(ngroups, 6)
+    ids = []
+    for prefix, _begin, _count, leader, start, _parent in groups:
+        covered = (int(prefix) * s.block_size) // 64 * 64 // s.block_size
+        ids += [int(wl.block_tables[leader, j]) for j in range(int(start), covered)]
+    want = gw.v_pool[torch.tensor(ids, device="cuda", dtype=torch.long)].to(torch.float16)
+    got = copy.view(torch.float16).view(want.shape)
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16)), name
+
+
 def test_cascade_close_to_plain_decode(case):
     name, wl, gw, _, plan = case
     _say(f"[cascade] vs plain {name}")
@@ -180,6 +219,11 @@ def test_bad_prefix_block_gives_nan_rows_of_the_group_only():
     others = [b for b in range(wl.spec.num_seqs) if prefix_group_of(wl.spec, b) != 0]
     assert np.isnan(out[group0]).all()
     assert np.array_equal(out[others], good[others])
+    # the fp16 prefix copy holds zeros for the bad block; the pass still sees the bad id
+    copy = ops.prefix_values_f16(gw.k_pool, gw.v_pool, gw.block_tables, plan)
+    out = out_to_f64(gw.decode(prefix_plan=plan, prefix_values=copy))
+    assert np.isnan(out[group0]).all()
+    assert np.array_equal(out[others], good[others])
 
 
 @pytest.mark.parametrize("min_eff", [0.0, 1.0])
@@ -216,6 +260,10 @@ def test_prefix_values_near_the_fp16_limit(bits, label, min_eff):
     assert np.abs(ref).max() > 10.0  # the large values did reach the output
     b = out_to_f64(gw.decode(prefix_plan=plan, min_eff_tokens=min_eff))
     check_attention(b, ref, "bf16", "bf16", f"cascade/{label}")
+    # through the fp16 prefix copy (+-inf there for the values beyond fp16): the same bits
+    copy = ops.prefix_values_f16(gw.k_pool, gw.v_pool, gw.block_tables, plan)
+    c = out_to_f64(gw.decode(prefix_plan=plan, out_dtype=torch.float32, min_eff_tokens=min_eff, prefix_values=copy))
+    assert np.array_equal(c, out), label
 
 
 def test_full_shared_prefix_workload():
@@ -233,12 +281,19 @@ def test_full_shared_prefix_workload():
     pairs = [(b, (b % s.num_kv_heads) * s.group + i) for b in range(s.num_seqs) for i in range(s.group)]
     _say(f"[cascade] full oracle on {len(pairs)} rows")
     ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale, pairs=pairs)
+    copy = ops.prefix_values_f16(gw.k_pool, gw.v_pool, gw.block_tables, plan)
     for out_dtype in ("f32", "bf16"):
         _say(f"[cascade] full shared-prefix out={out_dtype}")
-        out = out_to_f64(gw.decode(prefix_plan=plan, out_dtype=torch.float32 if out_dtype == "f32" else None))
+        odt = torch.float32 if out_dtype == "f32" else None
+        out_t = gw.decode(prefix_plan=plan, out_dtype=odt)
+        out = out_to_f64(out_t)
         assert np.isfinite(out).all()
         got = np.stack([out[b, h] for b, h in pairs])
         check_attention(got, ref, "bf16", out_dtype, f"cascade/full/{out_dtype}")
+        # with the fp16 prefix copy, as the benchmark runs it: the same bits
+        with_copy = gw.decode(prefix_plan=plan, out_dtype=odt, prefix_values=copy)
+        assert torch.equal(out_t.view(torch.int16) if odt is None else out_t,
+                           with_copy.view(torch.int16) if odt is None else with_copy)
 
 
 def _nested(name):
