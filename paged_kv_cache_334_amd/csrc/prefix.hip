@@ -515,7 +515,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
   // With causal tiles, the stage reaching past the tokens the tile sees has
   // those values zeroed on the way.
   auto convert_own = [&](int vb_i, int stage) {
-    if (from_copy) return;  // converted by the copy, zeros past the context
+    if (from_copy) return;  // already fp16 in the copy (causal tiles: zero past the context)
     if (CAUSAL && (stage + 1) * TOK > walk_end) {
 #pragma unroll
       for (int k = 0; k < kPiecesPerWave; ++k)
@@ -588,9 +588,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
       if (sub < 3) load_keys(kb_i, sub + 1, ka[(sub + 1) & 1]);
-      // raised wave priority from the last quarter of the step through the
-      // value products (compute_fast lowers it): see compute_fast
-      if (sub == 3) __builtin_amdgcn_s_setprio(1);
+      // shared-prefix pass: raised wave priority from the last quarter of the
+      // step through the value products (compute_fast lowers it): see there
+      if (!CAUSAL && sub == 3) __builtin_amdgcn_s_setprio(1);
       sn[sub][0] = f32x4{0.f, 0.f, 0.f, 0.f};
       sn[sub][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -654,13 +654,14 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
         weights();
       }
     }
-    // The value products and the conversion beside them run at raised wave
-    // priority (from the fused step's last quarter on): when the SIMD's other
-    // wave, of the other workgroup on the CU, is in its own fused step, its
-    // vector work then fills the cycles around this wave's matrix
-    // instructions rather than the other way round.  Measured, call against
-    // call: shared-prefix 186 -> 180 us, prefill 356 -> 351 us.
-    __builtin_amdgcn_s_setprio(1);
+    // The shared-prefix pass runs the value products and the conversion beside
+    // them at raised wave priority (from the fused step's last quarter on):
+    // when the SIMD's other wave, of the other workgroup on the CU, is in its
+    // own fused step, its vector work then fills the cycles around this wave's
+    // matrix instructions rather than the other way round.  Interleaved A/B
+    // with the fp16 prefix copy: shared-prefix 6.9 us per call faster than
+    // without; the causal tiles (prefill) 2.4 us slower, so they leave it.
+    if constexpr (!CAUSAL) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int pair = 0; pair < 2; ++pair) {
       // all eight value pieces of the run read before its matrix instructions
@@ -698,7 +699,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefix_kernel(PrefixArgs p) {
       lds_dma_wait<2 * kPiecesPerWave>();
       convert_own(convert_vb, stage + 1);
     }
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (!CAUSAL) __builtin_amdgcn_s_setprio(0);
   };
 
   // Exact path (bf16 values in LDS): per 32-token run, the reference moves
