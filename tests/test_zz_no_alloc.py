@@ -93,3 +93,11 @@ def test_noalloc_cascade_matches_workspace_decode():
         desc, kp, vp = oracle_pools(wl)
         ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale)
         check_attention(out_to_f64(got), ref, "bf16", "f32", f"noalloc/cascade/{label}")
+        # staging the plan's fp16 prefix copy: the same bits again
+        copy = ops.prefix_values_f16(gw.k_pool, gw.v_pool, gw.block_tables, plan)
+        assert copy is not None
+        got.fill_(7.0)
+        ops.paged_attn_decode_noalloc(gw.q, gw.k_pool, gw.v_pool, gw.block_tables, gw.context_lens, wl.scale, got,
+                                      max_context_len=wl.max_context, prefix_plan=plan, prefix_values=copy)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(got), to_bits(want)), f"{label} with the fp16 prefix copy"
