@@ -209,7 +209,10 @@ size_t pkv_plan_shared_prefix(const int32_t* block_tables, const int32_t* contex
  * least that many bytes) on stream, reading v_pool and the block tables
  * (DEVICE) through the plan (HOST words, checked as the decode call checks
  * them, and their DEVICE copy).  No copy needed (no pass blocks): PKV_OK with
- * nothing launched.
+ * nothing launched.  Errors, all before anything is launched: PKV_EUNSUPPORTED
+ * for a pool other than bf16 / head_dim 128; PKV_EINVAL for a plan that does
+ * not check against these tables, a NULL or misaligned pointer, or out_bytes
+ * below the copy's size; PKV_EHIP when the launch fails.
  */
 size_t pkv_prefix_values_f16_bytes(const pkv_pool_desc* pool, const int32_t* plan, size_t plan_words);
 pkv_status pkv_prefix_values_f16(const void* v_pool, const int32_t* block_tables, int32_t num_seqs,
