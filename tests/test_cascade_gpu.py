@@ -315,6 +315,19 @@ def _nested(name):
     return wl, 5
 
 
+def _same_with_prefix_copy(gw, plan, label, **kw):
+    """The decode with the plan's fp16 prefix copy gives the bits it gives
+    without (min_eff_tokens 1, so the fp16 path runs wherever the values fit,
+    and the default floor)."""
+    copy = ops.prefix_values_f16(gw.k_pool, gw.v_pool, gw.block_tables, plan)
+    assert copy is not None, label
+    for min_eff in (0.0, 1.0):
+        a = gw.decode(prefix_plan=plan, out_dtype=torch.float32, min_eff_tokens=min_eff, **kw)
+        b = gw.decode(prefix_plan=plan, out_dtype=torch.float32, min_eff_tokens=min_eff, prefix_values=copy, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"{label} min_eff={min_eff}"
+
+
 @pytest.mark.parametrize("name", ["nested-2-levels", "nested-3-levels"])
 def test_nested_cascade_matches_oracle(name):
     """Nested groups: each level's pass covers its own block range for its own
@@ -336,6 +349,8 @@ def test_nested_cascade_matches_oracle(name):
     a = out_to_f64(gw.decode(prefix_plan=plan, out_dtype=torch.float32))
     b = out_to_f64(gw.decode(out_dtype=torch.float32))
     assert np.abs(a - b).max() <= 2e-3
+    # each level's blocks at its own place in the fp16 prefix copy
+    _same_with_prefix_copy(gw, plan, name)
 
 
 def test_beam_tree_workload():
@@ -353,6 +368,7 @@ def test_beam_tree_workload():
     for out_dtype in ("bf16", "f32"):
         out = gw.decode(prefix_plan=plan, out_dtype=torch.float32 if out_dtype == "f32" else None)
         check_attention(out_to_f64(out), ref, "bf16", out_dtype, "cascade/beam-tree-small")
+    _same_with_prefix_copy(gw, plan, "beam-tree-small")
 
 
 def test_full_beam_tree_workload():
@@ -371,6 +387,8 @@ def test_full_beam_tree_workload():
         out = out_to_f64(gw.decode(prefix_plan=plan, out_dtype=torch.float32 if out_dtype == "f32" else None))
         assert np.isfinite(out).all()
         check_attention(out, ref, "bf16", out_dtype, f"cascade/full-beam-tree/{out_dtype}")
+    # as the benchmark runs it, with the plan's fp16 prefix copy: the same bits
+    _same_with_prefix_copy(gw, plan, "full beam-tree")
 
 
 @pytest.mark.parametrize("seed", range(3))
@@ -392,6 +410,7 @@ def test_random_beam_trees_match_oracle(seed):
     ref = oracle.paged_decode(wl.q, kp, vp, desc, wl.block_tables, wl.context_lens, wl.scale)
     out = gw.decode(prefix_plan=plan, out_dtype=torch.float32)
     check_attention(out_to_f64(out), ref, "bf16", "f32", f"cascade/random-tree-{seed}")
+    _same_with_prefix_copy(gw, plan, f"random tree {seed}")
 
 
 @pytest.mark.parametrize("min_eff", [0.0, 1.0])
